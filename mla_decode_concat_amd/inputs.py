@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the fused MLA decode epilogue.
+
+This module is shared by the tests (which feed the same bytes to the CPU
+oracle and to the GPU library) and by the benchmark.  It holds no arithmetic
+of the epilogue itself: it only draws random tensors, picks slots and
+positions, and builds the rotary table that the epilogue receives as an input
+(the prhub summary of vLLM PR #54896, "implementation breakdown" item 2,
+lists the rope table among the data the kernel reads).
+
+Shapes follow the page's test (section "key source snippets"): ql_nope
+[T, H, 512], q_pe [T, H, 64], kv_c [T, 512], k_pe [T, 64], a zero-filled paged
+cache [num_blocks, block_size, 576] and int64 slots drawn as a prefix of a
+random permutation of all cache slots.  The page seeds with 3; so do we.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+NOPE = 512
+PE = 64
+ROW = NOPE + PE
+DEFAULT_SEED = 3
+ROPE_THETA = 10000.0
+ROPE_MAX_POSITION = 32768
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    tokens: int
+    heads: int
+    num_blocks: int
+    block_size: int = 64
+    rope: bool = False
+    q_fp8: bool = False
+    kv_fp8: bool = False
+    # slot recipe: "randint" (one draw in [0, num_slots)) or "randperm"
+    # (first T of a permutation of all num_slots slots)
+    slots: str = "randperm"
+    # position recipe: "none", "uniform:<hi>" or "arange"
+    positions: str = "none"
+    q_scale: float = 0.05
+    kv_scale: float = 0.05
+    max_position: int = ROPE_MAX_POSITION
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_blocks * self.block_size
+
+    def describe(self) -> str:
+        bits = []
+        if self.rope:
+            bits.append("rope")
+        if self.q_fp8:
+            bits.append(f"q_e4m3(scale={self.q_scale})")
+        if self.kv_fp8:
+            bits.append(f"kv_e4m3(scale={self.kv_scale})")
+        flags = "+".join(bits) if bits else "bf16-copy"
+        return (f"T={self.tokens} H={self.heads} cache=[{self.num_blocks},"
+                f"{self.block_size},576] {flags}")
+
+
+# The five workloads: decode sizes around the row-split boundary, the
+# full-head decode batch and the prefill-sized bandwidth case.
+WORKLOADS = {
+    "t1_h16_copy": Workload("t1_h16_copy", 1, 16, 1, slots="randint"),
+    "t64_h16_rope_fp8": Workload("t64_h16_rope_fp8", 64, 16, 1, rope=True,
+                                 q_fp8=True, kv_fp8=True, positions="uniform:4096"),
+    "t65_h16_rope_fp8": Workload("t65_h16_rope_fp8", 65, 16, 2, rope=True,
+                                 q_fp8=True, kv_fp8=True, positions="uniform:4096"),
+    "t256_h128_rope_qfp8": Workload("t256_h128_rope_qfp8", 256, 128, 4096, rope=True,
+                                    q_fp8=True, kv_fp8=False, positions="uniform:32768"),
+    "t8192_h16_rope_kvfp8": Workload("t8192_h16_rope_kvfp8", 8192, 16, 4096, rope=True,
+                                     q_fp8=False, kv_fp8=True, positions="arange"),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+
+
+def rope_table(max_position: int = ROPE_MAX_POSITION, theta: float = ROPE_THETA,
+               rot_dim: int = PE) -> torch.Tensor:
+    """[max_position, 64] fp32 table: cos of the 32 angles, then their sin.
+
+    Angle (p, i) = p * theta^(-2i/64), evaluated in float64 and rounded once
+    to fp32.  This is the usual rotary frequency ladder; the epilogue takes
+    the table as data, so its exact values never enter a parity comparison.
+    """
+    half = rot_dim // 2
+    i = torch.arange(half, dtype=torch.float64)
+    inv_freq = theta ** (-2.0 * i / rot_dim)
+    p = torch.arange(max_position, dtype=torch.float64)
+    ang = p[:, None] * inv_freq[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).contiguous()
+
+
+_TABLE_CACHE: dict = {}
+
+
+def shared_rope_table(max_position: int = ROPE_MAX_POSITION) -> torch.Tensor:
+    if max_position not in _TABLE_CACHE:
+        _TABLE_CACHE[max_position] = rope_table(max_position)
+    return _TABLE_CACHE[max_position]
+
+
+def make_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
+    """CPU tensors for one workload, drawn in a fixed order from one generator:
+    ql_nope, q_pe, kv_c, k_pe (N(0,1) fp32 rounded to bf16), then slots, then
+    positions.  The cache starts as zeros."""
+    g = torch.Generator().manual_seed(seed)
+    T, H = w.tokens, w.heads
+
+    def randn_bf16(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+    ql_nope = randn_bf16(T, H, NOPE)
+    q_pe = randn_bf16(T, H, PE)
+    kv_c = randn_bf16(T, NOPE)
+    k_pe = randn_bf16(T, PE)
+    S = w.num_slots
+    if w.slots == "randint":
+        slots = torch.randint(0, S, (T,), generator=g, dtype=torch.int64)
+    elif w.slots == "randperm":
+        if T > S:
+            raise ValueError("more tokens than distinct slots")
+        slots = torch.randperm(S, generator=g, dtype=torch.int64)[:T].contiguous()
+    else:
+        raise ValueError(w.slots)
+    if w.positions == "none":
+        positions = None
+    elif w.positions == "arange":
+        positions = torch.arange(T, dtype=torch.int64)
+    elif w.positions.startswith("uniform:"):
+        hi = int(w.positions.split(":")[1])
+        positions = torch.randint(0, hi, (T,), generator=g, dtype=torch.int64)
+    else:
+        raise ValueError(w.positions)
+    kv_dtype = torch.float8_e4m3fn if w.kv_fp8 else torch.bfloat16
+    cache = torch.zeros(w.num_blocks, w.block_size, ROW, dtype=kv_dtype)
+    out = dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
+               slot_mapping=slots, positions=positions,
+               rope_cos_sin=shared_rope_table(w.max_position) if w.rope else None,
+               q_scale=torch.tensor([w.q_scale], dtype=torch.float32) if w.q_fp8 else None,
+               kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32) if w.kv_fp8 else None)
+    return out
+
+
+def custom(tokens: int, heads: int, num_blocks: int | None = None, block_size: int = 64,
+           rope: bool = False, q_fp8: bool = False, kv_fp8: bool = False,
+           positions: str | None = None, slots: str = "randperm", q_scale: float = 0.05,
+           kv_scale: float = 0.05, max_position: int = ROPE_MAX_POSITION,
+           name: str = "custom") -> Workload:
+    """A workload with the same recipe at another size (ragged tests)."""
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(tokens / block_size))
+    if positions is None:
+        positions = f"uniform:{max_position}" if rope else "none"
+    return Workload(name, tokens, heads, num_blocks, block_size, rope, q_fp8, kv_fp8,
+                    slots, positions, q_scale, kv_scale, max_position)

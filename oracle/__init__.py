@@ -1,0 +1,207 @@
+"""CPU oracle for the fused MLA decode epilogue -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and the
+two share no code, header, table or constant.
+
+The arithmetic lives in ``mla_oracle.c`` (plain scalar C, fp32 rounding per
+operation, no fused multiply-add); this module only compiles it with gcc and
+marshals numpy arrays.  What it computes is stated in the C file's header and
+follows the prhub summary of vLLM PR #54896 (Kimi-K3 MLA decode kernel),
+sections "implementation breakdown" and "key source snippets".
+
+Parity status: every exported function is pinned in ``tests/test_oracle_pins.py``
+(format definitions, brute force, closed forms, the page's own identity).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# -ffp-contract=off keeps every product and sum separately rounded.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+          "-ffp-contract=off", "-fno-fast-math"]
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle into ``oracle/liboracle.so`` (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    _lib = _configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_quant_e4m3.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.oracle_quant_e4m3.restype = ctypes.c_uint8
+    lib.oracle_rope_neox_f32.argtypes = [u16p, f32p, f32p]
+    lib.oracle_rope_neox_f32.restype = None
+    lib.oracle_rope_neox_f64.argtypes = [u16p, f32p, f64p]
+    lib.oracle_rope_neox_f64.restype = None
+    lib.oracle_mla_decode_q_concat_kv_insert.argtypes = [
+        u8p, u16p, u16p, u16p, u16p, u8p, i64p, i64p, f32p,
+        ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_mla_decode_q_concat_kv_insert.restype = ctypes.c_int
+    for name, outp in (("oracle_f32_to_e4m3_n", u8p), ("oracle_f32_to_bf16_n", u16p)):
+        fn = getattr(lib, name)
+        fn.argtypes = [f32p, outp, ctypes.c_int64]
+        fn.restype = None
+    lib.oracle_quant_e4m3_n.argtypes = [f32p, ctypes.c_float, u8p, ctypes.c_int64]
+    lib.oracle_quant_e4m3_n.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ---- element encoders (scalar wrappers, for pins) --------------------------
+
+def bf16_to_f32(bits: int) -> float:
+    return _load().oracle_bf16_to_f32(int(bits) & 0xFFFF)
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(_load().oracle_f32_to_bf16_rne(float(x)))
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(_load().oracle_f32_to_e4m3(float(x)))
+
+
+def quant_e4m3(x: float, inv: float) -> int:
+    return int(_load().oracle_quant_e4m3(float(x), float(inv)))
+
+
+def f32_to_bf16_array(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.size, dtype=np.uint16)
+    _load().oracle_f32_to_bf16_n(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def f32_to_e4m3_array(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.size, dtype=np.uint8)
+    _load().oracle_f32_to_e4m3_n(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint8), x.size)
+    return out
+
+
+def quant_e4m3_array(x: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3 codes of x under a per-tensor scale (inv = fl32(1/scale))."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    inv = float(np.float32(1.0) / np.float32(scale))
+    out = np.empty(x.size, dtype=np.uint8)
+    _load().oracle_quant_e4m3_n(_ptr(x, ctypes.c_float), inv, _ptr(out, ctypes.c_uint8), x.size)
+    return out
+
+
+# ---- rotation -----------------------------------------------------------------
+
+def rope_neox_f32(x_bits: np.ndarray, cs_row: np.ndarray) -> np.ndarray:
+    """fp32 NeoX rotation of one 64-wide bf16 tail (bits) by one table row."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    cs = np.ascontiguousarray(cs_row, dtype=np.float32)
+    assert x.size == 64 and cs.size == 64
+    y = np.empty(64, dtype=np.float32)
+    _load().oracle_rope_neox_f32(_ptr(x, ctypes.c_uint16), _ptr(cs, ctypes.c_float),
+                                 _ptr(y, ctypes.c_float))
+    return y
+
+
+def rope_neox_f64(x_bits: np.ndarray, cs_row: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    cs = np.ascontiguousarray(cs_row, dtype=np.float32)
+    y = np.empty(64, dtype=np.float64)
+    _load().oracle_rope_neox_f64(_ptr(x, ctypes.c_uint16), _ptr(cs, ctypes.c_float),
+                                 _ptr(y, ctypes.c_double))
+    return y
+
+
+# ---- the whole epilogue ---------------------------------------------------
+
+def insert(q_out: np.ndarray, ql_nope: np.ndarray, q_pe: np.ndarray,
+           kv_c: np.ndarray, k_pe: np.ndarray, cache: np.ndarray,
+           slots: np.ndarray, positions: np.ndarray | None,
+           cos_sin: np.ndarray | None, q_scale: float, kv_scale: float,
+           rope: bool, q_fp8: bool, kv_fp8: bool) -> None:
+    """Run the oracle in place.
+
+    Arrays are numpy, contiguous: bf16 tensors as uint16 bit patterns, E4M3
+    tensors as uint8 codes.  ``q_out`` is [T, H, 576] (uint16 or uint8),
+    ``cache`` is [num_blocks, block_size, 576] (uint16 or uint8) and is
+    updated in place.
+    """
+    T, H = ql_nope.shape[0], ql_nope.shape[1]
+    assert ql_nope.shape == (T, H, 512) and q_pe.shape == (T, H, 64)
+    assert kv_c.shape == (T, 512) and k_pe.shape == (T, 64)
+    assert slots.shape == (T,)
+    assert q_out.shape == (T, H, 576)
+    assert q_out.dtype == (np.uint8 if q_fp8 else np.uint16)
+    assert cache.dtype == (np.uint8 if kv_fp8 else np.uint16)
+    assert cache.shape[-1] == 576
+    num_slots = cache.size // 576
+    for a in (q_out, ql_nope, q_pe, kv_c, k_pe, cache, slots):
+        assert a.flags["C_CONTIGUOUS"]
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    if rope:
+        positions = np.ascontiguousarray(positions, dtype=np.int64)
+        cos_sin = np.ascontiguousarray(cos_sin, dtype=np.float32)
+        assert positions.shape == (T,) and cos_sin.ndim == 2 and cos_sin.shape[1] == 64
+        max_pos = cos_sin.shape[0]
+        pos_p = _ptr(positions, ctypes.c_int64)
+        cs_p = _ptr(cos_sin, ctypes.c_float)
+    else:
+        max_pos = 0
+        pos_p = None
+        cs_p = None
+    rc = _load().oracle_mla_decode_q_concat_kv_insert(
+        q_out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+        _ptr(ql_nope, ctypes.c_uint16), _ptr(q_pe, ctypes.c_uint16),
+        _ptr(kv_c, ctypes.c_uint16), _ptr(k_pe, ctypes.c_uint16),
+        cache.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+        _ptr(slots, ctypes.c_int64), pos_p, cs_p,
+        float(q_scale), float(kv_scale), T, H, num_slots, max_pos,
+        int(rope), int(q_fp8), int(kv_fp8))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the shapes (rc={rc})")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,102 @@
+"""Planted mistakes: each mutant is a copy of the oracle's C source with one
+plausible slip (a flipped sign, a wrong index, a dropped term, a transposed
+operand, a wrong rounding rule).  It is compiled on the CPU and loaded in
+place of the oracle; at least one pin from test_oracle_pins must then fail.
+This shows the pins would notice such a slip in the real oracle."""
+from __future__ import annotations
+
+import ctypes
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mla_oracle.c")
+
+# (name, text in the source, replacement) -- each text occurs exactly once
+MUTANTS = [
+    ("rope_sign", "y[i] = ac - bs;", "y[i] = ac + bs;"),
+    ("rope_dropped_term", "y[i + HALF] = bc + as;", "y[i + HALF] = bc;"),
+    ("rope_pair_index", "float b = oracle_bf16_to_f32(x[i + HALF]);\n        float c = cs[i], s = cs[HALF + i];\n        float ac",
+     "float b = oracle_bf16_to_f32(x[i + HALF - 1]);\n        float c = cs[i], s = cs[HALF + i];\n        float ac"),
+    ("rope_cos_sin_swapped", "float c = cs[i], s = cs[HALF + i];\n        float ac",
+     "float c = cs[HALF + i], s = cs[i];\n        float ac"),
+    ("bf16_truncates", "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))", "if (0)"),
+    ("bf16_ties_away", "(lo == 0x8000u && (hi & 1u))", "(lo == 0x8000u)"),
+    ("e4m3_ties_up", "return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "return f + 1.0;"),
+    ("e4m3_no_saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
+     "if (a >= 480.0) return (uint8_t)(sign | 0x7F);"),
+    ("e4m3_bias", "int be = ue + 7;", "int be = ue + 8;"),
+    ("e4m3_subnormal_step", "round_half_even(a * 512.0)", "round_half_even(a * 256.0)"),
+    ("quant_by_scale_not_inverse", "float qi = q_fp8 ? 1.0f / q_scale : 1.0f;",
+     "float qi = q_fp8 ? q_scale : 1.0f;"),
+    ("scatter_by_token", "write_row(cache + (size_t)s * kv_row_bytes", "write_row(cache + (size_t)t * kv_row_bytes"),
+    ("slot_zero_skipped", "if (s < 0 || s >= num_slots) continue;", "if (s <= 0 || s >= num_slots) continue;"),
+    ("q_rows_transposed", "int64_t r = t * H + h;", "int64_t r = h * T + t;"),
+    ("k_pe_not_rotated", "k_pe + (size_t)t * PE, rope, cs_row", "k_pe + (size_t)t * PE, 0, cs_row"),
+    ("q_pe_rotated_with_first_position", "write_row(q_out + (size_t)r * q_row_bytes, ql_nope + (size_t)r * NOPE,\n                      q_pe + (size_t)r * PE, rope, cs_row,",
+     "write_row(q_out + (size_t)r * q_row_bytes, ql_nope + (size_t)r * NOPE,\n                      q_pe + (size_t)r * PE, rope, rope ? cs + clamp_pos(positions[0], max_position) * PE : 0,"),
+]
+
+CHECKS = [
+    P.test_e4m3_golden_points,
+    P.test_e4m3_matches_brute_force_on_all_bf16,
+    P.test_bf16_golden_points,
+    P.test_bf16_rne_vs_torch,
+    P.test_rope_golden_rows,
+    P.test_rope_is_complex_rotation_by_position_angle,
+    lambda: P.test_page_identity_concat_and_scatter(64),
+    lambda: P.test_oracle_matches_library_composition("t64_h16_rope_fp8"),
+    lambda: P.test_oracle_matches_library_composition_all_modes((True, False, False)),
+    lambda: P.test_oracle_matches_library_composition_all_modes((True, True, False)),
+    P.test_out_of_range_slots_leave_cache_untouched,
+]
+
+
+def _caught(lib) -> bool:
+    saved = oracle._lib
+    oracle._lib = lib
+    try:
+        for check in CHECKS:
+            try:
+                check()
+            except AssertionError:
+                return True
+        return False
+    finally:
+        oracle._lib = saved
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def _build(src_text: str, d: str, name: str):
+    c = os.path.join(d, f"{name}.c")
+    so = os.path.join(d, f"lib{name}.so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", *oracle.CFLAGS, c, "-o", so, "-lm"], check=True)
+    return oracle._configure(ctypes.CDLL(so))
+
+
+def test_unmutated_copy_passes(workdir):
+    with open(SRC) as f:
+        text = f.read()
+    assert not _caught(_build(text, workdir, "unmutated"))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(workdir, name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    assert _caught(_build(text.replace(old, new), workdir, name)), f"mutant {name} survived the pins"

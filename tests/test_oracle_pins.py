@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a fact that the prhub summary of vLLM
+PR #54896 (Kimi-K3 MLA decode kernel) or the mathematics fixes: the page's own
+identity test (section "key source snippets"), the OCP E4M3 and IEEE bf16
+format definitions (brute force over the code table, library casts, hand-derived
+points in tests/golden/), and closed forms of the rotation (complex rotation,
+norm preservation, relative-position invariance, exact hand rows).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_decode_concat_amd import inputs as I
+from tests._util import bits, oracle_run
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f(v):
+    return float(v) if not isinstance(v, str) else float(v.replace("inf", "inf"))
+
+
+# ---------------------------------------------------------------- E4M3 ----
+
+def _e4m3_code_values() -> np.ndarray:
+    """Value of every code 0..255 from the OFP8 E4M3 layout (NaN for S.1111.111)."""
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = s * m * 2.0 ** -9
+        else:
+            vals[code] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def _nearest_e4m3(x: np.ndarray) -> np.ndarray:
+    """Brute force: nearest finite code to each value, ties to the even code,
+    saturating at +-448, NaN -> S.1111.111."""
+    vals = _e4m3_code_values()
+    pos_codes = np.arange(0, 0x7F)             # +0 .. 448, ascending in value
+    pos_vals = vals[pos_codes]
+    assert np.all(np.diff(pos_vals) > 0)
+    out = np.empty(x.shape, dtype=np.uint8)
+    with np.errstate(invalid="ignore"):
+        a = np.abs(x.astype(np.float64))
+    sign = np.signbit(x).astype(np.uint8) << 7
+    idx = np.searchsorted(pos_vals, a, side="left")       # pos_vals[idx-1] < a <= pos_vals[idx]
+    idx_hi = np.clip(idx, 0, len(pos_vals) - 1)
+    idx_lo = np.clip(idx - 1, 0, len(pos_vals) - 1)
+    d_hi = np.abs(pos_vals[idx_hi] - a)
+    d_lo = np.abs(a - pos_vals[idx_lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (pos_codes[idx_lo] % 2 == 0))
+    code = np.where(pick_lo, pos_codes[idx_lo], pos_codes[idx_hi])
+    code = np.where(a >= 448.0, 0x7E, code)
+    out[:] = code.astype(np.uint8) | sign
+    out[np.isnan(x)] = 0x7F | sign[np.isnan(x)]
+    return out
+
+
+def test_e4m3_golden_points():
+    g = _golden("e4m3_points.json")
+    for p in g["encode"]:
+        x = _f(p["x"])
+        assert oracle.f32_to_e4m3(x) == int(p["code"], 16), p
+    inv = float(np.float32(1.0) / np.float32(0.05))
+    assert inv == 20.0
+    for p in g["quantise_scale_0p05"]["points"]:
+        assert oracle.quant_e4m3(p["x"], inv) == int(p["code"], 16), p
+
+
+def test_e4m3_brute_force_wide_range():
+    """Every fp32 exponent from 2^-12 to 2^9, a dense mantissa sample plus every
+    midpoint between neighbouring codes and its two fp32 neighbours."""
+    rng = np.random.default_rng(11)
+    xs = []
+    for e in range(-12, 10):
+        m = rng.integers(0, 1 << 23, size=20000, dtype=np.int64)
+        u = ((e + 127) << 23) | m
+        xs.append(u.astype(np.uint32).view(np.float32))
+    vals = _e4m3_code_values()[0:0x7F]
+    mids = ((vals[:-1] + vals[1:]) / 2.0).astype(np.float32)
+    xs.append(mids)
+    xs.append(np.nextafter(mids, np.float32(np.inf)))
+    xs.append(np.nextafter(mids, np.float32(0)))
+    xs.append(vals.astype(np.float32))
+    x = np.concatenate(xs).astype(np.float32)
+    x = np.concatenate([x, -x])
+    got = oracle.f32_to_e4m3_array(x)
+    want = _nearest_e4m3(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.05, 2.0 ** -4, 3.7])
+def test_e4m3_exhaustive_bf16_vs_torch(scale):
+    """All 65536 bf16 bit patterns, quantised under the scale, equal torch's
+    library cast of the clamped product (torch's cast rounds to nearest even
+    but does not saturate, hence the clamp); NaN compared as NaN."""
+    b = np.arange(65536, dtype=np.uint32)
+    x = (b << 16).view(np.float32)
+    got = oracle.quant_e4m3_array(x, scale)
+    inv = np.float32(1.0) / np.float32(scale)
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = (x * inv).astype(np.float32)
+    v = torch.from_numpy(prod)
+    want = torch.clamp(v, -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = np.isnan(prod)
+    assert np.all((got[nan] & 0x7F) == 0x7F)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_e4m3_matches_brute_force_on_all_bf16():
+    b = np.arange(65536, dtype=np.uint32)
+    x = (b << 16).view(np.float32)
+    assert np.array_equal(oracle.f32_to_e4m3_array(x), _nearest_e4m3(x))
+
+
+# ---------------------------------------------------------------- bf16 ----
+
+def test_bf16_golden_points():
+    g = _golden("bf16_points.json")
+    for p in g["round"]:
+        x = np.array([int(p["f32"], 16)], dtype=np.uint32).view(np.float32)
+        assert oracle.f32_to_bf16_array(x)[0] == int(p["bf16"], 16), p
+    for n in g["nan_inputs"]:
+        x = np.array([int(n, 16)], dtype=np.uint32).view(np.float32)
+        r = int(oracle.f32_to_bf16_array(x)[0])
+        assert (r & 0x7F80) == 0x7F80 and (r & 0x7F) != 0
+
+
+def test_bf16_rne_vs_torch():
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 1 << 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties and their neighbours
+    hi = rng.integers(0, 1 << 16, size=200_000, dtype=np.uint64).astype(np.uint32) << 16
+    u = np.concatenate([u, hi | 0x8000, hi | 0x7FFF, hi | 0x8001])
+    x = u.view(np.float32)
+    got = oracle.f32_to_bf16_array(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
+
+
+def test_bf16_identity_on_exact_values():
+    b = np.arange(65536, dtype=np.uint32)
+    x = (b << 16).view(np.float32)
+    got = oracle.f32_to_bf16_array(x)
+    ok = ~np.isnan(x)
+    assert np.array_equal(got[ok], b[ok].astype(np.uint16))
+
+
+# ---------------------------------------------------------------- RoPE ----
+
+def _x_bits(seed=0, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return bits((torch.randn(64, generator=g) * scale).to(torch.bfloat16))
+
+
+def _f32(xb):
+    return (xb.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_rope_golden_rows():
+    g = _golden("rope_rows.json")
+    x = np.array(g["x"], dtype=np.float32)
+    xb = bits(torch.from_numpy(x).to(torch.bfloat16))
+    assert np.array_equal(_f32(xb), x)       # inputs are bf16-exact
+    for row in g["rows"]:
+        cs = np.array([row["cos"]] * 32 + [row["sin"]] * 32, dtype=np.float32)
+        y = oracle.rope_neox_f32(xb, cs)
+        assert np.array_equal(y, np.array(row["y"], dtype=np.float32)), row["name"]
+
+
+def test_rope_position_zero_is_identity():
+    table = I.rope_table(8)
+    assert np.all(table[0, :32].numpy() == 1.0) and np.all(table[0, 32:].numpy() == 0.0)
+    for seed in range(20):
+        xb = _x_bits(seed, scale=10.0)
+        y = oracle.rope_neox_f32(xb, table[0].numpy())
+        assert np.array_equal(y, _f32(xb))
+
+
+def test_rope_is_complex_rotation_by_position_angle():
+    """NeoX pairing as complex numbers: (x_i + j x_{i+32}) * exp(j p theta^(-2i/64))
+    evaluated in float64 from the angle itself (not the table)."""
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(1)
+    i = np.arange(32, dtype=np.float64)
+    inv_freq = 10000.0 ** (-2.0 * i / 64.0)
+    for trial in range(200):
+        p = int(rng.integers(0, 4096))
+        xb = _x_bits(trial, scale=3.0)
+        x = _f32(xb).astype(np.float64)
+        z = (x[:32] + 1j * x[32:]) * np.exp(1j * p * inv_freq)
+        want = np.concatenate([z.real, z.imag])
+        got = oracle.rope_neox_f32(xb, table[p]).astype(np.float64)
+        # fp32 table entries (rel 2^-24 each), two rounded products, one
+        # rounded sum: bounded by 3 * 2^-24 * (|a| + |b|) per output
+        mag = np.abs(x[:32]) + np.abs(x[32:])
+        tol = 3.0 * 2.0 ** -24 * np.concatenate([mag, mag]) + 1e-30
+        assert np.all(np.abs(got - want) <= tol), (p, np.max(np.abs(got - want) - tol))
+
+
+def test_rope_f32_within_rounding_bound_of_f64():
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(2)
+    for trial in range(200):
+        p = int(rng.integers(0, 4096))
+        xb = _x_bits(100 + trial, scale=5.0)
+        y32 = oracle.rope_neox_f32(xb, table[p]).astype(np.float64)
+        y64 = oracle.rope_neox_f64(xb, table[p])
+        x = _f32(xb).astype(np.float64)
+        c, s = table[p, :32].astype(np.float64), table[p, 32:].astype(np.float64)
+        t1 = np.abs(x[:32] * c) + np.abs(x[32:] * s)
+        t2 = np.abs(x[32:] * c) + np.abs(x[:32] * s)
+        u = 2.0 ** -24
+        bound = np.concatenate([t1, t2]) * (2 * u + u * u) + 1e-45
+        assert np.all(np.abs(y32 - y64) <= bound)
+
+
+def test_rope_matches_library_rotate_half_fp32():
+    """Eager torch fp32: x*cos + rotate_half(x)*sin, each op rounded."""
+    table = I.rope_table(4096)
+    rng = np.random.default_rng(3)
+    for trial in range(100):
+        p = int(rng.integers(0, 4096))
+        xb = _x_bits(300 + trial, scale=4.0)
+        x = torch.from_numpy(_f32(xb).copy())
+        cos = torch.cat([table[p, :32], table[p, :32]])
+        sin = torch.cat([table[p, 32:], table[p, 32:]])
+        rot = torch.cat([-x[32:], x[:32]])
+        want = (x * cos + rot * sin).numpy()
+        got = oracle.rope_neox_f32(xb, table[p].numpy())
+        assert np.array_equal(got, want)
+
+
+def test_rope_preserves_pair_norms_and_relative_position():
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        xa, xk = _x_bits(500 + trial), _x_bits(700 + trial)
+        p1, p2 = int(rng.integers(0, 2000)), int(rng.integers(0, 2000))
+        d = int(rng.integers(1, 2000))
+        ya = oracle.rope_neox_f64(xa, table[p1])
+        x = _f32(xa).astype(np.float64)
+        assert np.allclose(ya[:32] ** 2 + ya[32:] ** 2, x[:32] ** 2 + x[32:] ** 2, rtol=1e-6, atol=1e-12)
+        dot1 = ya @ oracle.rope_neox_f64(xk, table[p2])
+        dot2 = oracle.rope_neox_f64(xa, table[p1 + d]) @ oracle.rope_neox_f64(xk, table[p2 + d])
+        assert abs(dot1 - dot2) <= 1e-5 * (1 + abs(dot1))
+
+
+# ---------------------------------------------------------- whole epilogue ----
+
+@pytest.mark.parametrize("num_tokens", [64, 65])
+def test_page_identity_concat_and_scatter(num_tokens):
+    """The page's own boundary test: with rotation and FP8 off, q equals
+    cat(ql_nope, q_pe), the cache rows at the slots equal cat(kv_c, k_pe),
+    and every other cache byte keeps its initial zero."""
+    w = I.custom(num_tokens, 16, rope=False)
+    inp = I.make_inputs(w)
+    q, cache = oracle_run(w, inp)
+    want_q = bits(torch.cat([inp["ql_nope"], inp["q_pe"]], dim=-1))
+    assert np.array_equal(q, want_q)
+    rows = cache.reshape(-1, 576)
+    slots = inp["slot_mapping"].numpy()
+    assert np.array_equal(rows[slots], bits(torch.cat([inp["kv_c"], inp["k_pe"]], dim=-1)))
+    untouched = np.ones(rows.shape[0], dtype=bool)
+    untouched[slots] = False
+    assert np.all(rows[untouched] == 0)
+
+
+def _torch_textbook(w, inp):
+    """Library composition: cat, eager fp32 rotate_half rotation, bf16 cast or
+    clamp + float8_e4m3fn cast.  Used only to pin the oracle."""
+    T, H = w.tokens, w.heads
+    pe_q = inp["q_pe"].float()
+    pe_k = inp["k_pe"].float()
+    if w.rope:
+        cs = inp["rope_cos_sin"][inp["positions"].clamp(0, w.max_position - 1)]
+        cos = torch.cat([cs[:, :32], cs[:, :32]], dim=-1)
+        sin = torch.cat([cs[:, 32:], cs[:, 32:]], dim=-1)
+
+        def rot(x, c, s):
+            return x * c + torch.cat([-x[..., 32:], x[..., :32]], dim=-1) * s
+        pe_q = rot(pe_q, cos[:, None, :], sin[:, None, :])
+        pe_k = rot(pe_k, cos, sin)
+
+    def enc(nope_bf16, pe_f32, fp8, scale):
+        if fp8:
+            inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+            v = torch.cat([nope_bf16.float(), pe_f32], dim=-1) * inv
+            return bits(torch.clamp(v, -448, 448).to(torch.float8_e4m3fn))
+        return bits(torch.cat([nope_bf16, pe_f32.to(torch.bfloat16)], dim=-1))
+    q = enc(inp["ql_nope"], pe_q, w.q_fp8, w.q_scale)
+    kv = enc(inp["kv_c"], pe_k, w.kv_fp8, w.kv_scale)
+    return q, kv
+
+
+@pytest.mark.parametrize("name", ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8"])
+def test_oracle_matches_library_composition(name):
+    w = I.WORKLOADS[name]
+    inp = I.make_inputs(w)
+    q, cache = oracle_run(w, inp)
+    want_q, want_kv = _torch_textbook(w, inp)
+    assert np.array_equal(q, want_q)
+    rows = cache.reshape(-1, 576)
+    assert np.array_equal(rows[inp["slot_mapping"].numpy()], want_kv)
+
+
+@pytest.mark.parametrize("flags", [(True, False, False), (True, False, True), (True, True, False),
+                                   (False, True, True), (False, False, True)])
+def test_oracle_matches_library_composition_all_modes(flags):
+    rope, qf, kf = flags
+    w = I.custom(37, 5, num_blocks=3, rope=rope, q_fp8=qf, kv_fp8=kf, q_scale=0.03, kv_scale=0.2)
+    inp = I.make_inputs(w, seed=9)
+    q, cache = oracle_run(w, inp)
+    want_q, want_kv = _torch_textbook(w, inp)
+    assert np.array_equal(q, want_q)
+    assert np.array_equal(cache.reshape(-1, 576)[inp["slot_mapping"].numpy()], want_kv)
+
+
+def test_row_independence_prefix_property():
+    """Rows do not interact: the first 64 tokens of a 65-token call equal a
+    64-token call on the same inputs (the page's 64/65 boundary)."""
+    w65 = I.WORKLOADS["t65_h16_rope_fp8"]
+    inp = I.make_inputs(w65)
+    q65, c65 = oracle_run(w65, inp)
+    w64 = I.custom(64, 16, num_blocks=2, rope=True, q_fp8=True, kv_fp8=True)
+    inp64 = {k: (v[:64] if k in ("ql_nope", "q_pe", "kv_c", "k_pe", "slot_mapping", "positions") else v)
+             for k, v in inp.items()}
+    inp64 = {k: (v.contiguous() if isinstance(v, torch.Tensor) else v) for k, v in inp64.items()}
+    q64, c64 = oracle_run(w64, inp64)
+    assert np.array_equal(q65[:64], q64)
+    s65 = inp["slot_mapping"][64].item()
+    r65, r64 = c65.reshape(-1, 576).copy(), c64.reshape(-1, 576)
+    r65[s65] = 0
+    assert np.array_equal(r65, r64)
+
+
+def test_out_of_range_slots_leave_cache_untouched():
+    w = I.custom(6, 2, num_blocks=1, rope=True, kv_fp8=True)
+    inp = I.make_inputs(w, seed=4)
+    inp["slot_mapping"] = torch.tensor([-1, 64, 3, 1 << 40, -7, 63], dtype=torch.int64)
+    init = np.full((1, 64, 576), 0x5A, dtype=np.uint8)
+    q, cache = oracle_run(w, inp, cache_init=init)
+    rows = cache.reshape(-1, 576)
+    changed = np.nonzero(np.any(rows != 0x5A, axis=1))[0]
+    assert set(changed.tolist()) <= {3, 63}
+    assert np.any(rows[3] != 0x5A) and np.any(rows[63] != 0x5A)
+
+
+def test_positions_clamped_into_table():
+    w = I.custom(3, 2, num_blocks=1, rope=True, max_position=16)
+    inp = I.make_inputs(w, seed=8)
+    inp["positions"] = torch.tensor([-5, 16, 1000], dtype=torch.int64)
+    q, _ = oracle_run(w, inp)
+    inp2 = dict(inp)
+    inp2["positions"] = torch.tensor([0, 15, 15], dtype=torch.int64)
+    q2, _ = oracle_run(w, inp2)
+    assert np.array_equal(q, q2)
+
+
+def test_duplicate_slots_keep_later_token():
+    w = I.custom(3, 1, num_blocks=1)
+    inp = I.make_inputs(w, seed=2)
+    inp["slot_mapping"] = torch.tensor([5, 5, 9], dtype=torch.int64)
+    _, cache = oracle_run(w, inp)
+    want = bits(torch.cat([inp["kv_c"][1], inp["k_pe"][1]]))
+    assert np.array_equal(cache.reshape(-1, 576)[5], want)
