@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MLA decode epilogue on one MI355X.
+
+One step = one call of the epilogue (the whole path: index decode, loads,
+rotation, quantisation, q write and cache scatter) over one batch of
+synthetic input already resident in HBM.  The headline line is the
+8192-token prefill-sized workload (H=16, rotation on, bf16 q, e4m3 cache)
+as achieved HBM GB/s against the 8 TB/s peak, with the micro-second cost per
+call at 1, 64 and 65 tokens beside it.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_decode_concat_amd as M  # noqa: E402
+from mla_decode_concat_amd import inputs as I  # noqa: E402
+
+METRIC = "µs/call at 1/64/65 tokens + achieved HBM GB/s (% of peak) at 8192 tokens"
+HEADLINE = "t8192_h16_rope_kvfp8"
+LATENCY = ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8"]
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
+                  for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_t8192_h16_rope_kvfp8.json")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def algorithmic_bytes(w: I.Workload) -> int:
+    """Bytes the method must move per call: every input row read once (1152 B
+    of bf16 per 576-wide row), every output row written once (576 x 1 or 2
+    bytes), the slot (8 B) per token and, with rotation, the position (8 B)
+    and one 256-B cos/sin table row per token."""
+    T, H = w.tokens, w.heads
+    read = T * (H * 1152 + 1152 + 8 + (8 + 256 if w.rope else 0))
+    write = T * 576 * (H * (1 if w.q_fp8 else 2) + (1 if w.kv_fp8 else 2))
+    return read + write
+
+
+def flags_of(w: I.Workload) -> int:
+    return (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+
+
+class DeviceSet:
+    """One batch of device-resident inputs and outputs for a workload."""
+
+    def __init__(self, w: I.Workload, host: dict, dev: str):
+        self.w = w
+        self.t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in host.items()}
+        self.q = torch.empty(w.tokens, w.heads, I.ROW, device=dev,
+                             dtype=torch.float8_e4m3fn if w.q_fp8 else torch.bfloat16)
+        self.flags = flags_of(w)
+
+    def call(self):
+        t = self.t
+        M.mla_decode_q_concat_kv_insert(self.q, t["ql_nope"], t["q_pe"], t["kv_c"], t["k_pe"],
+                                        t["cache"], t["slot_mapping"], t["positions"],
+                                        t["rope_cos_sin"], t["q_scale"], t["kv_scale"], self.flags)
+
+
+def time_calls(sets: list, steps: int, warmup: int) -> dict:
+    """Back-to-back calls on torch's current stream (the stream the kernel is
+    launched on), bracketed by synchronisation; HIP events give the average
+    per-launch time, the host clock the wall time."""
+    for i in range(warmup):
+        sets[i % len(sets)].call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        sets[i % len(sets)].call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"event_ms_per_call": e0.elapsed_time(e1) / steps, "wall_ms_per_call": wall * 1e3 / steps}
+
+
+def time_graph(s: DeviceSet, calls: int = 100, replays: int = 20) -> float:
+    """µs per call when `calls` launches are captured in one HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        s.call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            s.call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(bytes_per_launch: int):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("sources_digest") != sources_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: I.Workload, host: dict, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on the same workload's host arrays."""
+    import numpy as np
+    import oracle
+
+    def bits(t):
+        t = t.contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.view(torch.uint8).numpy()
+
+    T, H = w.tokens, w.heads
+    q = np.zeros((T, H, I.ROW), dtype=np.uint8 if w.q_fp8 else np.uint16)
+    cache = bits(host["cache"]).copy()
+    args = (q, bits(host["ql_nope"]), bits(host["q_pe"]), bits(host["kv_c"]), bits(host["k_pe"]),
+            cache, host["slot_mapping"].numpy(),
+            host["positions"].numpy() if host["positions"] is not None else None,
+            host["rope_cos_sin"].numpy() if host["rope_cos_sin"] is not None else None,
+            w.q_scale, w.kv_scale, w.rope, w.q_fp8, w.kv_fp8)
+    oracle.insert(*args)                      # warm-up (page faults, thread start)
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.insert(*args)
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / runs
+    return {"value": round(algorithmic_bytes(w) / dt / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"full {w.name} workload ({w.describe()}), {runs} calls after 1 warm-up, "
+                      f"{dt * 1e3:.1f} ms per call"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, choices=I.WORKLOAD_ORDER)
+    ap.add_argument("--buffer-sets", type=int, default=4,
+                    help="independent input/output sets rotated between calls (defeats the MALL)")
+    ap.add_argument("--latency-steps", type=int, default=2000)
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch copies of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the epilogue has no cross-GPU step, and this "
+              "build runs and reports a single MI355X (use --gpus 1).", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB x {args.steps}")
+        return 0
+
+    M.load()
+    w = I.WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.describe()}")
+    host = I.make_inputs(w)
+    sets = []
+    for i in range(max(1, args.buffer_sets)):
+        sets.append(DeviceSet(w, host, dev))
+    torch.cuda.synchronize()
+    log(f"{len(sets)} buffer sets resident; timing {args.steps} steps after {args.warmup} warm-up")
+    r = time_calls(sets, args.steps, args.warmup)
+    nbytes = algorithmic_bytes(w)
+    ms = r["wall_ms_per_call"]
+    value = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (r["event_ms_per_call"] * 1e-3) / 1e9
+    log(f"{r['event_ms_per_call'] * 1e3:.2f} us/launch (events), {achieved:.0f} GB/s")
+    pl = M.plan(M.Dims(num_tokens=w.tokens, num_heads=w.heads, num_blocks=w.num_blocks,
+                       block_size=w.block_size, max_position=w.max_position), flags_of(w))
+    del sets
+    torch.cuda.empty_cache()
+
+    latency = {}
+    if not args.no_latency:
+        for name in LATENCY:
+            lw = I.WORKLOADS[name]
+            lh = I.make_inputs(lw)
+            lsets = [DeviceSet(lw, lh, dev)]
+            warm = time_calls(lsets, args.latency_steps, 50)
+            cold_sets = [DeviceSet(lw, lh, dev) for _ in range(8)]
+            cold = time_calls(cold_sets, args.latency_steps, 50)
+            gus = time_graph(lsets[0])
+            latency[name] = {"us_per_call": round(warm["event_ms_per_call"] * 1e3, 3),
+                             "us_per_call_8_sets": round(cold["event_ms_per_call"] * 1e3, 3),
+                             "us_per_call_graph": round(gus, 3),
+                             "bytes": algorithmic_bytes(lw)}
+            log(f"{name}: {latency[name]}")
+
+    traffic = traffic_entry(nbytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads,
+                   "cache": f"[{w.num_blocks},{w.block_size},576] {'e4m3' if w.kv_fp8 else 'bf16'}",
+                   "q_out": "e4m3" if w.q_fp8 else "bf16", "rope": w.rope,
+                   "buffer_sets": args.buffer_sets,
+                   "mapping": "small_t" if pl.mapping == 0 else "large_t",
+                   "grid_blocks": pl.grid_blocks, "block_threads": pl.block_threads,
+                   "chunks_per_lane": pl.chunks_per_lane},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "latency_us": latency,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_us": round(r["event_ms_per_call"] * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

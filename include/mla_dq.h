@@ -1,0 +1,147 @@
+/*
+ * mla_dq.h -- C ABI of the fused MLA decode epilogue for AMD MI355X (gfx950).
+ *
+ * The operation (prhub summary of vLLM PR #54896, "Kimi-K3 MLA decode
+ * kernel": sections "implementation breakdown" items 1-3 and "key source
+ * snippets"): for every token t, in one launch,
+ *
+ *   q_out[t, h, 0:512]   = enc_q( ql_nope[t, h, 0:512] )             h < H
+ *   q_out[t, h, 512:576] = enc_q( rope(q_pe[t, h, 0:64], pos[t]) )
+ *   row(s)[0:512]        = enc_kv( kv_c[t, 0:512] )                  s = slot_mapping[t]
+ *   row(s)[512:576]      = enc_kv( rope(k_pe[t, 0:64], pos[t]) )
+ *
+ * where row(s) is cache[s / block_size, s % block_size, :] of a paged latent
+ * cache [num_blocks, block_size, 576].  The page's test fixes the plain case
+ * (rotation and FP8 off): q is cat(ql_nope, q_pe) and the cache rows at the
+ * slots are cat(kv_c, k_pe); nothing else in the cache changes.
+ *
+ *   rope(x, p): NeoX half-split rotation; element i pairs with i+32, angle
+ *     from row p of the caller's table; y[i] = x[i]c - x[i+32]s,
+ *     y[i+32] = x[i+32]c + x[i]s in fp32, each product and sum rounded
+ *     separately.  Identity (bit copy) when MLA_DQ_ROPE is off.
+ *   enc (bf16 output): bit copy of untouched bf16 input, round-to-nearest-
+ *     even bf16 of rotated fp32 values.
+ *   enc (E4M3 output): OCP FP8 E4M3 of fl32(x * fl32(1/scale)) clamped to
+ *     [-448, 448] (NaN stays NaN), rounded to nearest even.
+ *
+ * Conventions where the page is silent:
+ *   - slots outside [0, num_blocks*block_size) (e.g. -1 padding) skip the
+ *     cache write for that token; the token's q rows are still written;
+ *   - positions outside [0, max_position) are clamped into the table;
+ *   - with repeated slots, which token's row remains is unspecified.
+ *
+ * Threading and ownership: the library allocates nothing, keeps no state
+ * beyond a read-once tuning environment variable, and may be called from
+ * several threads.  Every buffer belongs to the caller.  Work is enqueued on
+ * `stream` and the call returns without synchronising.
+ */
+#ifndef MLA_DQ_H
+#define MLA_DQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- flags ------------------------------------------------------------- */
+/* Feature switches; the page's kernel has the same three as template
+ * arguments (section "key source snippets"). */
+#define MLA_DQ_ROPE    (1u << 0) /* rotate the 64-wide tails of q and k     */
+#define MLA_DQ_Q_FP8   (1u << 1) /* q_out holds E4M3 codes (else bf16)      */
+#define MLA_DQ_KV_FP8  (1u << 2) /* cache holds E4M3 codes (else bf16)      */
+/* Mapping overrides for tests and sweeps.  By default the library picks the
+ * latency mapping (one 16-byte chunk per lane, wavefronts per row) for small
+ * token counts and the throughput mapping (several chunks per lane, rows per
+ * wavefront) above a measured threshold; the page's launcher makes the same
+ * token-count-dependent choice ("implementation breakdown" items 1 and 3). */
+#define MLA_DQ_FORCE_SMALL_T (1u << 8)
+#define MLA_DQ_FORCE_LARGE_T (1u << 9)
+
+/* ---- return codes ------------------------------------------------------ */
+#define MLA_DQ_OK          0
+#define MLA_DQ_ERR_NULL   -1 /* a required pointer (or dims) is NULL               */
+#define MLA_DQ_ERR_ALIGN  -2 /* pointer or stride misaligned (see below)          */
+#define MLA_DQ_ERR_DIM    -3 /* a dimension or stride is out of range             */
+#define MLA_DQ_ERR_FLAGS  -4 /* unknown flag bit, or both FORCE bits             */
+#define MLA_DQ_ERR_LAUNCH -5 /* the HIP launch reported an error                  */
+#define MLA_DQ_ERR_ALIAS  -6 /* q_out overlaps an input or the cache              */
+
+/* Shapes and input strides.  Strides are in elements (bf16) and let the
+ * inputs be views of larger buffers, as the page's neighbouring GEMM change
+ * allows for row-strided activations (prhub summary of vLLM PR #54565,
+ * "implementation breakdown" items 1-2): the inner stride is 1 and every row
+ * stride is a multiple of 8 elements (16 bytes).  q_out and cache are dense. */
+typedef struct mla_dq_dims {
+    int64_t num_tokens;       /* T >= 0; T == 0 returns MLA_DQ_OK, no launch   */
+    int64_t num_heads;        /* H >= 1                                         */
+    int64_t num_blocks;       /* cache blocks, >= 1                             */
+    int64_t block_size;       /* slots per block, >= 1                          */
+    int64_t max_position;     /* rows of rope_cos_sin; >= 1 when MLA_DQ_ROPE    */
+    int64_t ql_nope_stride_t; /* ql_nope[t, h, e] at t*st + h*sh + e            */
+    int64_t ql_nope_stride_h;
+    int64_t q_pe_stride_t;    /* q_pe[t, h, e] at t*st + h*sh + e               */
+    int64_t q_pe_stride_h;
+    int64_t kv_c_stride_t;    /* kv_c[t, e] at t*st + e                         */
+    int64_t k_pe_stride_t;    /* k_pe[t, e] at t*st + e                         */
+} mla_dq_dims;
+
+/*
+ * The fused epilogue (prhub summary of vLLM PR #54896: the launcher named in
+ * "implementation breakdown" item 3 and the op the test calls in "key source
+ * snippets").  All pointers are DEVICE pointers except `dims`, a host pointer.
+ *
+ *   q_out         [T, H, 576] dense; bf16, or E4M3 bytes with MLA_DQ_Q_FP8.
+ *                 16-byte aligned.  Written in full.
+ *   ql_nope       bf16 [T, H, 512] (strided, see mla_dq_dims), 16-B aligned.
+ *   q_pe          bf16 [T, H, 64]  (strided), 16-B aligned.
+ *   kv_c          bf16 [T, 512]    (strided), 16-B aligned.
+ *   k_pe          bf16 [T, 64]     (strided), 16-B aligned.
+ *   cache         [num_blocks, block_size, 576] dense; bf16, or E4M3 bytes
+ *                 with MLA_DQ_KV_FP8.  16-B aligned.  Only the rows at valid
+ *                 slots are written.
+ *   slot_mapping  int64 [T], 8-B aligned.
+ *   positions     int64 [T], 8-B aligned; required with MLA_DQ_ROPE, else
+ *                 ignored (may be NULL).
+ *   rope_cos_sin  fp32 [max_position, 64]: row p = cos of the 32 angles, then
+ *                 their sin.  16-B aligned; required with MLA_DQ_ROPE.
+ *   q_scale       fp32 scalar; required with MLA_DQ_Q_FP8 (may be NULL else).
+ *   kv_scale      fp32 scalar; required with MLA_DQ_KV_FP8 (may be NULL else).
+ *   flags         MLA_DQ_* bits.
+ *   dims          host pointer to shapes and strides.
+ *   stream        a hipStream_t (NULL = the null stream).
+ *
+ * Returns MLA_DQ_OK after enqueueing, or a negative MLA_DQ_ERR_* code.  On a
+ * validation error nothing is launched; validation reads no device memory.
+ */
+int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* q_pe,
+                                  const void* kv_c, const void* k_pe, void* cache,
+                                  const int64_t* slot_mapping, const int64_t* positions,
+                                  const float* rope_cos_sin, const float* q_scale,
+                                  const float* kv_scale, uint32_t flags,
+                                  const mla_dq_dims* dims, void* stream);
+
+/* Human-readable text for a return code; never NULL, static storage. */
+const char* mla_dq_strerror(int code);
+
+/* The launch the library would make for these dims and flags: host-only, no
+ * GPU needed, no device memory touched.  mapping is 0 for the small-T
+ * (latency) mapping and 1 for the large-T (throughput) mapping. */
+typedef struct mla_dq_launch_plan {
+    int32_t mapping;          /* 0 = small-T, 1 = large-T                   */
+    int32_t chunks_per_lane;  /* 16-byte input chunks handled by each lane  */
+    int32_t block_threads;    /* threads per workgroup                      */
+    int32_t small_t_max;      /* token threshold in force                   */
+    int64_t grid_blocks;      /* workgroups launched                        */
+    int64_t total_chunks;     /* T * (H + 1) * 72                           */
+} mla_dq_launch_plan;
+
+/* Returns MLA_DQ_OK and fills *plan, or a negative code for bad dims/flags.
+ * (Pointers are not checked here; T == 0 gives grid_blocks = 0.) */
+int mla_dq_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DQ_H */

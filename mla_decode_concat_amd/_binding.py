@@ -1,0 +1,217 @@
+"""ctypes binding of libmla_dq.so (the C ABI in include/mla_dq.h).
+
+Argument marshalling only: torch tensors -> device pointers, shapes and
+strides -> mla_dq_dims, torch's current HIP stream -> the stream argument.
+Every step of the epilogue runs in the library's gfx950 kernel; there is no
+fallback.  If the library is missing it is built once; if that fails, or no
+GPU is present, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+# Flag bits and return codes of include/mla_dq.h.
+ROPE = 1 << 0
+Q_FP8 = 1 << 1
+KV_FP8 = 1 << 2
+FORCE_SMALL_T = 1 << 8
+FORCE_LARGE_T = 1 << 9
+
+OK = 0
+ERR_NULL = -1
+ERR_ALIGN = -2
+ERR_DIM = -3
+ERR_FLAGS = -4
+ERR_LAUNCH = -5
+ERR_ALIAS = -6
+
+EXPORTED_SYMBOLS = ("mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_tokens", "num_heads", "num_blocks", "block_size", "max_position",
+        "ql_nope_stride_t", "ql_nope_stride_h", "q_pe_stride_t", "q_pe_stride_h",
+        "kv_c_stride_t", "k_pe_stride_t")]
+
+
+class LaunchPlan(ctypes.Structure):
+    _fields_ = [("mapping", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32), ("small_t_max", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int64), ("total_chunks", ctypes.c_int64)]
+
+
+class MlaDqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mla_dq error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla_dq.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        vp, i64p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        lib.mla_decode_q_concat_kv_insert.argtypes = [
+            vp, vp, vp, vp, vp, vp, i64p, i64p, f32p, f32p, f32p, ctypes.c_uint32,
+            ctypes.POINTER(Dims), vp]
+        lib.mla_decode_q_concat_kv_insert.restype = ctypes.c_int
+        lib.mla_dq_strerror.argtypes = [ctypes.c_int]
+        lib.mla_dq_strerror.restype = ctypes.c_char_p
+        lib.mla_dq_plan.argtypes = [ctypes.POINTER(Dims), ctypes.c_uint32, ctypes.POINTER(LaunchPlan)]
+        lib.mla_dq_plan.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    return load().mla_dq_strerror(int(code)).decode()
+
+
+def plan(dims: Dims, flags: int) -> LaunchPlan:
+    p = LaunchPlan()
+    rc = load().mla_dq_plan(ctypes.byref(dims), ctypes.c_uint32(flags), ctypes.byref(p))
+    if rc != OK:
+        raise MlaDqError(rc, strerror(rc))
+    return p
+
+
+def raw_call(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+             q_scale, kv_scale, flags: int, dims: Dims, stream) -> int:
+    """Call the C entry point with integer addresses; returns its code."""
+    return load().mla_decode_q_concat_kv_insert(
+        q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+        q_scale, kv_scale, ctypes.c_uint32(flags), ctypes.byref(dims), stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _dims(ql_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin) -> Dims:
+    d = Dims()
+    d.num_tokens, d.num_heads = ql_nope.shape[0], ql_nope.shape[1]
+    d.num_blocks, d.block_size = cache.shape[0], cache.shape[1]
+    d.max_position = rope_cos_sin.shape[0] if rope_cos_sin is not None else 0
+    d.ql_nope_stride_t, d.ql_nope_stride_h = ql_nope.stride(0), ql_nope.stride(1)
+    d.q_pe_stride_t, d.q_pe_stride_h = q_pe.stride(0), q_pe.stride(1)
+    d.kv_c_stride_t, d.k_pe_stride_t = kv_c.stride(0), k_pe.stride(0)
+    return d
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _check(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def mla_decode_q_concat_kv_insert(q_out: torch.Tensor, ql_nope: torch.Tensor, q_pe: torch.Tensor,
+                                  kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
+                                  slot_mapping: torch.Tensor, positions: torch.Tensor | None = None,
+                                  rope_cos_sin: torch.Tensor | None = None,
+                                  q_scale: torch.Tensor | None = None,
+                                  kv_scale: torch.Tensor | None = None, flags: int = 0,
+                                  stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the fused epilogue on ``stream`` (default: torch's current
+    stream).  Writes ``q_out`` [T,H,576] and the cache rows at the slots.
+
+    Flags are the MLA_DQ_* bits; the FP8 bits must agree with the dtypes of
+    ``q_out`` and ``cache`` (bf16, or float8_e4m3fn / uint8 codes)."""
+    T = ql_nope.shape[0]
+    _check(ql_nope.dim() == 3 and ql_nope.shape[2] == 512, "ql_nope must be [T, H, 512]")
+    H = ql_nope.shape[1]
+    _check(tuple(q_pe.shape) == (T, H, 64), "q_pe must be [T, H, 64]")
+    _check(tuple(kv_c.shape) == (T, 512) and tuple(k_pe.shape) == (T, 64),
+           "kv_c must be [T, 512] and k_pe [T, 64]")
+    _check(tuple(q_out.shape) == (T, H, 576) and q_out.is_contiguous(),
+           "q_out must be a contiguous [T, H, 576] tensor")
+    _check(cache.dim() == 3 and cache.shape[2] == 576 and cache.is_contiguous(),
+           "cache must be a contiguous [num_blocks, block_size, 576] tensor")
+    for name, t in (("ql_nope", ql_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe)):
+        _check(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+        _check(t.stride(-1) == 1, f"{name} must have unit inner stride")
+    _check(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,)
+           and slot_mapping.is_contiguous(), "slot_mapping must be a contiguous int64 [T]")
+    q_fp8 = bool(flags & Q_FP8)
+    kv_fp8 = bool(flags & KV_FP8)
+    _check((q_out.dtype in _FP8) == q_fp8 and (q_fp8 or q_out.dtype == torch.bfloat16),
+           "q_out dtype must be e4m3 with Q_FP8, bfloat16 without")
+    _check((cache.dtype in _FP8) == kv_fp8 and (kv_fp8 or cache.dtype == torch.bfloat16),
+           "cache dtype must be e4m3 with KV_FP8, bfloat16 without")
+    if flags & ROPE:
+        _check(positions is not None and rope_cos_sin is not None,
+               "ROPE needs positions and rope_cos_sin")
+        _check(positions.dtype == torch.int64 and tuple(positions.shape) == (T,)
+               and positions.is_contiguous(), "positions must be a contiguous int64 [T]")
+        _check(rope_cos_sin.dtype == torch.float32 and rope_cos_sin.dim() == 2
+               and rope_cos_sin.shape[1] == 64 and rope_cos_sin.is_contiguous(),
+               "rope_cos_sin must be a contiguous fp32 [max_position, 64]")
+    if q_fp8:
+        _check(q_scale is not None and q_scale.dtype == torch.float32 and q_scale.numel() >= 1,
+               "Q_FP8 needs an fp32 q_scale")
+    if kv_fp8:
+        _check(kv_scale is not None and kv_scale.dtype == torch.float32 and kv_scale.numel() >= 1,
+               "KV_FP8 needs an fp32 kv_scale")
+    tensors = [q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+               q_scale, kv_scale]
+    dev = q_out.device
+    _check(dev.type == "cuda", "tensors must be on a GPU")
+    for t in tensors:
+        if t is not None:
+            _check(t.device == dev, "all tensors must be on the same GPU")
+    dims = _dims(ql_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = raw_call(_ptr(q_out), _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(cache),
+                      _ptr(slot_mapping), _ptr(positions), _ptr(rope_cos_sin), _ptr(q_scale),
+                      _ptr(kv_scale), flags, dims, stream.cuda_stream)
+    if rc != OK:
+        raise MlaDqError(rc, strerror(rc))
+
+
+def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch.Tensor,
+                                              kv_c: torch.Tensor, k_pe: torch.Tensor,
+                                              cache: torch.Tensor, slot_mapping: torch.Tensor,
+                                              positions: torch.Tensor | None = None,
+                                              rope_cos_sin: torch.Tensor | None = None,
+                                              q_scale: torch.Tensor | None = None,
+                                              kv_scale: torch.Tensor | None = None,
+                                              q_fp8: bool = False) -> torch.Tensor:
+    """The page's user-level call: allocates and returns q [T, H, 576] and
+    updates ``cache`` in place.  RoPE is on when positions and a table are
+    given; the cache's FP8-ness follows its dtype."""
+    T, H = ql_nope.shape[0], ql_nope.shape[1]
+    flags = 0
+    if positions is not None or rope_cos_sin is not None:
+        flags |= ROPE
+    if q_fp8:
+        flags |= Q_FP8
+    if cache.dtype in _FP8:
+        flags |= KV_FP8
+    q = torch.empty((T, H, 576), device=ql_nope.device,
+                    dtype=torch.float8_e4m3fn if q_fp8 else torch.bfloat16)
+    mla_decode_q_concat_kv_insert(q, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                                  rope_cos_sin, q_scale, kv_scale, flags)
+    return q

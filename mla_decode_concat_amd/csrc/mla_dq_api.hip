@@ -1,0 +1,204 @@
+// C ABI of the fused MLA decode epilogue: argument validation, the choice of
+// mapping, and the launch on the caller's stream.  The contract is in
+// include/mla_dq.h.
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "mla_dq.h"
+#include "mla_dq_internal.h"
+
+namespace mla_dq {
+namespace {
+
+constexpr int kNothingToDo = 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range [lo, hi) touched by a strided bf16 tensor [T, H, width].
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+Extent extent3(const void* p, int64_t T, int64_t H, int64_t st, int64_t sh, int64_t width,
+               int64_t elem_bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    const int64_t last = (T - 1) * st + (H - 1) * sh + width;
+    return Extent{b, b + uintptr_t(last) * uintptr_t(elem_bytes)};
+}
+
+bool overlap(Extent x, Extent y) { return x.lo < y.hi && y.lo < x.hi; }
+
+int small_t_max() {
+    static const int v = [] {
+        const char* s = getenv("MLA_DQ_SMALL_T_MAX");
+        if (s == nullptr || *s == '\0') return kDefaultSmallTMax;
+        char* end = nullptr;
+        const long n = strtol(s, &end, 10);
+        if (end == s || n < 0 || n > INT_MAX) return kDefaultSmallTMax;
+        return int(n);
+    }();
+    return v;
+}
+
+// Checks that do not need any pointer: flags and shapes.
+int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
+    if (d == nullptr) return MLA_DQ_ERR_NULL;
+    const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FORCE_SMALL_T |
+                           MLA_DQ_FORCE_LARGE_T;
+    if (flags & ~known) return MLA_DQ_ERR_FLAGS;
+    if ((flags & MLA_DQ_FORCE_SMALL_T) && (flags & MLA_DQ_FORCE_LARGE_T)) return MLA_DQ_ERR_FLAGS;
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    if (T < 0 || H < 1 || d->num_blocks < 1 || d->block_size < 1) return MLA_DQ_ERR_DIM;
+    // Flat chunk indices are 32-bit on the device.
+    if (H > INT32_MAX / kRowChunks - 1) return MLA_DQ_ERR_DIM;
+    if (T > INT32_MAX / (kRowChunks * (H + 1))) return MLA_DQ_ERR_DIM;
+    if (d->num_blocks > (INT64_MAX / 2048) / d->block_size) return MLA_DQ_ERR_DIM;
+    if (flags & MLA_DQ_ROPE) {
+        if (d->max_position < 1 || d->max_position > (int64_t(1) << 40)) return MLA_DQ_ERR_DIM;
+    }
+    const int64_t strides[] = {d->ql_nope_stride_t, d->ql_nope_stride_h, d->q_pe_stride_t,
+                               d->q_pe_stride_h, d->kv_c_stride_t, d->k_pe_stride_t};
+    for (int64_t s : strides)
+        if (s < 0 || s > (int64_t(1) << 40)) return MLA_DQ_ERR_DIM;
+    if (T == 0) return kNothingToDo;
+    // Row strides must keep every 16-byte chunk aligned; a stride that is
+    // never used (one token, one head) may be anything.
+    const bool many_t = T > 1, many_h = H > 1;
+    if ((many_t && (d->ql_nope_stride_t % 8 || d->q_pe_stride_t % 8 || d->kv_c_stride_t % 8 ||
+                    d->k_pe_stride_t % 8)) ||
+        (many_h && (d->ql_nope_stride_h % 8 || d->q_pe_stride_h % 8)))
+        return MLA_DQ_ERR_ALIGN;
+    return MLA_DQ_OK;
+}
+
+}  // namespace
+
+int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
+    if (out == nullptr) return MLA_DQ_ERR_NULL;
+    const int rc = check_flags_dims(flags, d);
+    if (rc < 0) return rc;
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    const int thr = small_t_max();
+    int mapping;
+    if (flags & MLA_DQ_FORCE_SMALL_T)
+        mapping = 0;
+    else if (flags & MLA_DQ_FORCE_LARGE_T)
+        mapping = 1;
+    else
+        mapping = T <= thr ? 0 : 1;
+    const int cpl = mapping == 0 ? kSmallCpl : kLargeCpl;
+    const int block = mapping == 0 ? kSmallBlock : kLargeBlock;
+    const int64_t total = T * (H + 1) * kRowChunks;
+    const int64_t per_block = int64_t(cpl) * block;
+    out->mapping = mapping;
+    out->chunks_per_lane = cpl;
+    out->block_threads = block;
+    out->small_t_max = thr;
+    out->total_chunks = total;
+    out->grid_blocks = (total + per_block - 1) / per_block;
+    return MLA_DQ_OK;
+}
+
+int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_c,
+             const void* k_pe, void* cache, const int64_t* slot_mapping,
+             const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+             const float* kv_scale, uint32_t flags, const mla_dq_dims* d) {
+    const int rc = check_flags_dims(flags, d);
+    if (rc != MLA_DQ_OK) return rc;
+    const bool rope = flags & MLA_DQ_ROPE, qf8 = flags & MLA_DQ_Q_FP8, kvf8 = flags & MLA_DQ_KV_FP8;
+    if (!q_out || !ql_nope || !q_pe || !kv_c || !k_pe || !cache || !slot_mapping)
+        return MLA_DQ_ERR_NULL;
+    if (rope && (!positions || !rope_cos_sin)) return MLA_DQ_ERR_NULL;
+    if ((qf8 && !q_scale) || (kvf8 && !kv_scale)) return MLA_DQ_ERR_NULL;
+    if (!aligned(q_out, 16) || !aligned(ql_nope, 16) || !aligned(q_pe, 16) || !aligned(kv_c, 16) ||
+        !aligned(k_pe, 16) || !aligned(cache, 16) || !aligned(slot_mapping, 8))
+        return MLA_DQ_ERR_ALIGN;
+    if (rope && (!aligned(positions, 8) || !aligned(rope_cos_sin, 16))) return MLA_DQ_ERR_ALIGN;
+    if ((qf8 && !aligned(q_scale, 4)) || (kvf8 && !aligned(kv_scale, 4))) return MLA_DQ_ERR_ALIGN;
+
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    const int64_t slots = d->num_blocks * d->block_size;
+    const Extent q{reinterpret_cast<uintptr_t>(q_out),
+                   reinterpret_cast<uintptr_t>(q_out) + uintptr_t(T * H * 576 * (qf8 ? 1 : 2))};
+    const Extent c{reinterpret_cast<uintptr_t>(cache),
+                   reinterpret_cast<uintptr_t>(cache) + uintptr_t(slots * 576 * (kvf8 ? 1 : 2))};
+    const Extent in[] = {
+        extent3(ql_nope, T, H, d->ql_nope_stride_t, d->ql_nope_stride_h, 512, 2),
+        extent3(q_pe, T, H, d->q_pe_stride_t, d->q_pe_stride_h, 64, 2),
+        extent3(kv_c, T, 1, d->kv_c_stride_t, 0, 512, 2),
+        extent3(k_pe, T, 1, d->k_pe_stride_t, 0, 64, 2),
+        Extent{reinterpret_cast<uintptr_t>(slot_mapping),
+               reinterpret_cast<uintptr_t>(slot_mapping) + uintptr_t(T * 8)},
+    };
+    if (overlap(q, c)) return MLA_DQ_ERR_ALIAS;
+    for (const Extent& e : in)
+        if (overlap(q, e) || overlap(c, e)) return MLA_DQ_ERR_ALIAS;
+    return MLA_DQ_OK;
+}
+
+}  // namespace mla_dq
+
+extern "C" {
+
+int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* q_pe,
+                                  const void* kv_c, const void* k_pe, void* cache,
+                                  const int64_t* slot_mapping, const int64_t* positions,
+                                  const float* rope_cos_sin, const float* q_scale,
+                                  const float* kv_scale, uint32_t flags,
+                                  const mla_dq_dims* dims, void* stream) {
+    int rc = mla_dq::validate(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                              rope_cos_sin, q_scale, kv_scale, flags, dims);
+    if (rc == mla_dq::kNothingToDo) return MLA_DQ_OK;
+    if (rc != MLA_DQ_OK) return rc;
+    mla_dq_launch_plan p;
+    rc = mla_dq::plan(dims, flags, &p);
+    if (rc != MLA_DQ_OK) return rc;
+
+    mla_dq::KernelArgs a;
+    a.q_out = static_cast<uint8_t*>(q_out);
+    a.ql_nope = static_cast<const uint16_t*>(ql_nope);
+    a.q_pe = static_cast<const uint16_t*>(q_pe);
+    a.kv_c = static_cast<const uint16_t*>(kv_c);
+    a.k_pe = static_cast<const uint16_t*>(k_pe);
+    a.cache = static_cast<uint8_t*>(cache);
+    a.slot_mapping = slot_mapping;
+    a.positions = positions;
+    a.rope_cos_sin = rope_cos_sin;
+    a.q_scale = q_scale;
+    a.kv_scale = kv_scale;
+    a.ql_nope_st = dims->ql_nope_stride_t;
+    a.ql_nope_sh = dims->ql_nope_stride_h;
+    a.q_pe_st = dims->q_pe_stride_t;
+    a.q_pe_sh = dims->q_pe_stride_h;
+    a.kv_c_st = dims->kv_c_stride_t;
+    a.k_pe_st = dims->k_pe_stride_t;
+    a.num_slots = dims->num_blocks * dims->block_size;
+    a.max_position = (flags & MLA_DQ_ROPE) ? dims->max_position : 1;
+    a.rows_per_token = make_fastdiv31(uint32_t(dims->num_heads + 1));
+    a.num_heads = uint32_t(dims->num_heads);
+    a.total_chunks = uint32_t(p.total_chunks);
+    const hipError_t e = mla_dq::launch(a, p, flags, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
+}
+
+int mla_dq_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* plan) {
+    return mla_dq::plan(dims, flags, plan);
+}
+
+const char* mla_dq_strerror(int code) {
+    switch (code) {
+        case MLA_DQ_OK: return "success";
+        case MLA_DQ_ERR_NULL: return "a required pointer is NULL";
+        case MLA_DQ_ERR_ALIGN: return "pointer or stride misaligned (16-byte rows, 8-element strides)";
+        case MLA_DQ_ERR_DIM: return "dimension or stride out of range";
+        case MLA_DQ_ERR_FLAGS: return "unknown flag bit or conflicting mapping overrides";
+        case MLA_DQ_ERR_LAUNCH: return "HIP kernel launch failed";
+        case MLA_DQ_ERR_ALIAS: return "q_out overlaps an input or the cache, or the cache overlaps an input";
+        default: return "unknown mla_dq error code";
+    }
+}
+
+}  // extern "C"

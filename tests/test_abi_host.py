@@ -1,0 +1,254 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+function include/mla_dq.h declares, argument validation returns the documented
+codes without launching, the launch plan follows the token threshold, and
+the device-side fast division is exact."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import mla_decode_concat_amd as M
+from mla_decode_concat_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_dq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) == {"mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan"}
+    lib = ctypes.CDLL(B.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_flag_and_code_values_match_header():
+    text = open(HEADER).read()
+
+    def val(name):
+        m = re.search(rf"#define {name}\s+\(?([-\w<\s]+)\)?", text)
+        return eval(m.group(1).replace("u", ""))
+    assert val("MLA_DQ_ROPE") == M.ROPE and val("MLA_DQ_Q_FP8") == M.Q_FP8
+    assert val("MLA_DQ_KV_FP8") == M.KV_FP8
+    assert val("MLA_DQ_FORCE_SMALL_T") == M.FORCE_SMALL_T
+    assert val("MLA_DQ_FORCE_LARGE_T") == M.FORCE_LARGE_T
+    for name, v in (("MLA_DQ_ERR_NULL", B.ERR_NULL), ("MLA_DQ_ERR_ALIGN", B.ERR_ALIGN),
+                    ("MLA_DQ_ERR_DIM", B.ERR_DIM), ("MLA_DQ_ERR_FLAGS", B.ERR_FLAGS),
+                    ("MLA_DQ_ERR_LAUNCH", B.ERR_LAUNCH), ("MLA_DQ_ERR_ALIAS", B.ERR_ALIAS)):
+        assert int(re.search(rf"#define {name}\s+(-?\d+)", text).group(1)) == v
+
+
+def test_strerror_every_code():
+    seen = set()
+    for c in (0, -1, -2, -3, -4, -5, -6):
+        s = M.strerror(c)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in M.strerror(-99)
+
+
+# ---- validation (fake, never-dereferenced addresses; nothing launches) -----
+
+BASE = 1 << 36          # fake device addresses, 16-byte aligned, far apart
+GAP = 1 << 32
+
+
+def _dims(T=4, H=2, NB=1, BS=64, maxpos=16):
+    d = B.Dims()
+    d.num_tokens, d.num_heads, d.num_blocks, d.block_size, d.max_position = T, H, NB, BS, maxpos
+    d.ql_nope_stride_t, d.ql_nope_stride_h = H * 512, 512
+    d.q_pe_stride_t, d.q_pe_stride_h = H * 64, 64
+    d.kv_c_stride_t, d.k_pe_stride_t = 512, 64
+    return d
+
+
+def _ptrs():
+    names = ["q_out", "ql_nope", "q_pe", "kv_c", "k_pe", "cache", "slots", "pos", "cs", "qs", "ks"]
+    return {n: BASE + i * GAP for i, n in enumerate(names)}
+
+
+def _call(p, flags, dims):
+    return B.load().mla_decode_q_concat_kv_insert(
+        p["q_out"], p["ql_nope"], p["q_pe"], p["kv_c"], p["k_pe"], p["cache"], p["slots"],
+        p["pos"], p["cs"], p["qs"], p["ks"], ctypes.c_uint32(flags),
+        ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_null_dims():
+    assert _call(_ptrs(), 0, None) == B.ERR_NULL
+
+
+@pytest.mark.parametrize("flags", [1 << 3, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T])
+def test_bad_flags(flags):
+    assert _call(_ptrs(), flags, _dims()) == B.ERR_FLAGS
+
+
+@pytest.mark.parametrize("field,value", [("num_tokens", -1), ("num_heads", 0), ("num_blocks", 0),
+                                         ("block_size", 0), ("ql_nope_stride_t", -8)])
+def test_bad_dims(field, value):
+    d = _dims()
+    setattr(d, field, value)
+    assert _call(_ptrs(), 0, d) == B.ERR_DIM
+
+
+def test_too_many_chunks_for_32bit_indices():
+    d = _dims(T=(1 << 31) // (72 * 3) + 1, H=2)
+    assert _call(_ptrs(), 0, d) == B.ERR_DIM
+
+
+def test_rope_needs_table_rows():
+    assert _call(_ptrs(), M.ROPE, _dims(maxpos=0)) == B.ERR_DIM
+
+
+def test_zero_tokens_is_a_no_op_even_with_null_pointers():
+    p = {k: None for k in _ptrs()}
+    assert _call(p, M.ROPE | M.Q_FP8 | M.KV_FP8, _dims(T=0)) == B.OK
+
+
+@pytest.mark.parametrize("name", ["q_out", "ql_nope", "q_pe", "kv_c", "k_pe", "cache", "slots"])
+def test_null_required_pointer(name):
+    p = _ptrs()
+    p[name] = None
+    assert _call(p, 0, _dims()) == B.ERR_NULL
+
+
+@pytest.mark.parametrize("flags,name", [(M.ROPE, "pos"), (M.ROPE, "cs"), (M.Q_FP8, "qs"),
+                                        (M.KV_FP8, "ks")])
+def test_null_pointer_needed_by_flag(flags, name):
+    p = _ptrs()
+    p[name] = None
+    assert _call(p, flags, _dims()) == B.ERR_NULL
+
+
+def test_optional_pointers_may_be_null_when_unused():
+    p = _ptrs()
+    for n in ("pos", "cs", "qs", "ks"):
+        p[n] = None
+    # passes validation, then q_out overlapping the cache is caught before launch
+    p["q_out"] = p["cache"]
+    assert _call(p, 0, _dims()) == B.ERR_ALIAS
+
+
+@pytest.mark.parametrize("name,off", [("q_out", 8), ("ql_nope", 2), ("cache", 8), ("slots", 4)])
+def test_misaligned_pointer(name, off):
+    p = _ptrs()
+    p[name] += off
+    assert _call(p, 0, _dims()) == B.ERR_ALIGN
+
+
+@pytest.mark.parametrize("field", ["ql_nope_stride_t", "ql_nope_stride_h", "q_pe_stride_t",
+                                   "q_pe_stride_h", "kv_c_stride_t", "k_pe_stride_t"])
+def test_misaligned_stride(field):
+    d = _dims()
+    setattr(d, field, getattr(d, field) + 4)
+    assert _call(_ptrs(), 0, d) == B.ERR_ALIGN
+
+
+def test_unused_strides_unchecked_for_one_token_one_head():
+    d = _dims(T=1, H=1)
+    d.ql_nope_stride_t = d.q_pe_stride_t = d.kv_c_stride_t = d.k_pe_stride_t = 3
+    d.ql_nope_stride_h = d.q_pe_stride_h = 5
+    p = _ptrs()
+    p["q_out"] = p["cache"]       # reach the alias check: strides passed
+    assert _call(p, 0, d) == B.ERR_ALIAS
+
+
+def test_q_out_overlapping_input_is_rejected():
+    p = _ptrs()
+    p["q_out"] = p["ql_nope"] + 1024
+    assert _call(p, 0, _dims()) == B.ERR_ALIAS
+
+
+def test_cache_overlapping_input_is_rejected():
+    p = _ptrs()
+    p["cache"] = p["kv_c"] + 16
+    assert _call(p, 0, _dims()) == B.ERR_ALIAS
+
+
+# ---- launch plan -------------------------------------------------------------
+
+def test_plan_threshold_and_coverage():
+    for T in (1, 2, 63, 64, 65, 256, 8192):
+        for H in (1, 16, 128):
+            pl = M.plan(_dims(T=T, H=H), 0)
+            assert pl.mapping == (0 if T <= pl.small_t_max else 1)
+            assert pl.total_chunks == T * (H + 1) * 72
+            per = pl.chunks_per_lane * pl.block_threads
+            assert pl.grid_blocks * per >= pl.total_chunks > (pl.grid_blocks - 1) * per
+            assert pl.block_threads % 64 == 0
+    assert M.plan(_dims(T=1), M.FORCE_LARGE_T).mapping == 1
+    assert M.plan(_dims(T=10 ** 5), M.FORCE_SMALL_T).mapping == 0
+    assert M.plan(_dims(T=0), 0).grid_blocks == 0
+
+
+def test_plan_rejects_bad_input():
+    with pytest.raises(M.MlaDqError):
+        M.plan(_dims(T=-1), 0)
+    with pytest.raises(M.MlaDqError):
+        M.plan(_dims(), M.FORCE_SMALL_T | M.FORCE_LARGE_T)
+
+
+def test_threshold_env_override_in_fresh_process():
+    code = ("import mla_decode_concat_amd as M; from mla_decode_concat_amd import _binding as B;"
+            "d=B.Dims(); d.num_tokens=100; d.num_heads=16; d.num_blocks=1; d.block_size=64;"
+            "p=M.plan(d,0); print(p.small_t_max, p.mapping)")
+    env = dict(os.environ, MLA_DQ_SMALL_T_MAX="128", PYTHONPATH=ROOT)
+    out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["128", "0"]
+
+
+# ---- fast division used by the kernel's index decode --------------------------
+
+FASTDIV_CHECK = r"""
+#include "fastdiv.h"
+#include <stdio.h>
+int main() {
+    unsigned long long checked = 0;
+    for (uint32_t d = 1; d <= 4096; ++d) {
+        FastDiv31 f = make_fastdiv31(d);
+        for (uint32_t n = 0; n < 70000; ++n) {
+            if (fastdiv31(n, f) != n / d) { printf("FAIL d=%u n=%u\n", d, n); return 1; }
+            ++checked;
+        }
+        const uint32_t top = 0x7FFFFFFFu;
+        for (uint32_t k = 0; k < 4096; ++k) {
+            uint32_t n = top - k * 524287u;
+            if (fastdiv31(n, f) != n / d) { printf("FAIL d=%u n=%u\n", d, n); return 1; }
+            uint32_t m = (n / d) * d;   /* multiples and their neighbours */
+            if (fastdiv31(m, f) != m / d || (m && fastdiv31(m - 1, f) != (m - 1) / d)) {
+                printf("FAIL d=%u m=%u\n", d, m); return 1; }
+        }
+    }
+    const uint32_t big[] = {65535u, 65536u, 1000003u, 0x40000000u, 0x7FFFFFFFu};
+    for (uint32_t d : big) {
+        FastDiv31 f = make_fastdiv31(d);
+        for (uint32_t n = 0x7FFFFFFFu; n > 0x7FFFFFFFu - 3000000u; --n)
+            if (fastdiv31(n, f) != n / d) { printf("FAIL d=%u n=%u\n", d, n); return 1; }
+    }
+    printf("OK %llu\n", checked);
+    return 0;
+}
+"""
+
+
+def test_fastdiv_exact_on_host():
+    csrc = os.path.join(ROOT, "mla_decode_concat_amd", "csrc")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check.cpp")
+        exe = os.path.join(d, "check")
+        open(src, "w").write(FASTDIV_CHECK)
+        subprocess.run(["g++", "-O2", "-std=c++17", "-I", csrc, src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True)
+        assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout

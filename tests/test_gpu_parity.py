@@ -1,0 +1,289 @@
+"""GPU parity: the gfx950 kernel, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bar: bit-exact for every copied element and every E4M3 code; rotated bf16
+outputs within 1e-2 absolute (and, since both sides evaluate the rotation
+with the same fp32 operation order, bit-exact as well).  NaN codes are
+compared as NaN.  q_out is poison-filled (0xFF) before each call and guard
+bands around q_out and the cache catch stray writes; caches start from a
+random background where the test is about untouched rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_decode_concat_amd as M
+from mla_decode_concat_amd import inputs as I
+from tests._util import bits, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GUARD_ROWS = 2
+
+
+def announce(case: str) -> None:
+    sys.__stderr__.write(f"[gpu-case] {case}\n")
+    sys.__stderr__.flush()
+
+
+def flags_of(w: I.Workload) -> int:
+    return (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+
+
+def run_gpu(w: I.Workload, inp: dict, extra_flags: int = 0, cache_init: np.ndarray | None = None,
+            views: dict | None = None, case: str = ""):
+    """Run the kernel; returns (q bits, cache bits) and checks the guards."""
+    announce(f"{case} {w.describe()} flags+{extra_flags:#x}")
+    T, H = w.tokens, w.heads
+    qdt = torch.float8_e4m3fn if w.q_fp8 else torch.bfloat16
+    kvdt = torch.float8_e4m3fn if w.kv_fp8 else torch.bfloat16
+    n_q = T * H * I.ROW
+    pad = 4096
+    qbig = torch.empty(n_q + 2 * pad, dtype=qdt, device=DEV)
+    qbig.view(torch.uint8).fill_(0xFF)
+    q_out = qbig[pad:pad + n_q].view(T, H, I.ROW)
+    if cache_init is None:
+        cache_cpu = inp["cache"]
+    elif cache_init.dtype == np.uint16:
+        cache_cpu = torch.from_numpy(cache_init.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        cache_cpu = torch.from_numpy(cache_init.copy()).view(kvdt)
+    NB, BS = cache_cpu.shape[0], cache_cpu.shape[1]
+    cbig = torch.empty(NB + 2 * GUARD_ROWS, BS, I.ROW, dtype=kvdt, device=DEV)
+    gen = torch.Generator().manual_seed(1234)
+    guard = torch.randint(0, 256, (GUARD_ROWS, BS, I.ROW * cbig.element_size()), generator=gen,
+                          dtype=torch.uint8)
+    cbig.view(torch.uint8)[:GUARD_ROWS] = guard.to(DEV)
+    cbig.view(torch.uint8)[-GUARD_ROWS:] = guard.to(DEV)
+    cache = cbig[GUARD_ROWS:GUARD_ROWS + NB]
+    cache.copy_(cache_cpu.to(DEV))
+    views = views or {}
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    for k, fn in views.items():
+        dev[k] = fn(dev[k])
+    M.mla_decode_q_concat_kv_insert(q_out, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"],
+                                    cache, dev["slot_mapping"], dev["positions"],
+                                    dev["rope_cos_sin"], dev["q_scale"], dev["kv_scale"],
+                                    flags_of(w) | extra_flags)
+    torch.cuda.synchronize()
+    qb = qbig.view(torch.uint8).cpu()
+    assert torch.all(qb[:pad * qbig.element_size()] == 0xFF), "write before q_out"
+    assert torch.all(qb[(pad + n_q) * qbig.element_size():] == 0xFF), "write after q_out"
+    cb = cbig.view(torch.uint8).cpu()
+    assert torch.equal(cb[:GUARD_ROWS], guard) and torch.equal(cb[-GUARD_ROWS:], guard), \
+        "write outside the cache"
+    return bits(q_out.cpu()), bits(cache.cpu())
+
+
+def _nan_mask(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint8:
+        return (x & 0x7F) == 0x7F
+    return ((x & 0x7F80) == 0x7F80) & ((x & 0x7F) != 0)
+
+
+def assert_same(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape and got.dtype == want.dtype, what
+    ng, nw = _nan_mask(got), _nan_mask(want)
+    bad = np.nonzero((ng != nw) | (~nw & (got != want)))
+    if bad[0].size:
+        idx = tuple(b[0] for b in bad)
+        raise AssertionError(f"{what}: {bad[0].size} mismatches, first at {idx}: "
+                             f"got {got[idx]:#x} want {want[idx]:#x}")
+
+
+def _bf16_value(x: np.ndarray) -> np.ndarray:
+    return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+def check_against_oracle(w: I.Workload, inp: dict, q, cache, cache_init=None):
+    want_q, want_cache = oracle_run(w, inp, cache_init=cache_init)
+    if w.rope and not w.q_fp8:
+        # the stated bar on rotated bf16 outputs first
+        g, r = _bf16_value(q[..., 512:]), _bf16_value(want_q[..., 512:])
+        fin = np.isfinite(r)
+        assert np.all(np.abs(g[fin] - r[fin]) <= 1e-2), "rotated q beyond 1e-2"
+    assert_same(q, want_q, "q_out")
+    assert_same(cache, want_cache, "cache")
+
+
+@pytest.mark.parametrize("name", I.WORKLOAD_ORDER)
+def test_workload_matches_oracle(name):
+    w = I.WORKLOADS[name]
+    inp = I.make_inputs(w)
+    q, cache = run_gpu(w, inp, case=f"workload {name}")
+    check_against_oracle(w, inp, q, cache)
+
+
+@pytest.mark.parametrize("name", ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8",
+                                  "t256_h128_rope_qfp8"])
+def test_forced_mappings_agree(name):
+    """Both mappings give identical bytes on identical inputs (the page's
+    split path is bitwise identical to the unsplit one)."""
+    w = I.WORKLOADS[name]
+    inp = I.make_inputs(w)
+    qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"force-small {name}")
+    ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T, case=f"force-large {name}")
+    assert np.array_equal(qs, ql) and np.array_equal(cs, cl)
+    check_against_oracle(w, inp, qs, cs)
+
+
+@pytest.mark.parametrize("num_tokens", [64, 65])
+def test_page_row_split_boundary(num_tokens):
+    """The page's boundary test through the page's call: q == cat(ql_nope,
+    q_pe) and the cache rows at the slots == cat(kv_c, k_pe); the rest of the
+    zero cache stays zero."""
+    announce(f"page boundary T={num_tokens}")
+    w = I.custom(num_tokens, 16)
+    inp = I.make_inputs(w)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q = M.fused_mla_decode_q_concat_kv_cache_insert(dev["ql_nope"], dev["q_pe"], dev["kv_c"],
+                                                    dev["k_pe"], dev["cache"], dev["slot_mapping"])
+    torch.cuda.synchronize()
+    assert torch.equal(q.cpu(), torch.cat([inp["ql_nope"], inp["q_pe"]], dim=-1))
+    rows = dev["cache"].cpu().view(-1, I.ROW)
+    slots = inp["slot_mapping"]
+    assert torch.equal(rows[slots], torch.cat([inp["kv_c"], inp["k_pe"]], dim=-1))
+    mask = torch.ones(rows.shape[0], dtype=torch.bool)
+    mask[slots] = False
+    assert torch.all(rows[mask].view(torch.int16) == 0)
+
+
+FLAG_SETS = [(r, q, k) for r in (False, True) for q in (False, True) for k in (False, True)]
+
+
+@pytest.mark.parametrize("T,H", [(1, 1), (2, 3), (7, 16), (33, 5), (63, 16), (100, 1),
+                                 (129, 7), (300, 128), (1000, 16)])
+@pytest.mark.parametrize("fl", FLAG_SETS, ids=lambda f: "r%dq%dk%d" % f)
+def test_ragged_shapes_all_modes(T, H, fl):
+    rope, qf, kf = fl
+    if T * (H + 1) > 40000 and fl != (True, True, True):
+        pytest.skip("large shape covered in the all-on mode only")
+    w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64) + 1, rope=rope, q_fp8=qf, kv_fp8=kf,
+                 q_scale=0.04, kv_scale=0.3)
+    inp = I.make_inputs(w, seed=T * 131 + H)
+    rng = np.random.default_rng(T + H)
+    init = rng.integers(0, 256, size=(w.num_blocks, 64, 576 * (1 if kf else 2)), dtype=np.uint8)
+    init = init.view(np.uint8 if kf else np.uint16)
+    if not kf:
+        init = init & np.uint16(0x3FFF)   # finite bf16 background
+    q, cache = run_gpu(w, inp, cache_init=init, case=f"ragged T={T} H={H} {fl}")
+    check_against_oracle(w, inp, q, cache, cache_init=init)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.05, 2.0 ** -4, 3.7])
+def test_e4m3_exhaustive_all_bf16_inputs(scale):
+    """Every bf16 bit pattern through the quantiser, in the latent part, the
+    positional part and the cache row (rotation off, then on)."""
+    T, H = 8, 16
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    for rope in (False, True):
+        w = I.custom(T, H, num_blocks=1, rope=rope, q_fp8=True, kv_fp8=True, q_scale=scale,
+                     kv_scale=scale)
+        inp = I.make_inputs(w, seed=17)
+        inp["ql_nope"] = allbits.view(T, H, 512).clone()
+        perm = torch.randperm(65536, generator=torch.Generator().manual_seed(3))
+        inp["q_pe"] = allbits[perm[:T * H * 64]].view(T, H, 64).clone()
+        inp["kv_c"] = allbits[perm[:T * 512]].view(T, 512).clone()
+        inp["k_pe"] = allbits[perm[-T * 64:]].view(T, 64).clone()
+        q, cache = run_gpu(w, inp, case=f"e4m3 exhaustive scale={scale} rope={rope}")
+        check_against_oracle(w, inp, q, cache)
+
+
+def test_rotation_on_all_bf16_tails():
+    """Every bf16 pattern as a positional element (bf16 output): rounding,
+    signed zeros, infinities and NaN through the rotation."""
+    T, H = 64, 16
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    w = I.custom(T, H, num_blocks=1, rope=True)
+    inp = I.make_inputs(w, seed=21)
+    inp["q_pe"] = allbits.view(T, H, 64).clone()
+    q, cache = run_gpu(w, inp, case="rope all-bf16 tails")
+    want_q, want_cache = oracle_run(w, inp)
+    assert_same(q, want_q, "q_out")
+    assert_same(cache, want_cache, "cache")
+
+
+def test_strided_input_views():
+    """Inputs as row-strided views of larger buffers."""
+    w = I.custom(37, 16, num_blocks=2, rope=True, q_fp8=True, kv_fp8=False)
+    inp = I.make_inputs(w, seed=5)
+    T, H = w.tokens, w.heads
+
+    def wide(x, extra):  # embed the last dim in a wider row, return the view
+        shape = list(x.shape)
+        big = torch.zeros(shape[:-1] + [shape[-1] + extra], dtype=x.dtype, device=x.device)
+        big[..., 8:8 + shape[-1]] = x
+        return big[..., 8:8 + shape[-1]]
+    views = {
+        "ql_nope": lambda x: wide(x, 64),                         # head stride 576
+        "q_pe": lambda x: wide(x.reshape(T, H, 64), 128),         # head stride 192
+        "kv_c": lambda x: wide(x, 64),                            # token stride 576
+        "k_pe": lambda x: wide(x, 520),                           # token stride 584
+    }
+    q, cache = run_gpu(w, inp, views=views, case="strided views")
+    check_against_oracle(w, inp, q, cache)
+
+
+def test_out_of_range_slots_and_positions():
+    w = I.custom(6, 4, num_blocks=1, rope=True, kv_fp8=True, max_position=16)
+    inp = I.make_inputs(w, seed=4)
+    inp["slot_mapping"] = torch.tensor([-1, 64, 3, 1 << 40, -7, 63], dtype=torch.int64)
+    inp["positions"] = torch.tensor([-5, 16, 1000, 3, 15, 0], dtype=torch.int64)
+    init = np.full((1, 64, 576), 0x5A, dtype=np.uint8)
+    q, cache = run_gpu(w, inp, cache_init=init, case="out-of-range slots/positions")
+    check_against_oracle(w, inp, q, cache, cache_init=init)
+
+
+def test_duplicate_slots_leave_one_candidate():
+    w = I.custom(3, 2, num_blocks=1)
+    inp = I.make_inputs(w, seed=2)
+    inp["slot_mapping"] = torch.tensor([5, 5, 9], dtype=torch.int64)
+    q, cache = run_gpu(w, inp, case="duplicate slots")
+    rows = cache.reshape(-1, 576)
+    cands = [bits(torch.cat([inp["kv_c"][t], inp["k_pe"][t]])) for t in (0, 1)]
+    assert any(np.array_equal(rows[5], c) for c in cands)
+    assert np.array_equal(rows[9], bits(torch.cat([inp["kv_c"][2], inp["k_pe"][2]])))
+
+
+def test_zero_tokens_launches_nothing():
+    w = I.custom(0, 16, num_blocks=1)
+    inp = I.make_inputs(w)
+    q, cache = run_gpu(w, inp, case="T=0")
+    assert q.size == 0 and np.all(cache == 0)
+
+
+def test_non_default_stream():
+    announce("non-default stream")
+    w = I.WORKLOADS["t64_h16_rope_fp8"]
+    inp = I.make_inputs(w)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        q = M.fused_mla_decode_q_concat_kv_cache_insert(
+            dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"], dev["cache"],
+            dev["slot_mapping"], dev["positions"], dev["rope_cos_sin"], dev["q_scale"],
+            dev["kv_scale"], q_fp8=True)
+    s.synchronize()
+    want_q, want_cache = oracle_run(w, inp)
+    assert_same(bits(q.cpu()), want_q, "q_out")
+    assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
+
+
+def test_binding_rejects_wrong_dtypes():
+    w = I.WORKLOADS["t1_h16_copy"]
+    inp = I.make_inputs(w)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q = torch.empty(1, 16, 576, dtype=torch.float8_e4m3fn, device=DEV)
+    with pytest.raises(ValueError):
+        M.mla_decode_q_concat_kv_insert(q, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"],
+                                        dev["cache"], dev["slot_mapping"])
+    q16 = torch.empty(1, 16, 576, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        M.mla_decode_q_concat_kv_insert(q16, dev["ql_nope"].float(), dev["q_pe"], dev["kv_c"],
+                                        dev["k_pe"], dev["cache"], dev["slot_mapping"])
