@@ -262,8 +262,9 @@ def main() -> int:
                    "q_out": "e4m3" if w.q_fp8 else "bf16", "rope": w.rope,
                    "buffer_sets": args.buffer_sets,
                    "mapping": "small_t" if pl.mapping == 0 else "large_t",
+                   "streaming": bool(pl.streaming),
                    "grid_blocks": pl.grid_blocks, "block_threads": pl.block_threads,
-                   "chunks_per_lane": pl.chunks_per_lane},
+                   "rows_per_wave": pl.rows_per_wave, "tail_steps": pl.tail_steps},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "latency_us": latency,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

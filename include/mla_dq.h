@@ -28,7 +28,9 @@
  *   - slots outside [0, num_blocks*block_size) (e.g. -1 padding) skip the
  *     cache write for that token; the token's q rows are still written;
  *   - positions outside [0, max_position) are clamped into the table;
- *   - with repeated slots, which token's row remains is unspecified.
+ *   - valid slots are expected to be unique; with a repeated slot, every
+ *     8-element chunk of the row holds that chunk of one of the tokens that
+ *     share it, not necessarily the same token for every chunk.
  *
  * Threading and ownership: the library allocates nothing, keeps no state
  * beyond a read-once tuning environment variable, and may be called from
@@ -50,20 +52,25 @@ extern "C" {
 #define MLA_DQ_ROPE    (1u << 0) /* rotate the 64-wide tails of q and k     */
 #define MLA_DQ_Q_FP8   (1u << 1) /* q_out holds E4M3 codes (else bf16)      */
 #define MLA_DQ_KV_FP8  (1u << 2) /* cache holds E4M3 codes (else bf16)      */
-/* Mapping overrides for tests and sweeps.  By default the library picks the
- * latency mapping (one 16-byte chunk per lane, wavefronts per row) for small
- * token counts and the throughput mapping (several chunks per lane, rows per
- * wavefront) above a measured threshold; the page's launcher makes the same
- * token-count-dependent choice ("implementation breakdown" items 1 and 3). */
-#define MLA_DQ_FORCE_SMALL_T (1u << 8)
-#define MLA_DQ_FORCE_LARGE_T (1u << 9)
+/* Launch overrides for tests and sweeps; they never change the results.
+ * By default the library picks the latency mapping (one latent row per
+ * wavefront in 64-thread workgroups) while T * (H + 1) is small and the
+ * throughput mapping (256-thread workgroups, tails batched) above a measured
+ * row threshold; the page's launcher makes the same token-count-dependent
+ * choice ("implementation breakdown" items 1 and 3).  Independently, loads
+ * and stores stream past the caches (non-temporal) once one call moves more
+ * bytes than the Infinity Cache can keep. */
+#define MLA_DQ_FORCE_SMALL_T (1u << 8)  /* latency mapping                 */
+#define MLA_DQ_FORCE_LARGE_T (1u << 9)  /* throughput mapping              */
+#define MLA_DQ_FORCE_STREAM  (1u << 10) /* non-temporal loads and stores   */
+#define MLA_DQ_FORCE_CACHED  (1u << 11) /* default cache policy            */
 
 /* ---- return codes ------------------------------------------------------ */
 #define MLA_DQ_OK          0
 #define MLA_DQ_ERR_NULL   -1 /* a required pointer (or dims) is NULL               */
 #define MLA_DQ_ERR_ALIGN  -2 /* pointer or stride misaligned (see below)          */
 #define MLA_DQ_ERR_DIM    -3 /* a dimension or stride is out of range             */
-#define MLA_DQ_ERR_FLAGS  -4 /* unknown flag bit, or both FORCE bits             */
+#define MLA_DQ_ERR_FLAGS  -4 /* unknown flag bit, or contradictory FORCE bits    */
 #define MLA_DQ_ERR_LAUNCH -5 /* the HIP launch reported an error                  */
 #define MLA_DQ_ERR_ALIAS  -6 /* q_out overlaps an input or the cache              */
 
@@ -125,15 +132,24 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
 const char* mla_dq_strerror(int code);
 
 /* The launch the library would make for these dims and flags: host-only, no
- * GPU needed, no device memory touched.  mapping is 0 for the small-T
- * (latency) mapping and 1 for the large-T (throughput) mapping. */
+ * GPU needed, no device memory touched.  The kernel splits every 576-wide
+ * row into its 512-wide latent part (64 sixteen-byte chunks: one chunk per
+ * lane of one wavefront) and its 64-wide positional tail (8 chunks: 8 lanes,
+ * so 8 rows' tails per wavefront). */
 typedef struct mla_dq_launch_plan {
-    int32_t mapping;          /* 0 = small-T, 1 = large-T                   */
-    int32_t chunks_per_lane;  /* 16-byte input chunks handled by each lane  */
-    int32_t block_threads;    /* threads per workgroup                      */
-    int32_t small_t_max;      /* token threshold in force                   */
-    int64_t grid_blocks;      /* workgroups launched                        */
-    int64_t total_chunks;     /* T * (H + 1) * 72                           */
+    int32_t mapping;          /* 0 = small-T (latency), 1 = large-T (throughput) */
+    int32_t streaming;        /* 1 = non-temporal loads and stores               */
+    int32_t block_threads;    /* threads per workgroup (a multiple of 64)        */
+    int32_t rows_per_wave;    /* latent rows per wavefront                       */
+    int32_t tail_steps;       /* steps of 8 tails per wavefront                  */
+    int32_t reserved;
+    int64_t small_rows_max;   /* row threshold in force                          */
+    int64_t stream_bytes_min; /* byte threshold in force                         */
+    int64_t bytes;            /* bytes the call reads and writes                 */
+    int64_t tail_blocks;      /* workgroups doing positional tails (first)       */
+    int64_t latent_blocks;    /* workgroups doing latent parts (after them)      */
+    int64_t grid_blocks;      /* tail_blocks + latent_blocks                     */
+    int64_t total_rows;       /* T * (H + 1)                                     */
 } mla_dq_launch_plan;
 
 /* Returns MLA_DQ_OK and fills *plan, or a negative code for bad dims/flags.

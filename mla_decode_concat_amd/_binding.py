@@ -22,6 +22,8 @@ Q_FP8 = 1 << 1
 KV_FP8 = 1 << 2
 FORCE_SMALL_T = 1 << 8
 FORCE_LARGE_T = 1 << 9
+FORCE_STREAM = 1 << 10
+FORCE_CACHED = 1 << 11
 
 OK = 0
 ERR_NULL = -1
@@ -42,9 +44,13 @@ class Dims(ctypes.Structure):
 
 
 class LaunchPlan(ctypes.Structure):
-    _fields_ = [("mapping", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
-                ("block_threads", ctypes.c_int32), ("small_t_max", ctypes.c_int32),
-                ("grid_blocks", ctypes.c_int64), ("total_chunks", ctypes.c_int64)]
+    _fields_ = [("mapping", ctypes.c_int32), ("streaming", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32),
+                ("tail_steps", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("small_rows_max", ctypes.c_int64), ("stream_bytes_min", ctypes.c_int64),
+                ("bytes", ctypes.c_int64), ("tail_blocks", ctypes.c_int64),
+                ("latent_blocks", ctypes.c_int64), ("grid_blocks", ctypes.c_int64),
+                ("total_rows", ctypes.c_int64)]
 
 
 class MlaDqError(RuntimeError):

@@ -31,28 +31,47 @@ Extent extent3(const void* p, int64_t T, int64_t H, int64_t st, int64_t sh, int6
 
 bool overlap(Extent x, Extent y) { return x.lo < y.hi && y.lo < x.hi; }
 
-int small_t_max() {
-    static const int v = [] {
-        const char* s = getenv("MLA_DQ_SMALL_T_MAX");
-        if (s == nullptr || *s == '\0') return kDefaultSmallTMax;
-        char* end = nullptr;
-        const long n = strtol(s, &end, 10);
-        if (end == s || n < 0 || n > INT_MAX) return kDefaultSmallTMax;
-        return int(n);
-    }();
+int64_t env_int64(const char* name, int64_t fallback) {
+    const char* s = getenv(name);
+    if (s == nullptr || *s == '\0') return fallback;
+    char* end = nullptr;
+    const long long n = strtoll(s, &end, 10);
+    if (end == s || *end != '\0' || n < 0) return fallback;
+    return int64_t(n);
+}
+
+int64_t small_rows_max() {
+    static const int64_t v = env_int64("MLA_DQ_SMALL_ROWS_MAX", kDefaultSmallRowsMax);
     return v;
+}
+
+int64_t stream_bytes_min() {
+    static const int64_t v = env_int64("MLA_DQ_STREAM_BYTES_MIN", kDefaultStreamBytesMin);
+    return v;
+}
+
+// Bytes one call reads and writes: each 576-wide input row once as bf16, each
+// output row once, plus slot, position and rope table row per token.
+int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    const bool rope = flags & MLA_DQ_ROPE;
+    const int64_t read = T * (H * 1152 + 1152 + 8 + (rope ? 8 + 256 : 0));
+    const int64_t write = T * 576 * (H * ((flags & MLA_DQ_Q_FP8) ? 1 : 2) +
+                                     ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
+    return read + write;
 }
 
 // Checks that do not need any pointer: flags and shapes.
 int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
     if (d == nullptr) return MLA_DQ_ERR_NULL;
     const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FORCE_SMALL_T |
-                           MLA_DQ_FORCE_LARGE_T;
+                           MLA_DQ_FORCE_LARGE_T | MLA_DQ_FORCE_STREAM | MLA_DQ_FORCE_CACHED;
     if (flags & ~known) return MLA_DQ_ERR_FLAGS;
     if ((flags & MLA_DQ_FORCE_SMALL_T) && (flags & MLA_DQ_FORCE_LARGE_T)) return MLA_DQ_ERR_FLAGS;
+    if ((flags & MLA_DQ_FORCE_STREAM) && (flags & MLA_DQ_FORCE_CACHED)) return MLA_DQ_ERR_FLAGS;
     const int64_t T = d->num_tokens, H = d->num_heads;
     if (T < 0 || H < 1 || d->num_blocks < 1 || d->block_size < 1) return MLA_DQ_ERR_DIM;
-    // Flat chunk indices are 32-bit on the device.
+    // Row indices, and T * (H + 1) * 72 chunk counts, stay below 2^31.
     if (H > INT32_MAX / kRowChunks - 1) return MLA_DQ_ERR_DIM;
     if (T > INT32_MAX / (kRowChunks * (H + 1))) return MLA_DQ_ERR_DIM;
     if (d->num_blocks > (INT64_MAX / 2048) / d->block_size) return MLA_DQ_ERR_DIM;
@@ -81,24 +100,37 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     const int rc = check_flags_dims(flags, d);
     if (rc < 0) return rc;
     const int64_t T = d->num_tokens, H = d->num_heads;
-    const int thr = small_t_max();
-    int mapping;
-    if (flags & MLA_DQ_FORCE_SMALL_T)
-        mapping = 0;
-    else if (flags & MLA_DQ_FORCE_LARGE_T)
-        mapping = 1;
-    else
-        mapping = T <= thr ? 0 : 1;
-    const int cpl = mapping == 0 ? kSmallCpl : kLargeCpl;
-    const int block = mapping == 0 ? kSmallBlock : kLargeBlock;
-    const int64_t total = T * (H + 1) * kRowChunks;
-    const int64_t per_block = int64_t(cpl) * block;
+    const int64_t rows = T * (H + 1);
+    const int64_t rows_thr = small_rows_max(), bytes_thr = stream_bytes_min();
+    const int64_t bytes = call_bytes(d, flags);
+    int mapping = rows <= rows_thr ? 0 : 1;
+    if (flags & MLA_DQ_FORCE_SMALL_T) mapping = 0;
+    if (flags & MLA_DQ_FORCE_LARGE_T) mapping = 1;
+    int streaming = bytes >= bytes_thr ? 1 : 0;
+    if (flags & MLA_DQ_FORCE_STREAM) streaming = 1;
+    if (flags & MLA_DQ_FORCE_CACHED) streaming = 0;
+    const Mapping& m = mapping == 0 ? kSmallMapping : kLargeMapping;
+    const int64_t latent_per_block = int64_t(m.block / 64) * m.rows_per_wave;
+    const int64_t tails_per_block = int64_t(m.block / 8) * m.tail_steps;
+    int64_t tail_blocks = (rows + tails_per_block - 1) / tails_per_block;
+#if MLA_DQ_XCD_REMAP
+    // A multiple of 8 keeps every latent workgroup on the XCD its index
+    // implies (workgroups are dealt to the 8 XCDs round-robin).
+    tail_blocks = (tail_blocks + 7) / 8 * 8;
+#endif
     out->mapping = mapping;
-    out->chunks_per_lane = cpl;
-    out->block_threads = block;
-    out->small_t_max = thr;
-    out->total_chunks = total;
-    out->grid_blocks = (total + per_block - 1) / per_block;
+    out->streaming = streaming;
+    out->block_threads = m.block;
+    out->rows_per_wave = m.rows_per_wave;
+    out->tail_steps = m.tail_steps;
+    out->reserved = 0;
+    out->small_rows_max = rows_thr;
+    out->stream_bytes_min = bytes_thr;
+    out->bytes = bytes;
+    out->tail_blocks = T == 0 ? 0 : tail_blocks;
+    out->latent_blocks = (rows + latent_per_block - 1) / latent_per_block;
+    out->grid_blocks = out->tail_blocks + out->latent_blocks;
+    out->total_rows = rows;
     return MLA_DQ_OK;
 }
 
@@ -179,7 +211,8 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
     a.max_position = (flags & MLA_DQ_ROPE) ? dims->max_position : 1;
     a.rows_per_token = make_fastdiv31(uint32_t(dims->num_heads + 1));
     a.num_heads = uint32_t(dims->num_heads);
-    a.total_chunks = uint32_t(p.total_chunks);
+    a.total_rows = uint32_t(p.total_rows);
+    a.tail_blocks = uint32_t(p.tail_blocks);
     const hipError_t e = mla_dq::launch(a, p, flags, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
 }
@@ -194,7 +227,7 @@ const char* mla_dq_strerror(int code) {
         case MLA_DQ_ERR_NULL: return "a required pointer is NULL";
         case MLA_DQ_ERR_ALIGN: return "pointer or stride misaligned (16-byte rows, 8-element strides)";
         case MLA_DQ_ERR_DIM: return "dimension or stride out of range";
-        case MLA_DQ_ERR_FLAGS: return "unknown flag bit or conflicting mapping overrides";
+        case MLA_DQ_ERR_FLAGS: return "unknown flag bit or contradictory launch overrides";
         case MLA_DQ_ERR_LAUNCH: return "HIP kernel launch failed";
         case MLA_DQ_ERR_ALIAS: return "q_out overlaps an input or the cache, or the cache overlaps an input";
         default: return "unknown mla_dq error code";

@@ -10,19 +10,61 @@
 #include <hip/hip_runtime.h>
 #endif
 
+// Tuning knobs (compile-time; the defaults are the measured choice on
+// MI355X).  Workgroup sizes, latent rows per wavefront and tail steps of the
+// two mappings, and the default thresholds of the launch plan.
+#ifndef MLA_DQ_SMALL_BLOCK
+#define MLA_DQ_SMALL_BLOCK 64
+#endif
+#ifndef MLA_DQ_LARGE_BLOCK
+#define MLA_DQ_LARGE_BLOCK 256
+#endif
+#ifndef MLA_DQ_LARGE_ROWS_PER_WAVE
+#define MLA_DQ_LARGE_ROWS_PER_WAVE 1
+#endif
+#ifndef MLA_DQ_LARGE_TAIL_STEPS
+#define MLA_DQ_LARGE_TAIL_STEPS 2
+#endif
+// Small-T mapping while T * (H + 1) <= this many rows.
+#ifndef MLA_DQ_SMALL_ROWS_MAX_DEFAULT
+#define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 2304
+#endif
+// Streaming (non-temporal) loads and stores once a call moves at least this
+// many bytes: above the 256 MB Infinity Cache nothing survives to the next
+// call anyway, below it the default policy lets the data stay resident.
+#ifndef MLA_DQ_STREAM_BYTES_MIN_DEFAULT
+#define MLA_DQ_STREAM_BYTES_MIN_DEFAULT (192ll << 20)
+#endif
+// Cache-policy bits for streaming buffer loads and stores (the non-temporal
+// bit of gfx94x/gfx950).
+#ifndef MLA_DQ_STREAM_AUX
+#define MLA_DQ_STREAM_AUX 2
+#endif
+// Deal each XCD one contiguous range of latent workgroups (measured slower
+// for this streaming kernel, so off).
+#ifndef MLA_DQ_XCD_REMAP
+#define MLA_DQ_XCD_REMAP 0
+#endif
+
 namespace mla_dq {
 
-// Mapping parameters: chunks (16-byte bf16 loads) per lane and threads per
-// workgroup, for the latency mapping and the throughput mapping.
-constexpr int kSmallCpl = 1;
-constexpr int kSmallBlock = 64;
-constexpr int kLargeCpl = 4;
-constexpr int kLargeBlock = 256;
-// Default token threshold between the two (overridable with the
-// environment variable MLA_DQ_SMALL_T_MAX, read once).
-constexpr int kDefaultSmallTMax = 64;
+// A mapping: threads per workgroup, latent rows handled by each wavefront
+// (one row = 64 chunks = one 16-byte load per lane), and steps of 8 tails
+// per wavefront for the positional part.
+struct Mapping {
+    int block;
+    int rows_per_wave;
+    int tail_steps;
+};
+constexpr Mapping kSmallMapping{MLA_DQ_SMALL_BLOCK, 1, 1};
+constexpr Mapping kLargeMapping{MLA_DQ_LARGE_BLOCK, MLA_DQ_LARGE_ROWS_PER_WAVE,
+                                MLA_DQ_LARGE_TAIL_STEPS};
+// Thresholds (overridable with the environment variables
+// MLA_DQ_SMALL_ROWS_MAX and MLA_DQ_STREAM_BYTES_MIN, read once).
+constexpr int64_t kDefaultSmallRowsMax = MLA_DQ_SMALL_ROWS_MAX_DEFAULT;
+constexpr int64_t kDefaultStreamBytesMin = MLA_DQ_STREAM_BYTES_MIN_DEFAULT;
 
-constexpr int64_t kRowChunks = 72;   // 576 elements / 8 per chunk
+constexpr int64_t kRowChunks = 72;   // 576 elements / 8 per 16-byte chunk
 
 struct KernelArgs {
     uint8_t* q_out;
@@ -41,7 +83,8 @@ struct KernelArgs {
     int64_t max_position;
     FastDiv31 rows_per_token;   // divides a row index by H + 1
     uint32_t num_heads;
-    uint32_t total_chunks;
+    uint32_t total_rows;        // T * (H + 1)
+    uint32_t tail_blocks;       // workgroups [0, tail_blocks) do the tails
 };
 
 // Host-side validation and planning (pure host code, no HIP calls).

@@ -7,40 +7,46 @@
 // Work layout.  Every token owns H + 1 latent rows of 576 elements: its H
 // query rows, then its cache row (the page's kernel orders a token's work
 // items the same way: query slots first, then the cache slot).  A row is 72
-// chunks of 8 elements -- 64 chunks of the 512-wide latent part, 8 chunks of
-// the 64-wide positional tail -- and one chunk is one 16-byte bf16 load.
-// Chunks are numbered flat, g = 72 * row + c, and every wavefront processes
-// 64 consecutive chunks per step, starting at a multiple of 64.  Because
-// 72 * row + 64 = 8 * row (mod 64), the 8 tail chunks of any row then sit in
-// one aligned group of 8 lanes of one wavefront, and the NeoX partner of tail
-// chunk j (element i pairs with i + 32, so chunk j with chunk j ^ 4) is lane
-// (lane ^ 4): the rotation exchanges partner chunks with ds_swizzle, entirely
-// in registers.
+// chunks of 8 bf16 elements, one chunk being one 16-byte load: 64 chunks of
+// the 512-wide latent part and 8 chunks of the 64-wide positional tail.
 //
-// Two mappings.  Small token counts are latency-bound (a few thousand
-// chunks, far fewer than the chip has lanes), so each lane takes one chunk
-// and every load is issued at once; a row spans 72 lanes, i.e. wavefronts per
-// row.  Large token counts are bandwidth-bound, so each lane takes CPL chunks
-// (loads for all of them in flight before the first store), i.e. rows per
-// wavefront.  The page's kernel makes the same token-count-dependent choice
-// with whole warps (implementation breakdown item 1); the threshold here is
-// set by measurement on MI355X.
+//  * Latent parts.  64 chunks are exactly one 16-byte load per lane of a
+//    wave64, so a wavefront moves one whole latent part per step.  The row,
+//    and with it the token, head, slot and both base addresses, is uniform
+//    across the wavefront and lives in scalar registers; each lane adds only
+//    its own 16-byte offset.  Loads and stores are fully coalesced (1 KiB
+//    contiguous per instruction), and the slot is a scalar load.
+//  * Positional tails.  8 lanes take one row's 8 tail chunks, so a wavefront
+//    takes the tails of 8 rows per step.  NeoX pairs element i with i + 32,
+//    i.e. chunk j with chunk j ^ 4, which sits in lane (lane ^ 4): the
+//    partner's 8 values arrive by ds_swizzle, in registers.  Each tail lane
+//    loads the 8 cos and 8 sin values it needs from the caller's table row.
 //
-// Loads that do not depend on the upstream projection (slot, position, scale)
-// are issued first, then the activations, then the rope table rows that need
-// the position (the analogue of the page's reordering around its dependency
-// wait, implementation breakdown item 2).
+// Workgroups [0, tail_blocks) do tails, the rest do latent parts; tails go
+// first because their dependency chain (position -> table row -> rotate) is
+// the longer one.
+//
+// Two mappings.  Small token counts are latency-bound, so every wavefront
+// takes one latent row (and 8 tails) and all loads are in flight at once
+// across as many CUs as possible.  Large token counts are bandwidth-bound,
+// so each wavefront takes several latent rows, issuing all their loads
+// before its first store.  The page's kernel makes the same token-count-
+// dependent choice with whole warps (implementation breakdown item 1); the
+// threshold here is set by measurement on MI355X.
+//
+// Loads that do not depend on the upstream projection (slot, position,
+// scale) are issued before the activations, as the page's kernel reorders
+// its reads around the dependency wait (implementation breakdown item 2).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "mla_dq.h"
 #include "fastdiv.h"
 #include "mla_dq_internal.h"
 
-// Every product and sum of the rotation rounds on its own, like the
-// reference definition: no contraction into fused multiply-adds.
+// Every product and sum of the rotation rounds on its own: no contraction
+// into fused multiply-adds.
 #pragma clang fp contract(off)
 
 namespace mla_dq {
@@ -50,6 +56,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
 
 // Workgroup index -> tile index such that each of the 8 XCDs (which receive
 // workgroups round-robin) works on one contiguous range of tiles.
@@ -62,6 +70,14 @@ __device__ __forceinline__ uint32_t xcd_contiguous_tile(uint32_t b, uint32_t n) 
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack_bf16(u32x4 d, float (&v)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        v[2 * p] = bf16_lo(d[p]);
+        v[2 * p + 1] = bf16_hi(d[p]);
+    }
+}
 
 // Exchange a 16-byte chunk with lane (lane ^ 4) of the same wavefront.
 __device__ __forceinline__ u32x4 swap_lane4(u32x4 v) {
@@ -107,167 +123,251 @@ __device__ __forceinline__ u32x4 pack_bf16(const float (&v)[8]) {
     return r;
 }
 
-__device__ __forceinline__ void unpack_bf16(u32x4 d, float (&v)[8]) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        v[2 * p] = bf16_lo(d[p]);
-        v[2 * p + 1] = bf16_hi(d[p]);
-    }
+template <bool STREAM, typename V>
+__device__ __forceinline__ void store_out(uint8_t* p, V v) {
+    if constexpr (STREAM)
+        __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+    else
+        *reinterpret_cast<V*>(p) = v;
 }
 
-template <int CPL, int BLOCK, bool ROPE, bool QF8, bool KVF8>
-__global__ void __launch_bounds__(BLOCK)
-mla_dq_epilogue_kernel(const KernelArgs a) {
-    const uint32_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
-    const uint32_t g0 = tile * uint32_t(CPL * BLOCK) + threadIdx.x;
+template <bool STREAM, typename V>
+__device__ __forceinline__ V load_in(const void* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+    else
+        return *reinterpret_cast<const V*>(p);
+}
+
+// ---- latent parts: one 512-wide row per wavefront step ---------------------
+
+// Raw buffer descriptor over [p, p + bytes): base, stride 0, num_records =
+// bytes, and the GFX9-family word 3.  Accesses past num_records are dropped
+// (stores) or return zero (loads) by the hardware, so a row that must not be
+// read or written gets bytes = 0 instead of a branch.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x2 e4m3_of_bf16(u32x4 d, float inv) {
+    float v[8];
+    unpack_bf16(d, v);
+    return pack_e4m3(v, inv);
+}
+
+template <int BLOCK, int RPW, bool STREAM, bool QF8, bool KVF8>
+__device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) {
+    constexpr int kAux = STREAM ? MLA_DQ_STREAM_AUX : 0;
+    constexpr uint32_t kWaves = BLOCK / kWave;
+    constexpr uint32_t kQRowBytes = QF8 ? 576u : 1152u;
+    constexpr uint32_t kKvRowBytes = KVF8 ? 576u : 1152u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane = threadIdx.x % kWave;
     const uint32_t H = a.num_heads;
+    const uint32_t row0 = tile * (kWaves * RPW) + wave;
 
-    // Per-chunk coordinates.
-    uint32_t tok[CPL], head[CPL], chunk[CPL];
-    bool live[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const uint32_t g = g0 + uint32_t(k * BLOCK);
-        live[k] = g < a.total_chunks;
-        const uint32_t row = g / 72u;
-        chunk[k] = g - row * 72u;
-        tok[k] = fastdiv31(row, a.rows_per_token);
-        head[k] = row - tok[k] * (H + 1);  // == H for the cache row
-    }
-
-    // Independent small loads first: scales, slots, positions.
     float q_inv = 1.0f, kv_inv = 1.0f;
     if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
     if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
-    int64_t slot[CPL];
-    int64_t pos[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const bool is_cache = head[k] == H;
-        slot[k] = (live[k] && is_cache) ? a.slot_mapping[tok[k]] : int64_t(-1);
-        pos[k] = 0;
-        if constexpr (ROPE) {
-            if (live[k] && chunk[k] >= 64u) pos[k] = a.positions[tok[k]];
-        }
-    }
 
-    // The activations: one 16-byte chunk per step.
-    u32x4 d[CPL];
+    // Wave-uniform row coordinates (scalar registers).  Rows past the end
+    // take row 0's coordinates and zero-sized descriptors.
+    __amdgpu_buffer_rsrc_t src[RPW], qdst[RPW], cdst[RPW];
+    bool is_q[RPW];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const bool is_cache = head[k] == H;
-        const bool is_pe = chunk[k] >= 64u;
-        const uint64_t t = tok[k];
-        const uint16_t* src;
-        if (!is_cache) {
-            src = is_pe ? a.q_pe + t * a.q_pe_st + uint64_t(head[k]) * a.q_pe_sh + (chunk[k] - 64u) * 8u
-                        : a.ql_nope + t * a.ql_nope_st + uint64_t(head[k]) * a.ql_nope_sh + chunk[k] * 8u;
+    for (int k = 0; k < RPW; ++k) {
+        const uint32_t row = row0 + uint32_t(k) * kWaves;
+        const bool live = row < a.total_rows;
+        const uint32_t r = live ? row : 0u;
+        const uint32_t t = fastdiv31(r, a.rows_per_token);
+        const uint32_t h = r - t * (H + 1);
+        is_q[k] = h < H;
+        // The slot is read for every row (a scalar load, independent of the
+        // activations) and used only by the cache row.
+        const int64_t s = a.slot_mapping[t];
+        const bool slot_ok = s >= 0 && s < a.num_slots;
+        const uint16_t* sp = is_q[k] ? a.ql_nope + uint64_t(t) * a.ql_nope_st + uint64_t(h) * a.ql_nope_sh
+                                     : a.kv_c + uint64_t(t) * a.kv_c_st;
+        src[k] = row_rsrc(sp, live ? 1024u : 0u);
+        qdst[k] = row_rsrc(a.q_out + (uint64_t(t) * H + h) * kQRowBytes,
+                           live && is_q[k] ? kQRowBytes : 0u);
+        cdst[k] = row_rsrc(a.cache + uint64_t(slot_ok ? s : 0) * kKvRowBytes,
+                           live && !is_q[k] && slot_ok ? kKvRowBytes : 0u);
+    }
+    u32x4 d[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k)
+        d[k] = __builtin_amdgcn_raw_buffer_load_b128(src[k], lane * 16u, 0, kAux);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        // Each row is written through exactly one of its two descriptors; the
+        // other has zero size, so that store is dropped.
+        if constexpr (QF8 == KVF8) {
+            const __amdgpu_buffer_rsrc_t dst = is_q[k] ? qdst[k] : cdst[k];
+            if constexpr (QF8)
+                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_bf16(d[k], is_q[k] ? q_inv : kv_inv),
+                                                      dst, lane * 8u, 0, kAux);
+            else
+                __builtin_amdgcn_raw_buffer_store_b128(d[k], dst, lane * 16u, 0, kAux);
         } else {
-            src = is_pe ? a.k_pe + t * a.k_pe_st + (chunk[k] - 64u) * 8u
-                        : a.kv_c + t * a.kv_c_st + chunk[k] * 8u;
-        }
-        d[k] = u32x4{0u, 0u, 0u, 0u};
-        if (live[k]) d[k] = *reinterpret_cast<const u32x4*>(src);
-    }
-
-    // Rope table: tail chunk j needs cos and sin of angles 8*(j&3) .. +7.
-    f32x4 cosv[ROPE ? CPL : 1][2], sinv[ROPE ? CPL : 1][2];
-    if constexpr (ROPE) {
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-            cosv[k][0] = cosv[k][1] = sinv[k][0] = sinv[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (live[k] && chunk[k] >= 64u) {
-                int64_t p = pos[k];
-                p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
-                const float* row = a.rope_cos_sin + p * 64 + ((chunk[k] - 64u) & 3u) * 8u;
-                cosv[k][0] = *reinterpret_cast<const f32x4*>(row);
-                cosv[k][1] = *reinterpret_cast<const f32x4*>(row + 4);
-                sinv[k][0] = *reinterpret_cast<const f32x4*>(row + 32);
-                sinv[k][1] = *reinterpret_cast<const f32x4*>(row + 36);
+            const u32x2 f8 = e4m3_of_bf16(d[k], QF8 ? q_inv : kv_inv);
+            if constexpr (QF8) {
+                __builtin_amdgcn_raw_buffer_store_b64(f8, qdst[k], lane * 8u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst[k], lane * 16u, 0, kAux);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(d[k], qdst[k], lane * 16u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b64(f8, cdst[k], lane * 8u, 0, kAux);
             }
         }
     }
+}
 
+// ---- positional tails: 8 rows' tails per wavefront step --------------------
+template <int BLOCK, int STEPS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
+__device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
+    constexpr uint32_t kRowsPerStep = BLOCK / 8;
+    const uint32_t H = a.num_heads;
+    const uint32_t j = threadIdx.x % 8u;           // tail chunk 0..7
+    const bool first_half = j < 4u;                // elements 8j..8j+7 < 32
+
+    float q_inv = 1.0f, kv_inv = 1.0f;
+    if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
+    if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
+
+    // Lanes past the last row read row 0 (always valid) and store nothing,
+    // so every load below is unconditional.
+    uint32_t tok[STEPS], head[STEPS];
+    bool live[STEPS];
+    int64_t slot[STEPS], pos[STEPS];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const bool is_cache = head[k] == H;
-        const bool is_pe = chunk[k] >= 64u;
+    for (int k = 0; k < STEPS; ++k) {
+        const uint32_t row = (tile * STEPS + k) * kRowsPerStep + threadIdx.x / 8u;
+        live[k] = row < a.total_rows;
+        const uint32_t r = live[k] ? row : 0u;
+        tok[k] = fastdiv31(r, a.rows_per_token);
+        head[k] = r - tok[k] * (H + 1);
+        slot[k] = a.slot_mapping[tok[k]];
+        pos[k] = 0;
+        if constexpr (ROPE) pos[k] = a.positions[tok[k]];
+    }
+    u32x4 d[STEPS];
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+        const uint64_t t = tok[k];
+        const uint16_t* src = head[k] < H
+                                  ? a.q_pe + t * a.q_pe_st + uint64_t(head[k]) * a.q_pe_sh
+                                  : a.k_pe + t * a.k_pe_st;
+        d[k] = load_in<STREAM, u32x4>(src + j * 8u);
+    }
+    f32x4 cs[ROPE ? STEPS : 1][4];
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) {
+            int64_t p = pos[k];
+            p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
+            const float* trow = a.rope_cos_sin + p * 64 + (j & 3u) * 8u;
+            cs[k][0] = *reinterpret_cast<const f32x4*>(trow);        // cos
+            cs[k][1] = *reinterpret_cast<const f32x4*>(trow + 4);
+            cs[k][2] = *reinterpret_cast<const f32x4*>(trow + 32);   // sin
+            cs[k][3] = *reinterpret_cast<const f32x4*>(trow + 36);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+        const bool is_q = head[k] < H;
         float y[8];
         if constexpr (ROPE) {
-            // Every lane takes part in the exchange; only tail lanes use it.
+            // Every lane takes part in the exchange.  First half: y = x_i c -
+            // x_{i+32} s with own = x_i; second half: y = x_{i+32} c + x_i s
+            // with own = x_{i+32}.
             const u32x4 partner = swap_lane4(d[k]);
             float own[8], par[8];
             unpack_bf16(d[k], own);
             unpack_bf16(partner, par);
-            // First half (j < 4): y = x_i c - x_{i+32} s, own = x_i.
-            // Second half:        y = x_{i+32} c + x_i s, own = x_{i+32}.
-            const bool first = ((chunk[k] - 64u) & 4u) == 0u;
-            const float c[8] = {cosv[k][0].x, cosv[k][0].y, cosv[k][0].z, cosv[k][0].w,
-                                cosv[k][1].x, cosv[k][1].y, cosv[k][1].z, cosv[k][1].w};
-            const float s[8] = {sinv[k][0].x, sinv[k][0].y, sinv[k][0].z, sinv[k][0].w,
-                                sinv[k][1].x, sinv[k][1].y, sinv[k][1].z, sinv[k][1].w};
+            const float c[8] = {cs[k][0].x, cs[k][0].y, cs[k][0].z, cs[k][0].w,
+                                cs[k][1].x, cs[k][1].y, cs[k][1].z, cs[k][1].w};
+            const float s[8] = {cs[k][2].x, cs[k][2].y, cs[k][2].z, cs[k][2].w,
+                                cs[k][3].x, cs[k][3].y, cs[k][3].z, cs[k][3].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float oc = own[e] * c[e];
                 const float ps = par[e] * s[e];
-                y[e] = first ? oc - ps : oc + ps;
+                y[e] = first_half ? oc - ps : oc + ps;
             }
-        }
-        if (!live[k]) continue;
-        const bool rotated = ROPE && is_pe;
-        const bool out_fp8 = is_cache ? KVF8 : QF8;
-        uint8_t* dst;
-        if (is_cache) {
-            if (slot[k] < 0 || slot[k] >= a.num_slots) continue;
-            dst = a.cache + (uint64_t(slot[k]) * 576u + chunk[k] * 8u) * (KVF8 ? 1u : 2u);
         } else {
-            const uint64_t qrow = uint64_t(tok[k]) * H + head[k];
-            dst = a.q_out + (qrow * 576u + chunk[k] * 8u) * (QF8 ? 1u : 2u);
+            unpack_bf16(d[k], y);
         }
-        if (out_fp8) {
-            float v[8];
-            if (rotated) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = y[e];
-            } else {
-                unpack_bf16(d[k], v);
-            }
-            *reinterpret_cast<u32x2*>(dst) = pack_e4m3(v, is_cache ? kv_inv : q_inv);
-        } else {
-            *reinterpret_cast<u32x4*>(dst) = rotated ? pack_bf16(y) : d[k];
-        }
+        const bool slot_ok = slot[k] >= 0 && slot[k] < a.num_slots;
+        if (!live[k] || (!is_q && !slot_ok)) continue;
+        const bool fp8 = is_q ? QF8 : KVF8;
+        uint8_t* dst = is_q ? a.q_out + ((uint64_t(tok[k]) * H + head[k]) * 576u + 512u + j * 8u) *
+                                            (QF8 ? 1u : 2u)
+                            : a.cache + (uint64_t(slot[k]) * 576u + 512u + j * 8u) * (KVF8 ? 1u : 2u);
+        if (fp8)
+            store_out<STREAM>(dst, pack_e4m3(y, is_q ? q_inv : kv_inv));
+        else if (ROPE)
+            store_out<STREAM>(dst, pack_bf16(y));
+        else
+            store_out<STREAM>(dst, d[k]);
     }
 }
 
-template <int CPL, int BLOCK, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int RPW, int TAIL_STEPS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
+__global__ void __launch_bounds__(BLOCK)
+mla_dq_epilogue_kernel(const KernelArgs a) {
+    const uint32_t b = blockIdx.x;
+    if (b < a.tail_blocks) {
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, ROPE, QF8, KVF8>(a, b);
+        return;
+    }
+    uint32_t tile = b - a.tail_blocks;
+#if MLA_DQ_XCD_REMAP
+    // tail_blocks is a multiple of 8, so tile and b share their XCD.
+    tile = xcd_contiguous_tile(tile, gridDim.x - a.tail_blocks);
+#endif
+    latent_rows<BLOCK, RPW, STREAM, QF8, KVF8>(a, tile);
+}
+
+template <int BLOCK, int RPW, int TS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
 static hipError_t launch_one(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((mla_dq_epilogue_kernel<CPL, BLOCK, ROPE, QF8, KVF8>), dim3(grid),
-                       dim3(BLOCK), 0, stream, a);
+    hipLaunchKernelGGL((mla_dq_epilogue_kernel<BLOCK, RPW, TS, STREAM, ROPE, QF8, KVF8>),
+                       dim3(grid), dim3(BLOCK), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int CPL, int BLOCK>
+template <int BLOCK, int RPW, int TS, bool STREAM>
 static hipError_t launch_flags(const KernelArgs& a, uint32_t grid, uint32_t flags,
                                hipStream_t stream) {
     const bool r = flags & MLA_DQ_ROPE, q = flags & MLA_DQ_Q_FP8, kv = flags & MLA_DQ_KV_FP8;
     if (r) {
-        if (q) return kv ? launch_one<CPL, BLOCK, true, true, true>(a, grid, stream)
-                         : launch_one<CPL, BLOCK, true, true, false>(a, grid, stream);
-        return kv ? launch_one<CPL, BLOCK, true, false, true>(a, grid, stream)
-                  : launch_one<CPL, BLOCK, true, false, false>(a, grid, stream);
+        if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, true, true, true>(a, grid, stream)
+                         : launch_one<BLOCK, RPW, TS, STREAM, true, true, false>(a, grid, stream);
+        return kv ? launch_one<BLOCK, RPW, TS, STREAM, true, false, true>(a, grid, stream)
+                  : launch_one<BLOCK, RPW, TS, STREAM, true, false, false>(a, grid, stream);
     }
-    if (q) return kv ? launch_one<CPL, BLOCK, false, true, true>(a, grid, stream)
-                     : launch_one<CPL, BLOCK, false, true, false>(a, grid, stream);
-    return kv ? launch_one<CPL, BLOCK, false, false, true>(a, grid, stream)
-              : launch_one<CPL, BLOCK, false, false, false>(a, grid, stream);
+    if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, false, true, true>(a, grid, stream)
+                     : launch_one<BLOCK, RPW, TS, STREAM, false, true, false>(a, grid, stream);
+    return kv ? launch_one<BLOCK, RPW, TS, STREAM, false, false, true>(a, grid, stream)
+              : launch_one<BLOCK, RPW, TS, STREAM, false, false, false>(a, grid, stream);
+}
+
+template <bool STREAM>
+static hipError_t launch_mapping(const KernelArgs& a, const mla_dq_launch_plan& plan,
+                                 uint32_t flags, hipStream_t stream) {
+    const uint32_t grid = (uint32_t)plan.grid_blocks;
+    if (plan.mapping == 0)
+        return launch_flags<kSmallMapping.block, kSmallMapping.rows_per_wave,
+                            kSmallMapping.tail_steps, STREAM>(a, grid, flags, stream);
+    return launch_flags<kLargeMapping.block, kLargeMapping.rows_per_wave,
+                        kLargeMapping.tail_steps, STREAM>(a, grid, flags, stream);
 }
 
 hipError_t launch(const KernelArgs& a, const mla_dq_launch_plan& plan, uint32_t flags,
                   hipStream_t stream) {
-    const uint32_t grid = (uint32_t)plan.grid_blocks;
-    if (plan.mapping == 0)
-        return launch_flags<kSmallCpl, kSmallBlock>(a, grid, flags, stream);
-    return launch_flags<kLargeCpl, kLargeBlock>(a, grid, flags, stream);
+    return plan.streaming ? launch_mapping<true>(a, plan, flags, stream)
+                          : launch_mapping<false>(a, plan, flags, stream);
 }
 
 }  // namespace mla_dq

@@ -44,6 +44,8 @@ def test_flag_and_code_values_match_header():
     assert val("MLA_DQ_KV_FP8") == M.KV_FP8
     assert val("MLA_DQ_FORCE_SMALL_T") == M.FORCE_SMALL_T
     assert val("MLA_DQ_FORCE_LARGE_T") == M.FORCE_LARGE_T
+    assert val("MLA_DQ_FORCE_STREAM") == M.FORCE_STREAM
+    assert val("MLA_DQ_FORCE_CACHED") == M.FORCE_CACHED
     for name, v in (("MLA_DQ_ERR_NULL", B.ERR_NULL), ("MLA_DQ_ERR_ALIGN", B.ERR_ALIGN),
                     ("MLA_DQ_ERR_DIM", B.ERR_DIM), ("MLA_DQ_ERR_FLAGS", B.ERR_FLAGS),
                     ("MLA_DQ_ERR_LAUNCH", B.ERR_LAUNCH), ("MLA_DQ_ERR_ALIAS", B.ERR_ALIAS)):
@@ -90,7 +92,8 @@ def test_null_dims():
     assert _call(_ptrs(), 0, None) == B.ERR_NULL
 
 
-@pytest.mark.parametrize("flags", [1 << 3, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T])
+@pytest.mark.parametrize("flags", [1 << 3, 1 << 12, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+                                   M.FORCE_STREAM | M.FORCE_CACHED])
 def test_bad_flags(flags):
     assert _call(_ptrs(), flags, _dims()) == B.ERR_FLAGS
 
@@ -179,18 +182,45 @@ def test_cache_overlapping_input_is_rejected():
 
 # ---- launch plan -------------------------------------------------------------
 
+def _bytes(T, H, flags):
+    rope = bool(flags & M.ROPE)
+    read = T * (H * 1152 + 1152 + 8 + (264 if rope else 0))
+    write = T * 576 * (H * (1 if flags & M.Q_FP8 else 2) + (1 if flags & M.KV_FP8 else 2))
+    return read + write
+
+
 def test_plan_threshold_and_coverage():
-    for T in (1, 2, 63, 64, 65, 256, 8192):
+    for T in (1, 2, 63, 64, 65, 135, 136, 256, 8192):
         for H in (1, 16, 128):
-            pl = M.plan(_dims(T=T, H=H), 0)
-            assert pl.mapping == (0 if T <= pl.small_t_max else 1)
-            assert pl.total_chunks == T * (H + 1) * 72
-            per = pl.chunks_per_lane * pl.block_threads
-            assert pl.grid_blocks * per >= pl.total_chunks > (pl.grid_blocks - 1) * per
-            assert pl.block_threads % 64 == 0
+            for flags in (0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8 | M.KV_FP8):
+                pl = M.plan(_dims(T=T, H=H), flags)
+                rows = T * (H + 1)
+                assert pl.total_rows == rows
+                assert pl.mapping == (0 if rows <= pl.small_rows_max else 1)
+                assert pl.bytes == _bytes(T, H, flags)
+                assert pl.streaming == (1 if pl.bytes >= pl.stream_bytes_min else 0)
+                assert pl.block_threads % 64 == 0
+                # every latent row and every tail covered, no spare workgroup
+                lat = pl.block_threads // 64 * pl.rows_per_wave
+                assert pl.latent_blocks * lat >= rows > (pl.latent_blocks - 1) * lat
+                tails = pl.block_threads // 8 * pl.tail_steps
+                assert pl.tail_blocks * tails >= rows > (pl.tail_blocks - 1) * tails
+                assert pl.grid_blocks == pl.tail_blocks + pl.latent_blocks
     assert M.plan(_dims(T=1), M.FORCE_LARGE_T).mapping == 1
     assert M.plan(_dims(T=10 ** 5), M.FORCE_SMALL_T).mapping == 0
+    assert M.plan(_dims(T=1), M.FORCE_STREAM).streaming == 1
+    assert M.plan(_dims(T=10 ** 5, H=128), M.FORCE_CACHED).streaming == 0
     assert M.plan(_dims(T=0), 0).grid_blocks == 0
+
+
+def test_plan_defaults_match_measured_choice():
+    """The 8192-token workload streams on the throughput mapping; the
+    1/64/65-token workloads use the latency mapping with the default policy."""
+    big = M.plan(_dims(T=8192, H=16, NB=4096), M.ROPE | M.KV_FP8)
+    assert (big.mapping, big.streaming) == (1, 1)
+    for T in (1, 64, 65):
+        p = M.plan(_dims(T=T, H=16), M.ROPE | M.Q_FP8 | M.KV_FP8)
+        assert (p.mapping, p.streaming) == (0, 0)
 
 
 def test_plan_rejects_bad_input():
@@ -202,11 +232,12 @@ def test_plan_rejects_bad_input():
 
 def test_threshold_env_override_in_fresh_process():
     code = ("import mla_decode_concat_amd as M; from mla_decode_concat_amd import _binding as B;"
-            "d=B.Dims(); d.num_tokens=100; d.num_heads=16; d.num_blocks=1; d.block_size=64;"
-            "p=M.plan(d,0); print(p.small_t_max, p.mapping)")
-    env = dict(os.environ, MLA_DQ_SMALL_T_MAX="128", PYTHONPATH=ROOT)
+            "d=B.Dims(); d.num_tokens=1000; d.num_heads=16; d.num_blocks=1; d.block_size=64;"
+            "p=M.plan(d,0); print(p.small_rows_max, p.mapping, p.stream_bytes_min, p.streaming)")
+    env = dict(os.environ, MLA_DQ_SMALL_ROWS_MAX="17000", MLA_DQ_STREAM_BYTES_MIN="1000",
+               PYTHONPATH=ROOT)
     out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
-    assert out.stdout.split() == ["128", "0"]
+    assert out.stdout.split() == ["17000", "0", "1000", "1"]
 
 
 # ---- fast division used by the kernel's index decode --------------------------

@@ -119,17 +119,22 @@ def test_workload_matches_oracle(name):
     check_against_oracle(w, inp, q, cache)
 
 
+LAUNCHES = [M.FORCE_SMALL_T | M.FORCE_CACHED, M.FORCE_SMALL_T | M.FORCE_STREAM,
+            M.FORCE_LARGE_T | M.FORCE_CACHED, M.FORCE_LARGE_T | M.FORCE_STREAM]
+
+
 @pytest.mark.parametrize("name", ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8",
                                   "t256_h128_rope_qfp8"])
-def test_forced_mappings_agree(name):
-    """Both mappings give identical bytes on identical inputs (the page's
-    split path is bitwise identical to the unsplit one)."""
+def test_forced_launches_agree(name):
+    """Both mappings and both cache policies give identical bytes on
+    identical inputs (the page's split path is bitwise identical to the
+    unsplit one)."""
     w = I.WORKLOADS[name]
     inp = I.make_inputs(w)
-    qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"force-small {name}")
-    ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T, case=f"force-large {name}")
-    assert np.array_equal(qs, ql) and np.array_equal(cs, cl)
-    check_against_oracle(w, inp, qs, cs)
+    outs = [run_gpu(w, inp, f, case=f"launch {f:#x} {name}") for f in LAUNCHES]
+    for q, c in outs[1:]:
+        assert np.array_equal(q, outs[0][0]) and np.array_equal(c, outs[0][1])
+    check_against_oracle(w, inp, *outs[0])
 
 
 @pytest.mark.parametrize("num_tokens", [64, 65])
@@ -245,8 +250,11 @@ def test_duplicate_slots_leave_one_candidate():
     inp["slot_mapping"] = torch.tensor([5, 5, 9], dtype=torch.int64)
     q, cache = run_gpu(w, inp, case="duplicate slots")
     rows = cache.reshape(-1, 576)
-    cands = [bits(torch.cat([inp["kv_c"][t], inp["k_pe"][t]])) for t in (0, 1)]
-    assert any(np.array_equal(rows[5], c) for c in cands)
+    # each 8-element chunk of the shared row comes from one of the two tokens
+    cands = [bits(torch.cat([inp["kv_c"][t], inp["k_pe"][t]])).reshape(72, 8) for t in (0, 1)]
+    got = rows[5].reshape(72, 8)
+    for c in range(72):
+        assert any(np.array_equal(got[c], cand[c]) for cand in cands), c
     assert np.array_equal(rows[9], bits(torch.cat([inp["kv_c"][2], inp["k_pe"][2]])))
 
 
