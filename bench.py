@@ -35,7 +35,7 @@ LATENCY = ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8"]
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
                   for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_t8192_h16_rope_kvfp8.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_dq_epilogue_t8192_h16_traffic.json")
 
 
 def log(msg: str) -> None:
@@ -67,6 +67,11 @@ class DeviceSet:
         self.q = torch.empty(w.tokens, w.heads, I.ROW, device=dev,
                              dtype=torch.float8_e4m3fn if w.q_fp8 else torch.bfloat16)
         self.flags = flags_of(w)
+        t = self.t
+        self.prepared = M.PreparedInsert(self.q, t["ql_nope"], t["q_pe"], t["kv_c"], t["k_pe"],
+                                         t["cache"], t["slot_mapping"], t["positions"],
+                                         t["rope_cos_sin"], t["q_scale"], t["kv_scale"],
+                                         self.flags)
 
     def call(self):
         t = self.t
@@ -94,18 +99,20 @@ def time_calls(sets: list, steps: int, warmup: int) -> dict:
     return {"event_ms_per_call": e0.elapsed_time(e1) / steps, "wall_ms_per_call": wall * 1e3 / steps}
 
 
-def time_graph(s: DeviceSet, calls: int = 100, replays: int = 20) -> float:
-    """µs per call when `calls` launches are captured in one HIP graph."""
-    g = torch.cuda.CUDAGraph()
+def time_graph(sets: list, calls: int = 100, replays: int = 20) -> float:
+    """Device µs per call when `calls` launches (cycling through the sets) are
+    captured in one HIP graph and replayed."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        s.call()
+        for s in sets:
+            s.prepared()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(calls):
-            s.call()
+        for i in range(calls):
+            sets[i % len(sets)].prepared()
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -115,6 +122,36 @@ def time_graph(s: DeviceSet, calls: int = 100, replays: int = 20) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
+def time_queued(s, calls: int = 200) -> float:
+    """Device µs per call for launches queued behind a spin kernel, so that
+    the host has enqueued them all before the first one starts."""
+    for _ in range(10):
+        s.prepared()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        s.prepared()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def time_host(fn, calls: int = 2000) -> float:
+    """Host µs per call of a Python-level launch path (GPU work drained once
+    at the end)."""
+    for _ in range(20):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return (t1 - t0) * 1e6 / calls
 
 
 def sources_digest() -> str:
@@ -179,7 +216,6 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE, choices=I.WORKLOAD_ORDER)
     ap.add_argument("--buffer-sets", type=int, default=4,
                     help="independent input/output sets rotated between calls (defeats the MALL)")
-    ap.add_argument("--latency-steps", type=int, default=2000)
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -232,16 +268,18 @@ def main() -> int:
         for name in LATENCY:
             lw = I.WORKLOADS[name]
             lh = I.make_inputs(lw)
-            lsets = [DeviceSet(lw, lh, dev)]
-            warm = time_calls(lsets, args.latency_steps, 50)
-            cold_sets = [DeviceSet(lw, lh, dev) for _ in range(8)]
-            cold = time_calls(cold_sets, args.latency_steps, 50)
-            gus = time_graph(lsets[0])
-            latency[name] = {"us_per_call": round(warm["event_ms_per_call"] * 1e3, 3),
-                             "us_per_call_8_sets": round(cold["event_ms_per_call"] * 1e3, 3),
-                             "us_per_call_graph": round(gus, 3),
-                             "bytes": algorithmic_bytes(lw)}
+            one = [DeviceSet(lw, lh, dev)]
+            eight = [DeviceSet(lw, lh, dev) for _ in range(8)]
+            latency[name] = {
+                "us_per_call_graph": round(time_graph(one), 3),
+                "us_per_call_graph_8_sets": round(time_graph(eight), 3),
+                "us_per_call_queued": round(time_queued(one[0]), 3),
+                "host_us_per_call_binding": round(time_host(one[0].call), 3),
+                "host_us_per_call_prepared": round(time_host(one[0].prepared), 3),
+                "bytes": algorithmic_bytes(lw),
+            }
             log(f"{name}: {latency[name]}")
+            del one, eight
 
     traffic = traffic_entry(nbytes)
     out = {

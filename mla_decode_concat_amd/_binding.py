@@ -144,6 +144,18 @@ def mla_decode_q_concat_kv_insert(q_out: torch.Tensor, ql_nope: torch.Tensor, q_
 
     Flags are the MLA_DQ_* bits; the FP8 bits must agree with the dtypes of
     ``q_out`` and ``cache`` (bf16, or float8_e4m3fn / uint8 codes)."""
+    _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+                   q_scale, kv_scale, flags)
+    dev = q_out.device
+    dims = _dims(ql_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
+    args = (_ptr(q_out), _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(cache),
+            _ptr(slot_mapping), _ptr(positions), _ptr(rope_cos_sin), _ptr(q_scale), _ptr(kv_scale))
+    _launch(args, flags, dims, dev.index, stream)
+
+
+def _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                   rope_cos_sin, q_scale, kv_scale, flags) -> None:
+    """Dtype, shape, layout and device checks the C ABI cannot make."""
     T = ql_nope.shape[0]
     _check(ql_nope.dim() == 3 and ql_nope.shape[2] == 512, "ql_nope must be [T, H, 512]")
     H = ql_nope.shape[1]
@@ -179,22 +191,58 @@ def mla_decode_q_concat_kv_insert(q_out: torch.Tensor, ql_nope: torch.Tensor, q_
     if kv_fp8:
         _check(kv_scale is not None and kv_scale.dtype == torch.float32 and kv_scale.numel() >= 1,
                "KV_FP8 needs an fp32 kv_scale")
-    tensors = [q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
-               q_scale, kv_scale]
     dev = q_out.device
     _check(dev.type == "cuda", "tensors must be on a GPU")
-    for t in tensors:
+    for t in (ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin, q_scale,
+              kv_scale):
         if t is not None:
             _check(t.device == dev, "all tensors must be on the same GPU")
-    dims = _dims(ql_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    with torch.cuda.device(dev):
-        rc = raw_call(_ptr(q_out), _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(cache),
-                      _ptr(slot_mapping), _ptr(positions), _ptr(rope_cos_sin), _ptr(q_scale),
-                      _ptr(kv_scale), flags, dims, stream.cuda_stream)
+
+
+def _raw_stream(index: int, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    return _current_raw_stream(index)
+
+
+try:  # torch's C-level accessor for the current stream's handle (no Stream object)
+    _current_raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover
+    def _current_raw_stream(index):
+        return torch.cuda.current_stream(index).cuda_stream
+
+
+def _launch(args: tuple, flags: int, dims: Dims, index: int, stream) -> None:
+    fn = load().mla_decode_q_concat_kv_insert
+    if index == torch.cuda.current_device():
+        rc = fn(*args, flags, ctypes.byref(dims), _raw_stream(index, stream))
+    else:
+        with torch.cuda.device(index):
+            rc = fn(*args, flags, ctypes.byref(dims), _raw_stream(index, stream))
     if rc != OK:
         raise MlaDqError(rc, strerror(rc))
+
+
+class PreparedInsert:
+    """The epilogue bound to fixed tensors: arguments are checked and
+    marshalled once, and each call only enqueues the launch (for loops over
+    static buffers, e.g. under stream capture).  Same arguments as
+    mla_decode_q_concat_kv_insert; the tensors must stay alive and keep their
+    storage."""
+
+    def __init__(self, q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions=None,
+                 rope_cos_sin=None, q_scale=None, kv_scale=None, flags: int = 0):
+        tensors = (q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                   rope_cos_sin, q_scale, kv_scale)
+        _validate_only(*tensors, flags)
+        self._tensors = tensors
+        self._args = tuple(_ptr(t) for t in tensors)
+        self._dims = _dims(ql_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
+        self._flags = flags
+        self._index = q_out.device.index
+
+    def __call__(self, stream=None) -> None:
+        _launch(self._args, self._flags, self._dims, self._index, stream)
 
 
 def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch.Tensor,

@@ -283,6 +283,55 @@ def test_non_default_stream():
     assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
 
 
+def test_prepared_insert_matches_oracle_twice():
+    announce("prepared insert")
+    w = I.WORKLOADS["t65_h16_rope_fp8"]
+    inp = I.make_inputs(w)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q = torch.empty(w.tokens, w.heads, 576, dtype=torch.float8_e4m3fn, device=DEV)
+    op = M.PreparedInsert(q, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"], dev["cache"],
+                          dev["slot_mapping"], dev["positions"], dev["rope_cos_sin"],
+                          dev["q_scale"], dev["kv_scale"], flags_of(w))
+    want_q, want_cache = oracle_run(w, inp)
+    for _ in range(2):
+        q.view(torch.uint8).fill_(0xFF)
+        op()
+        torch.cuda.synchronize()
+        assert_same(bits(q.cpu()), want_q, "q_out")
+        assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
+
+
+def test_graph_replays_match_eager():
+    """The call captured in a HIP graph, replayed several times with eager
+    work in between, gives the eager bytes every time."""
+    announce("graph replay")
+    w = I.WORKLOADS["t64_h16_rope_fp8"]
+    inp = I.make_inputs(w)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q = torch.empty(w.tokens, w.heads, 576, dtype=torch.float8_e4m3fn, device=DEV)
+    op = M.PreparedInsert(q, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"], dev["cache"],
+                          dev["slot_mapping"], dev["positions"], dev["rope_cos_sin"],
+                          dev["q_scale"], dev["kv_scale"], flags_of(w))
+    want_q, want_cache = oracle_run(w, inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        op()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op()
+    for _ in range(3):
+        q.view(torch.uint8).fill_(0xFF)
+        dev["cache"].view(torch.uint8).fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(bits(q.cpu()), want_q, "q_out")
+        assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
+
+
 def test_binding_rejects_wrong_dtypes():
     w = I.WORKLOADS["t1_h16_copy"]
     inp = I.make_inputs(w)
