@@ -32,6 +32,7 @@ from mla_decode_concat_amd import inputs as I  # noqa: E402
 METRIC = "µs/call at 1/64/65 tokens + achieved HBM GB/s (% of peak) at 8192 tokens"
 HEADLINE = "t8192_h16_rope_kvfp8"
 LATENCY = ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8"]
+MID = ["t256_h128_rope_qfp8"]
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
                   for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
@@ -193,19 +194,28 @@ def cpu_baseline(w: I.Workload, host: dict, budget_s: float) -> dict:
             host["positions"].numpy() if host["positions"] is not None else None,
             host["rope_cos_sin"].numpy() if host["rope_cos_sin"] is not None else None,
             w.q_scale, w.kv_scale, w.rope, w.q_fp8, w.kv_fp8)
-    oracle.insert(*args)                      # warm-up (page faults, thread start)
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.insert(*args)
-        runs += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / runs
-    return {"value": round(algorithmic_bytes(w) / dt / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+    def timed(seconds):
+        oracle.insert(*args)                  # warm-up (page faults, thread start)
+        runs = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.insert(*args)
+            runs += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return (time.perf_counter() - t0) / runs, runs
+
+    cores = oracle.num_threads()
+    dt, runs = timed(budget_s)
+    oracle.set_num_threads(1)
+    dt1, runs1 = timed(budget_s / 3)
+    oracle.set_num_threads(cores)
+    nb = algorithmic_bytes(w)
+    return {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"full {w.name} workload ({w.describe()}), {runs} calls after 1 warm-up, "
-                      f"{dt * 1e3:.1f} ms per call"}
+                      f"{dt * 1e3:.1f} ms per call",
+            "single_thread": {"value": round(nb / dt1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "sample": f"{runs1} calls, {dt1 * 1e3:.1f} ms per call"}}
 
 
 def main() -> int:
@@ -280,6 +290,19 @@ def main() -> int:
             }
             log(f"{name}: {latency[name]}")
             del one, eight
+        for name in MID:
+            mw = I.WORKLOADS[name]
+            mh = I.make_inputs(mw)
+            sets4 = [DeviceSet(mw, mh, dev) for _ in range(4)]
+            warm_us = time_graph(sets4[:1], calls=50, replays=10)
+            cold_us = time_graph(sets4, calls=50, replays=10)
+            nb = algorithmic_bytes(mw)
+            latency[name] = {"us_per_call_graph": round(warm_us, 3),
+                             "us_per_call_graph_4_sets": round(cold_us, 3),
+                             "gbs_graph": round(nb / warm_us / 1e3, 1),
+                             "gbs_graph_4_sets": round(nb / cold_us / 1e3, 1), "bytes": nb}
+            log(f"{name}: {latency[name]}")
+            del sets4
 
     traffic = traffic_entry(nbytes)
     out = {

@@ -83,6 +83,8 @@ def _configure(lib):
     lib.oracle_quant_e4m3_n.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
@@ -205,3 +207,8 @@ def insert(q_out: np.ndarray, ql_nope: np.ndarray, q_pe: np.ndarray,
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the OpenMP loop over tokens (timing only)."""
+    _load().oracle_set_num_threads(int(n))

@@ -245,3 +245,12 @@ void oracle_quant_e4m3_n(const float* x, float inv, uint8_t* out, int64_t n) {
 void oracle_f32_to_bf16_n(const float* x, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16_rne(x[i]);
 }
+
+/* Thread count of the OpenMP loop (timing only; results do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
