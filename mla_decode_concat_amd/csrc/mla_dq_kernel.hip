@@ -157,7 +157,7 @@ __device__ __forceinline__ u32x2 e4m3_of_bf16(u32x4 d, float inv) {
     return pack_e4m3(v, inv);
 }
 
-template <int BLOCK, int RPW, bool STREAM, bool QF8, bool KVF8>
+template <int BLOCK, int RPW, bool STREAM, bool LF, bool QF8, bool KVF8>
 __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) {
     constexpr int kAux = STREAM ? MLA_DQ_STREAM_AUX : 0;
     constexpr uint32_t kWaves = BLOCK / kWave;
@@ -168,79 +168,103 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
     const uint32_t H = a.num_heads;
     const uint32_t row0 = tile * (kWaves * RPW) + wave;
 
-    float q_inv = 1.0f, kv_inv = 1.0f;
-    if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
-    if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
-
     // Wave-uniform row coordinates (scalar registers).  Rows past the end
-    // take row 0's coordinates and zero-sized descriptors.
-    __amdgpu_buffer_rsrc_t src[RPW], qdst[RPW], cdst[RPW];
-    bool is_q[RPW];
+    // take row 0's coordinates and zero-sized descriptors.  The activation
+    // loads go out first: they need nothing but the kernel arguments.
+    uint32_t tok[RPW], head[RPW];
+    bool live[RPW];
+    u32x4 d[RPW];
+    int64_t slot_early[RPW];
+    float q_inv = 1.0f, kv_inv = 1.0f;
+    if constexpr (!LF) {
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+            const uint32_t row = row0 + uint32_t(k) * kWaves;
+            const uint32_t r = row < a.total_rows ? row : 0u;
+            slot_early[k] = a.slot_mapping[fastdiv31(r, a.rows_per_token)];
+        }
+        if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
+        if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
+    }
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
         const uint32_t row = row0 + uint32_t(k) * kWaves;
-        const bool live = row < a.total_rows;
-        const uint32_t r = live ? row : 0u;
-        const uint32_t t = fastdiv31(r, a.rows_per_token);
-        const uint32_t h = r - t * (H + 1);
-        is_q[k] = h < H;
-        // The slot is read for every row (a scalar load, independent of the
-        // activations) and used only by the cache row.
-        const int64_t s = a.slot_mapping[t];
-        const bool slot_ok = s >= 0 && s < a.num_slots;
-        const uint16_t* sp = is_q[k] ? a.ql_nope + uint64_t(t) * a.ql_nope_st + uint64_t(h) * a.ql_nope_sh
-                                     : a.kv_c + uint64_t(t) * a.kv_c_st;
-        src[k] = row_rsrc(sp, live ? 1024u : 0u);
-        qdst[k] = row_rsrc(a.q_out + (uint64_t(t) * H + h) * kQRowBytes,
-                           live && is_q[k] ? kQRowBytes : 0u);
-        cdst[k] = row_rsrc(a.cache + uint64_t(slot_ok ? s : 0) * kKvRowBytes,
-                           live && !is_q[k] && slot_ok ? kKvRowBytes : 0u);
+        live[k] = row < a.total_rows;
+        const uint32_t r = live[k] ? row : 0u;
+        tok[k] = fastdiv31(r, a.rows_per_token);
+        head[k] = r - tok[k] * (H + 1);
+        const uint16_t* sp = head[k] < H ? a.ql_nope + uint64_t(tok[k]) * a.ql_nope_st +
+                                               uint64_t(head[k]) * a.ql_nope_sh
+                                         : a.kv_c + uint64_t(tok[k]) * a.kv_c_st;
+        d[k] = __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(sp, live[k] ? 1024u : 0u),
+                                                     lane * 16u, 0, kAux);
     }
-    u32x4 d[RPW];
-#pragma unroll
-    for (int k = 0; k < RPW; ++k)
-        d[k] = __builtin_amdgcn_raw_buffer_load_b128(src[k], lane * 16u, 0, kAux);
+    // Slot and scales are needed by the stores only.
+    if constexpr (LF) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
+        if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
+    }
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
+        const bool is_q = head[k] < H;
+        const int64_t s = LF ? a.slot_mapping[tok[k]] : slot_early[k];
+        const bool slot_ok = s >= 0 && s < a.num_slots;
+        const __amdgpu_buffer_rsrc_t qdst =
+            row_rsrc(a.q_out + (uint64_t(tok[k]) * H + head[k]) * kQRowBytes,
+                     live[k] && is_q ? kQRowBytes : 0u);
+        const __amdgpu_buffer_rsrc_t cdst =
+            row_rsrc(a.cache + uint64_t(slot_ok ? s : 0) * kKvRowBytes,
+                     live[k] && !is_q && slot_ok ? kKvRowBytes : 0u);
         // Each row is written through exactly one of its two descriptors; the
         // other has zero size, so that store is dropped.
         if constexpr (QF8 == KVF8) {
-            const __amdgpu_buffer_rsrc_t dst = is_q[k] ? qdst[k] : cdst[k];
+            const __amdgpu_buffer_rsrc_t dst = is_q ? qdst : cdst;
             if constexpr (QF8)
-                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_bf16(d[k], is_q[k] ? q_inv : kv_inv),
-                                                      dst, lane * 8u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_bf16(d[k], is_q ? q_inv : kv_inv), dst,
+                                                      lane * 8u, 0, kAux);
             else
                 __builtin_amdgcn_raw_buffer_store_b128(d[k], dst, lane * 16u, 0, kAux);
         } else {
             const u32x2 f8 = e4m3_of_bf16(d[k], QF8 ? q_inv : kv_inv);
             if constexpr (QF8) {
-                __builtin_amdgcn_raw_buffer_store_b64(f8, qdst[k], lane * 8u, 0, kAux);
-                __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst[k], lane * 16u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b64(f8, qdst, lane * 8u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst, lane * 16u, 0, kAux);
             } else {
-                __builtin_amdgcn_raw_buffer_store_b128(d[k], qdst[k], lane * 16u, 0, kAux);
-                __builtin_amdgcn_raw_buffer_store_b64(f8, cdst[k], lane * 8u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b128(d[k], qdst, lane * 16u, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b64(f8, cdst, lane * 8u, 0, kAux);
             }
         }
     }
 }
 
 // ---- positional tails: 8 rows' tails per wavefront step --------------------
-template <int BLOCK, int STEPS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int STEPS, bool STREAM, bool LF, bool ROPE, bool QF8, bool KVF8>
 __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
     constexpr uint32_t kRowsPerStep = BLOCK / 8;
     const uint32_t H = a.num_heads;
     const uint32_t j = threadIdx.x % 8u;           // tail chunk 0..7
     const bool first_half = j < 4u;                // elements 8j..8j+7 < 32
 
-    float q_inv = 1.0f, kv_inv = 1.0f;
-    if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
-    if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
-
     // Lanes past the last row read row 0 (always valid) and store nothing,
-    // so every load below is unconditional.
+    // so every load below is unconditional.  Activations and positions go
+    // first, then the table rows (which need the positions); slots and
+    // scales are needed by the stores only.
     uint32_t tok[STEPS], head[STEPS];
     bool live[STEPS];
-    int64_t slot[STEPS], pos[STEPS];
+    int64_t pos[STEPS], slot[STEPS];
+    u32x4 d[STEPS];
+    float q_inv = 1.0f, kv_inv = 1.0f;
+    if constexpr (!LF) {
+        if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
+        if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) {
+            const uint32_t row = (tile * STEPS + k) * kRowsPerStep + threadIdx.x / 8u;
+            const uint32_t r = row < a.total_rows ? row : 0u;
+            slot[k] = a.slot_mapping[fastdiv31(r, a.rows_per_token)];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
         const uint32_t row = (tile * STEPS + k) * kRowsPerStep + threadIdx.x / 8u;
@@ -248,18 +272,13 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         const uint32_t r = live[k] ? row : 0u;
         tok[k] = fastdiv31(r, a.rows_per_token);
         head[k] = r - tok[k] * (H + 1);
-        slot[k] = a.slot_mapping[tok[k]];
-        pos[k] = 0;
-        if constexpr (ROPE) pos[k] = a.positions[tok[k]];
-    }
-    u32x4 d[STEPS];
-#pragma unroll
-    for (int k = 0; k < STEPS; ++k) {
         const uint64_t t = tok[k];
         const uint16_t* src = head[k] < H
                                   ? a.q_pe + t * a.q_pe_st + uint64_t(head[k]) * a.q_pe_sh
                                   : a.k_pe + t * a.k_pe_st;
         d[k] = load_in<STREAM, u32x4>(src + j * 8u);
+        pos[k] = 0;
+        if constexpr (ROPE) pos[k] = a.positions[t];
     }
     f32x4 cs[ROPE ? STEPS : 1][4];
     if constexpr (ROPE) {
@@ -273,6 +292,13 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
             cs[k][2] = *reinterpret_cast<const f32x4*>(trow + 32);   // sin
             cs[k][3] = *reinterpret_cast<const f32x4*>(trow + 36);
         }
+    }
+    if constexpr (LF) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) slot[k] = a.slot_mapping[tok[k]];
+        if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
+        if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
     }
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
@@ -317,17 +343,47 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
 template <int BLOCK, int RPW, int TAIL_STEPS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
 __global__ void __launch_bounds__(BLOCK)
 mla_dq_epilogue_kernel(const KernelArgs a) {
+    // The latency mapping issues the activation loads before anything the
+    // stores alone need; the throughput mapping reads slots and scales first.
+    constexpr bool kSmall = BLOCK == kSmallMapping.block;
+    constexpr bool LATENT_LF = kSmall ? MLA_DQ_SMALL_LATENT_LF : MLA_DQ_LARGE_LATENT_LF;
+    constexpr bool TAIL_LF = kSmall ? MLA_DQ_SMALL_TAIL_LF : MLA_DQ_LARGE_TAIL_LF;
     const uint32_t b = blockIdx.x;
+#if MLA_DQ_BLOCK_ORDER == 0
     if (b < a.tail_blocks) {
-        tail_rows<BLOCK, TAIL_STEPS, STREAM, ROPE, QF8, KVF8>(a, b);
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, b);
         return;
     }
     uint32_t tile = b - a.tail_blocks;
+#elif MLA_DQ_BLOCK_ORDER == 1
+    const uint32_t latent_blocks = gridDim.x - a.tail_blocks;
+    if (b >= latent_blocks) {
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, b - latent_blocks);
+        return;
+    }
+    uint32_t tile = b;
+#else
+    // groups of one tail workgroup followed by `run` latent workgroups
+    const uint32_t latent_blocks = gridDim.x - a.tail_blocks;
+    const uint32_t run = a.tail_blocks ? latent_blocks / a.tail_blocks : 0u;
+    const uint32_t grouped = a.tail_blocks * (run + 1);
+    uint32_t tile;
+    if (b < grouped) {
+        const uint32_t grp = b / (run + 1), pos = b % (run + 1);
+        if (pos == 0) {
+            tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, grp);
+            return;
+        }
+        tile = grp * run + pos - 1;
+    } else {
+        tile = a.tail_blocks * run + (b - grouped);
+    }
+#endif
 #if MLA_DQ_XCD_REMAP
     // tail_blocks is a multiple of 8, so tile and b share their XCD.
     tile = xcd_contiguous_tile(tile, gridDim.x - a.tail_blocks);
 #endif
-    latent_rows<BLOCK, RPW, STREAM, QF8, KVF8>(a, tile);
+    latent_rows<BLOCK, RPW, STREAM, LATENT_LF, QF8, KVF8>(a, tile);
 }
 
 template <int BLOCK, int RPW, int TS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
