@@ -45,15 +45,24 @@ class Workload:
     q_scale: float = 0.05
     kv_scale: float = 0.05
     max_position: int = ROPE_MAX_POSITION
+    dtype: str = "bf16"          # activations and unquantised outputs: bf16 | fp16
+    rope_style: str = "neox"     # neox (i, i+32) | gptj (2i, 2i+1)
+    table_dtype: str = "f32"     # rope table: f32 | bf16
 
     @property
     def num_slots(self) -> int:
         return self.num_blocks * self.block_size
 
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "fp16" else torch.bfloat16
+
     def describe(self) -> str:
-        bits = []
+        bits = [] if self.dtype == "bf16" else [self.dtype]
         if self.rope:
-            bits.append("rope")
+            bits.append("rope" if self.rope_style == "neox" else "rope_gptj")
+            if self.table_dtype != "f32":
+                bits.append(f"table_{self.table_dtype}")
         if self.q_fp8:
             bits.append(f"q_e4m3(scale={self.q_scale})")
         if self.kv_fp8:
@@ -106,18 +115,18 @@ def shared_rope_table(max_position: int = ROPE_MAX_POSITION) -> torch.Tensor:
 
 def make_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
     """CPU tensors for one workload, drawn in a fixed order from one generator:
-    ql_nope, q_pe, kv_c, k_pe (N(0,1) fp32 rounded to bf16), then slots, then
-    positions.  The cache starts as zeros."""
+    ql_nope, q_pe, kv_c, k_pe (N(0,1) fp32 rounded to the activation type,
+    bf16 or fp16), then slots, then positions.  The cache starts as zeros."""
     g = torch.Generator().manual_seed(seed)
     T, H = w.tokens, w.heads
 
-    def randn_bf16(*shape):
-        return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    def randn_act(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32).to(w.torch_dtype)
 
-    ql_nope = randn_bf16(T, H, NOPE)
-    q_pe = randn_bf16(T, H, PE)
-    kv_c = randn_bf16(T, NOPE)
-    k_pe = randn_bf16(T, PE)
+    ql_nope = randn_act(T, H, NOPE)
+    q_pe = randn_act(T, H, PE)
+    kv_c = randn_act(T, NOPE)
+    k_pe = randn_act(T, PE)
     S = w.num_slots
     if w.slots == "randint":
         slots = torch.randint(0, S, (T,), generator=g, dtype=torch.int64)
@@ -136,11 +145,15 @@ def make_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
         positions = torch.randint(0, hi, (T,), generator=g, dtype=torch.int64)
     else:
         raise ValueError(w.positions)
-    kv_dtype = torch.float8_e4m3fn if w.kv_fp8 else torch.bfloat16
+    kv_dtype = torch.float8_e4m3fn if w.kv_fp8 else w.torch_dtype
     cache = torch.zeros(w.num_blocks, w.block_size, ROW, dtype=kv_dtype)
+    table = None
+    if w.rope:
+        table = shared_rope_table(w.max_position)
+        if w.table_dtype == "bf16":
+            table = table.to(torch.bfloat16)
     out = dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
-               slot_mapping=slots, positions=positions,
-               rope_cos_sin=shared_rope_table(w.max_position) if w.rope else None,
+               slot_mapping=slots, positions=positions, rope_cos_sin=table,
                q_scale=torch.tensor([w.q_scale], dtype=torch.float32) if w.q_fp8 else None,
                kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32) if w.kv_fp8 else None)
     return out
@@ -150,11 +163,13 @@ def custom(tokens: int, heads: int, num_blocks: int | None = None, block_size: i
            rope: bool = False, q_fp8: bool = False, kv_fp8: bool = False,
            positions: str | None = None, slots: str = "randperm", q_scale: float = 0.05,
            kv_scale: float = 0.05, max_position: int = ROPE_MAX_POSITION,
-           name: str = "custom") -> Workload:
+           name: str = "custom", dtype: str = "bf16", rope_style: str = "neox",
+           table_dtype: str = "f32") -> Workload:
     """A workload with the same recipe at another size (ragged tests)."""
     if num_blocks is None:
         num_blocks = max(1, math.ceil(tokens / block_size))
     if positions is None:
         positions = f"uniform:{max_position}" if rope else "none"
     return Workload(name, tokens, heads, num_blocks, block_size, rope, q_fp8, kv_fp8,
-                    slots, positions, q_scale, kv_scale, max_position)
+                    slots, positions, q_scale, kv_scale, max_position, dtype, rope_style,
+                    table_dtype)

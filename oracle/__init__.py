@@ -70,6 +70,24 @@ def _configure(lib):
     lib.oracle_rope_neox_f32.restype = None
     lib.oracle_rope_neox_f64.argtypes = [u16p, f32p, f64p]
     lib.oracle_rope_neox_f64.restype = None
+    lib.oracle_rope_f32.argtypes = [f32p, f32p, f32p, ctypes.c_int, f32p]
+    lib.oracle_rope_f32.restype = None
+    lib.oracle_rope_f64.argtypes = [f32p, f32p, f32p, ctypes.c_int, f64p]
+    lib.oracle_rope_f64.restype = None
+    lib.oracle_fp16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_fp16_rne.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_fp16_rne.restype = ctypes.c_uint16
+    lib.oracle_f32_to_fp16_n.argtypes = [f32p, u16p, ctypes.c_int64]
+    lib.oracle_f32_to_fp16_n.restype = None
+    lib.oracle_fp16_to_f32_n.argtypes = [u16p, f32p, ctypes.c_int64]
+    lib.oracle_fp16_to_f32_n.restype = None
+    lib.oracle_mla_decode_ex.argtypes = [
+        u8p, u16p, u16p, u16p, u16p, u8p, i64p, i64p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_mla_decode_ex.restype = ctypes.c_int
     lib.oracle_mla_decode_q_concat_kv_insert.argtypes = [
         u8p, u16p, u16p, u16p, u16p, u8p, i64p, i64p, f32p,
         ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
@@ -134,7 +152,44 @@ def quant_e4m3_array(x: np.ndarray, scale: float) -> np.ndarray:
     return out
 
 
+def f32_to_fp16_array(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.size, dtype=np.uint16)
+    _load().oracle_f32_to_fp16_n(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def fp16_to_f32_array(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(b.size, dtype=np.float32)
+    _load().oracle_fp16_to_f32_n(_ptr(b, ctypes.c_uint16), _ptr(out, ctypes.c_float), b.size)
+    return out
+
+
 # ---- rotation -----------------------------------------------------------------
+
+def rope_f32(x: np.ndarray, cos_row: np.ndarray, sin_row: np.ndarray, gptj: bool) -> np.ndarray:
+    """fp32 rotation of one 64-wide tail of fp32 values by 32 cos/sin values;
+    NeoX pairing (i, i+32) or, with gptj, interleaved pairing (2i, 2i+1)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(cos_row, dtype=np.float32)
+    s = np.ascontiguousarray(sin_row, dtype=np.float32)
+    assert x.size == 64 and c.size == 32 and s.size == 32
+    y = np.empty(64, dtype=np.float32)
+    _load().oracle_rope_f32(_ptr(x, ctypes.c_float), _ptr(c, ctypes.c_float),
+                            _ptr(s, ctypes.c_float), int(gptj), _ptr(y, ctypes.c_float))
+    return y
+
+
+def rope_f64(x: np.ndarray, cos_row: np.ndarray, sin_row: np.ndarray, gptj: bool) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(cos_row, dtype=np.float32)
+    s = np.ascontiguousarray(sin_row, dtype=np.float32)
+    y = np.empty(64, dtype=np.float64)
+    _load().oracle_rope_f64(_ptr(x, ctypes.c_float), _ptr(c, ctypes.c_float),
+                            _ptr(s, ctypes.c_float), int(gptj), _ptr(y, ctypes.c_double))
+    return y
+
 
 def rope_neox_f32(x_bits: np.ndarray, cs_row: np.ndarray) -> np.ndarray:
     """fp32 NeoX rotation of one 64-wide bf16 tail (bits) by one table row."""
@@ -162,13 +217,15 @@ def insert(q_out: np.ndarray, ql_nope: np.ndarray, q_pe: np.ndarray,
            kv_c: np.ndarray, k_pe: np.ndarray, cache: np.ndarray,
            slots: np.ndarray, positions: np.ndarray | None,
            cos_sin: np.ndarray | None, q_scale: float, kv_scale: float,
-           rope: bool, q_fp8: bool, kv_fp8: bool) -> None:
+           rope: bool, q_fp8: bool, kv_fp8: bool, fp16: bool = False,
+           gptj: bool = False) -> None:
     """Run the oracle in place.
 
-    Arrays are numpy, contiguous: bf16 tensors as uint16 bit patterns, E4M3
-    tensors as uint8 codes.  ``q_out`` is [T, H, 576] (uint16 or uint8),
-    ``cache`` is [num_blocks, block_size, 576] (uint16 or uint8) and is
-    updated in place.
+    Arrays are numpy, contiguous: bf16 or fp16 tensors as uint16 bit
+    patterns, E4M3 tensors as uint8 codes.  ``q_out`` is [T, H, 576] (uint16
+    or uint8), ``cache`` is [num_blocks, block_size, 576] (uint16 or uint8)
+    and is updated in place.  ``cos_sin`` is the [max_position, 64] table as
+    float32, or as uint16 bf16 bit patterns.
     """
     T, H = ql_nope.shape[0], ql_nope.shape[1]
     assert ql_nope.shape == (T, H, 512) and q_pe.shape == (T, H, 64)
@@ -182,25 +239,28 @@ def insert(q_out: np.ndarray, ql_nope: np.ndarray, q_pe: np.ndarray,
     for a in (q_out, ql_nope, q_pe, kv_c, k_pe, cache, slots):
         assert a.flags["C_CONTIGUOUS"]
     slots = np.ascontiguousarray(slots, dtype=np.int64)
+    table_bf16 = False
     if rope:
         positions = np.ascontiguousarray(positions, dtype=np.int64)
-        cos_sin = np.ascontiguousarray(cos_sin, dtype=np.float32)
+        cos_sin = np.ascontiguousarray(cos_sin)
+        assert cos_sin.dtype in (np.float32, np.uint16)
+        table_bf16 = cos_sin.dtype == np.uint16
         assert positions.shape == (T,) and cos_sin.ndim == 2 and cos_sin.shape[1] == 64
         max_pos = cos_sin.shape[0]
         pos_p = _ptr(positions, ctypes.c_int64)
-        cs_p = _ptr(cos_sin, ctypes.c_float)
+        cs_p = cos_sin.ctypes.data_as(ctypes.c_void_p)
     else:
         max_pos = 0
         pos_p = None
         cs_p = None
-    rc = _load().oracle_mla_decode_q_concat_kv_insert(
+    rc = _load().oracle_mla_decode_ex(
         q_out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
         _ptr(ql_nope, ctypes.c_uint16), _ptr(q_pe, ctypes.c_uint16),
         _ptr(kv_c, ctypes.c_uint16), _ptr(k_pe, ctypes.c_uint16),
         cache.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
         _ptr(slots, ctypes.c_int64), pos_p, cs_p,
         float(q_scale), float(kv_scale), T, H, num_slots, max_pos,
-        int(rope), int(q_fp8), int(kv_fp8))
+        int(rope), int(q_fp8), int(kv_fp8), int(fp16), int(gptj), int(table_bf16))
     if rc != 0:
         raise ValueError(f"oracle rejected the shapes (rc={rc})")
 

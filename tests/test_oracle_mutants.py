@@ -20,14 +20,24 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "mla_oracle.c")
 
 # (name, text in the source, replacement) -- each text occurs exactly once
 MUTANTS = [
-    ("rope_sign", "y[i] = ac - bs;", "y[i] = ac + bs;"),
-    ("rope_dropped_term", "y[i + HALF] = bc + as;", "y[i + HALF] = bc;"),
-    ("rope_pair_index", "float b = oracle_bf16_to_f32(x[i + HALF]);\n        float c = cs[i], s = cs[HALF + i];\n        float ac",
-     "float b = oracle_bf16_to_f32(x[i + HALF - 1]);\n        float c = cs[i], s = cs[HALF + i];\n        float ac"),
-    ("rope_cos_sin_swapped", "float c = cs[i], s = cs[HALF + i];\n        float ac",
-     "float c = cs[HALF + i], s = cs[i];\n        float ac"),
+    ("rope_sign", "y[i0] = ac - bs;", "y[i0] = ac + bs;"),
+    ("rope_dropped_term", "y[i1] = bc + as;", "y[i1] = bc;"),
+    ("rope_neox_pair_index", "*i1 = p + HALF; }", "*i1 = p + HALF - 1; }"),
+    ("rope_gptj_pair_swapped", "*i0 = 2 * p; *i1 = 2 * p + 1; }", "*i0 = 2 * p + 1; *i1 = 2 * p; }"),
+    ("rope_cos_sin_swapped", "float a = x[i0], b = x[i1], c = cos_row[p], s = sin_row[p];",
+     "float a = x[i0], b = x[i1], c = sin_row[p], s = cos_row[p];"),
+    ("table_bf16_read_as_fp16", "c[p] = oracle_bf16_to_f32(t[p]);", "c[p] = oracle_fp16_to_f32(t[p]);"),
+    ("q_rotated_at_position_zero",
+     "q_pe + (size_t)r * PE, rope, gptj, trow,", "q_pe + (size_t)r * PE, rope, gptj, table,"),
+    ("k_pe_not_rotated", "k_pe + (size_t)t * PE, rope, gptj", "k_pe + (size_t)t * PE, 0, gptj"),
     ("bf16_truncates", "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))", "if (0)"),
     ("bf16_ties_away", "(lo == 0x8000u && (hi & 1u))", "(lo == 0x8000u)"),
+    ("fp16_decode_bias", "ldexp(1.0 + m / 1024.0, e - 15)", "ldexp(1.0 + m / 1024.0, e - 16)"),
+    ("fp16_encode_bias", "(uint16_t)((ue + 15) << 10)", "(uint16_t)((ue + 16) << 10)"),
+    ("fp16_overflow_threshold", "if (a >= 65520.0) return", "if (a >= 131072.0) return"),
+    ("fp16_subnormal_step", "round_half_even(a * 16777216.0)", "round_half_even(a * 8388608.0)"),
+    ("fp16_activations_read_as_bf16", "return fp16 ? oracle_fp16_to_f32(v) : oracle_bf16_to_f32(v);",
+     "return oracle_bf16_to_f32(v);"),
     ("e4m3_ties_up", "return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "return f + 1.0;"),
     ("e4m3_no_saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
      "if (a >= 480.0) return (uint8_t)(sign | 0x7F);"),
@@ -38,12 +48,16 @@ MUTANTS = [
     ("scatter_by_token", "write_row(cache + (size_t)s * kv_row_bytes", "write_row(cache + (size_t)t * kv_row_bytes"),
     ("slot_zero_skipped", "if (s < 0 || s >= num_slots) continue;", "if (s <= 0 || s >= num_slots) continue;"),
     ("q_rows_transposed", "int64_t r = t * H + h;", "int64_t r = h * T + t;"),
-    ("k_pe_not_rotated", "k_pe + (size_t)t * PE, rope, cs_row", "k_pe + (size_t)t * PE, 0, cs_row"),
-    ("q_pe_rotated_with_first_position", "write_row(q_out + (size_t)r * q_row_bytes, ql_nope + (size_t)r * NOPE,\n                      q_pe + (size_t)r * PE, rope, cs_row,",
-     "write_row(q_out + (size_t)r * q_row_bytes, ql_nope + (size_t)r * NOPE,\n                      q_pe + (size_t)r * PE, rope, rope ? cs + clamp_pos(positions[0], max_position) * PE : 0,"),
 ]
 
 CHECKS = [
+    P.test_fp16_golden_points,
+    P.test_fp16_decode_all_patterns_vs_numpy,
+    P.test_fp16_rne_vs_numpy,
+    P.test_gptj_rope_golden_rows,
+    P.test_gptj_rope_is_complex_rotation_by_position_angle,
+    lambda: P.test_oracle_matches_library_composition_variants("bf16", "neox", "bf16", False, False),
+    lambda: P.test_oracle_matches_library_composition_variants("fp16", "gptj", "f32", True, False),
     P.test_e4m3_golden_points,
     P.test_e4m3_matches_brute_force_on_all_bf16,
     P.test_bf16_golden_points,

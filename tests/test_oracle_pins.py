@@ -168,6 +168,47 @@ def test_bf16_identity_on_exact_values():
     assert np.array_equal(got[ok], b[ok].astype(np.uint16))
 
 
+# ---------------------------------------------------------------- fp16 ----
+
+def test_fp16_golden_points():
+    g = _golden("fp16_points.json")
+    for p in g["round"]:
+        x = np.array([_f(p["x"])], dtype=np.float32)
+        assert oracle.f32_to_fp16_array(x)[0] == int(p["fp16"], 16), p
+
+
+def test_fp16_rne_vs_numpy():
+    """numpy's float32 -> float16 cast is IEEE round-to-nearest-even."""
+    rng = np.random.default_rng(6)
+    u = rng.integers(0, 1 << 32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    # dense coverage of the fp16 range, its ties and neighbours
+    e = rng.integers(-26, 17, size=1_000_000)
+    m = rng.random(1_000_000)
+    y = (np.ldexp(1.0 + m, e) * np.where(rng.random(1_000_000) < 0.5, -1, 1)).astype(np.float32)
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    h = h[np.isfinite(h)]
+    hs = np.unique(h)
+    mids = ((hs[:-1] + hs[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, y, mids, np.nextafter(mids, np.float32(np.inf)),
+                        np.nextafter(mids, np.float32(-np.inf))])
+    got = oracle.f32_to_fp16_array(x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.all((got[nan] & 0x7C00) == 0x7C00) and np.all((got[nan] & 0x3FF) != 0)
+
+
+def test_fp16_decode_all_patterns_vs_numpy():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.fp16_to_f32_array(b)
+    want = b.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
 # ---------------------------------------------------------------- RoPE ----
 
 def _x_bits(seed=0, scale=1.0):
@@ -188,6 +229,58 @@ def test_rope_golden_rows():
         cs = np.array([row["cos"]] * 32 + [row["sin"]] * 32, dtype=np.float32)
         y = oracle.rope_neox_f32(xb, cs)
         assert np.array_equal(y, np.array(row["y"], dtype=np.float32)), row["name"]
+
+
+def test_gptj_rope_golden_rows():
+    g = _golden("rope_rows.json")
+    x = np.array(g["x"], dtype=np.float32)
+    for row in g["rows_gptj"]:
+        c = np.full(32, row["cos"], dtype=np.float32)
+        s_ = np.full(32, row["sin"], dtype=np.float32)
+        y = oracle.rope_f32(x, c, s_, gptj=True)
+        assert np.array_equal(y, np.array(row["y"], dtype=np.float32)), row["name"]
+
+
+def test_general_rotation_neox_matches_bf16_entry():
+    table = I.rope_table(64).numpy()
+    for seed in range(10):
+        xb = _x_bits(900 + seed, scale=3.0)
+        a = oracle.rope_neox_f32(xb, table[37])
+        b = oracle.rope_f32(_f32(xb), table[37, :32], table[37, 32:], gptj=False)
+        assert np.array_equal(a, b)
+
+
+def test_gptj_rope_is_complex_rotation_by_position_angle():
+    """Interleaved pairing as complex numbers: (x_2p + j x_2p+1) * exp(j pos
+    theta^(-2p/64)), evaluated in float64 from the angle."""
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(7)
+    p_idx = np.arange(32, dtype=np.float64)
+    inv_freq = 10000.0 ** (-2.0 * p_idx / 64.0)
+    for trial in range(200):
+        pos = int(rng.integers(0, 4096))
+        x = _f32(_x_bits(1100 + trial, scale=3.0))
+        z = (x[0::2].astype(np.float64) + 1j * x[1::2]) * np.exp(1j * pos * inv_freq)
+        want = np.empty(64)
+        want[0::2], want[1::2] = z.real, z.imag
+        got = oracle.rope_f32(x, table[pos, :32], table[pos, 32:], gptj=True).astype(np.float64)
+        mag = np.abs(x[0::2]).astype(np.float64) + np.abs(x[1::2])
+        tol = 3.0 * 2.0 ** -24 * np.repeat(mag, 2) + 1e-30
+        assert np.all(np.abs(got - want) <= tol)
+
+
+def test_gptj_rope_matches_library_rotate_every_two():
+    table = I.rope_table(4096)
+    rng = np.random.default_rng(8)
+    for trial in range(100):
+        pos = int(rng.integers(0, 4096))
+        x = torch.from_numpy(_f32(_x_bits(1300 + trial, scale=4.0)).copy())
+        cos = table[pos, :32].repeat_interleave(2)
+        sin = table[pos, 32:].repeat_interleave(2)
+        rot = torch.stack([-x[1::2], x[0::2]], dim=-1).reshape(64)
+        want = (x * cos + rot * sin).numpy()
+        got = oracle.rope_f32(x.numpy(), table[pos, :32].numpy(), table[pos, 32:].numpy(), gptj=True)
+        assert np.array_equal(got, want)
 
 
 def test_rope_position_zero_is_identity():
@@ -289,27 +382,36 @@ def test_page_identity_concat_and_scatter(num_tokens):
 
 
 def _torch_textbook(w, inp):
-    """Library composition: cat, eager fp32 rotate_half rotation, bf16 cast or
-    clamp + float8_e4m3fn cast.  Used only to pin the oracle."""
-    T, H = w.tokens, w.heads
+    """Library composition: cat, eager fp32 rotate_half / rotate_every_two
+    rotation, activation-type cast or clamp + float8_e4m3fn cast.  Used only
+    to pin the oracle."""
     pe_q = inp["q_pe"].float()
     pe_k = inp["k_pe"].float()
+    act = w.torch_dtype
     if w.rope:
-        cs = inp["rope_cos_sin"][inp["positions"].clamp(0, w.max_position - 1)]
-        cos = torch.cat([cs[:, :32], cs[:, :32]], dim=-1)
-        sin = torch.cat([cs[:, 32:], cs[:, 32:]], dim=-1)
+        cs = inp["rope_cos_sin"].float()[inp["positions"].clamp(0, w.max_position - 1)]
+        if w.rope_style == "gptj":
+            cos = cs[:, :32].repeat_interleave(2, dim=-1)
+            sin = cs[:, 32:].repeat_interleave(2, dim=-1)
 
-        def rot(x, c, s):
-            return x * c + torch.cat([-x[..., 32:], x[..., :32]], dim=-1) * s
+            def rot(x, c, s):
+                r = torch.stack([-x[..., 1::2], x[..., 0::2]], dim=-1).reshape(x.shape)
+                return x * c + r * s
+        else:
+            cos = torch.cat([cs[:, :32], cs[:, :32]], dim=-1)
+            sin = torch.cat([cs[:, 32:], cs[:, 32:]], dim=-1)
+
+            def rot(x, c, s):
+                return x * c + torch.cat([-x[..., 32:], x[..., :32]], dim=-1) * s
         pe_q = rot(pe_q, cos[:, None, :], sin[:, None, :])
         pe_k = rot(pe_k, cos, sin)
 
-    def enc(nope_bf16, pe_f32, fp8, scale):
+    def enc(nope, pe_f32, fp8, scale):
         if fp8:
             inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
-            v = torch.cat([nope_bf16.float(), pe_f32], dim=-1) * inv
+            v = torch.cat([nope.float(), pe_f32], dim=-1) * inv
             return bits(torch.clamp(v, -448, 448).to(torch.float8_e4m3fn))
-        return bits(torch.cat([nope_bf16, pe_f32.to(torch.bfloat16)], dim=-1))
+        return bits(torch.cat([nope, pe_f32.to(act)], dim=-1))
     q = enc(inp["ql_nope"], pe_q, w.q_fp8, w.q_scale)
     kv = enc(inp["kv_c"], pe_k, w.kv_fp8, w.kv_scale)
     return q, kv
@@ -336,6 +438,29 @@ def test_oracle_matches_library_composition_all_modes(flags):
     want_q, want_kv = _torch_textbook(w, inp)
     assert np.array_equal(q, want_q)
     assert np.array_equal(cache.reshape(-1, 576)[inp["slot_mapping"].numpy()], want_kv)
+
+
+@pytest.mark.parametrize("dtype,style,table", [("fp16", "neox", "f32"), ("bf16", "gptj", "f32"),
+                                               ("bf16", "neox", "bf16"), ("fp16", "gptj", "bf16")])
+@pytest.mark.parametrize("qf,kf", [(False, False), (True, False), (False, True), (True, True)])
+def test_oracle_matches_library_composition_variants(dtype, style, table, qf, kf):
+    w = I.custom(29, 3, num_blocks=2, rope=True, q_fp8=qf, kv_fp8=kf, q_scale=0.03, kv_scale=0.2,
+                 dtype=dtype, rope_style=style, table_dtype=table)
+    inp = I.make_inputs(w, seed=10)
+    q, cache = oracle_run(w, inp)
+    want_q, want_kv = _torch_textbook(w, inp)
+    assert np.array_equal(q, want_q)
+    assert np.array_equal(cache.reshape(-1, 576)[inp["slot_mapping"].numpy()], want_kv)
+
+
+def test_fp16_copy_path_is_identity():
+    w = I.custom(40, 4, num_blocks=1, dtype="fp16")
+    inp = I.make_inputs(w, seed=12)
+    q, cache = oracle_run(w, inp)
+    assert np.array_equal(q, bits(torch.cat([inp["ql_nope"], inp["q_pe"]], dim=-1)))
+    rows = cache.reshape(-1, 576)
+    assert np.array_equal(rows[inp["slot_mapping"].numpy()],
+                          bits(torch.cat([inp["kv_c"], inp["k_pe"]], dim=-1)))
 
 
 def test_row_independence_prefix_property():
