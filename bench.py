@@ -33,6 +33,10 @@ METRIC = "µs/call at 1/64/65 tokens + achieved HBM GB/s (% of peak) at 8192 tok
 HEADLINE = "t8192_h16_rope_kvfp8"
 LATENCY = ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8"]
 MID = ["t256_h128_rope_qfp8"]
+# The headline shape in the other element type, rotation style and table type.
+VARIANTS = {"fp16": dict(dtype="fp16"), "gptj": dict(rope_style="gptj"),
+            "table_bf16": dict(table_dtype="bf16"),
+            "fp16_gptj_table_bf16": dict(dtype="fp16", rope_style="gptj", table_dtype="bf16")}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
                   for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
@@ -50,13 +54,21 @@ def algorithmic_bytes(w: I.Workload) -> int:
     bytes), the slot (8 B) per token and, with rotation, the position (8 B)
     and one 256-B cos/sin table row per token."""
     T, H = w.tokens, w.heads
-    read = T * (H * 1152 + 1152 + 8 + (8 + 256 if w.rope else 0))
+    table_row = 128 if w.table_dtype == "bf16" else 256
+    read = T * (H * 1152 + 1152 + 8 + (8 + table_row if w.rope else 0))
     write = T * 576 * (H * (1 if w.q_fp8 else 2) + (1 if w.kv_fp8 else 2))
     return read + write
 
 
 def flags_of(w: I.Workload) -> int:
-    return (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+    f = (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+    if w.dtype == "fp16":
+        f |= M.FP16
+    if w.rope and w.rope_style == "gptj":
+        f |= M.ROPE_GPTJ
+    if w.rope and w.table_dtype == "bf16":
+        f |= M.TABLE_BF16
+    return f
 
 
 class DeviceSet:
@@ -66,7 +78,7 @@ class DeviceSet:
         self.w = w
         self.t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in host.items()}
         self.q = torch.empty(w.tokens, w.heads, I.ROW, device=dev,
-                             dtype=torch.float8_e4m3fn if w.q_fp8 else torch.bfloat16)
+                             dtype=torch.float8_e4m3fn if w.q_fp8 else w.torch_dtype)
         self.flags = flags_of(w)
         t = self.t
         self.prepared = M.PreparedInsert(self.q, t["ql_nope"], t["q_pe"], t["kv_c"], t["k_pe"],
@@ -227,6 +239,7 @@ def main() -> int:
     ap.add_argument("--buffer-sets", type=int, default=4,
                     help="independent input/output sets rotated between calls (defeats the MALL)")
     ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -304,6 +317,22 @@ def main() -> int:
             log(f"{name}: {latency[name]}")
             del sets4
 
+    variants = {}
+    if not args.no_variants:
+        import dataclasses
+        for vname, kw in VARIANTS.items():
+            vw = dataclasses.replace(w, name=f"{w.name}_{vname}", **kw)
+            vh = I.make_inputs(vw)
+            vsets = [DeviceSet(vw, vh, dev) for _ in range(max(1, args.buffer_sets))]
+            vr = time_calls(vsets, max(20, args.steps // 4), 5)
+            vb = algorithmic_bytes(vw)
+            variants[vname] = {"us_per_call": round(vr["event_ms_per_call"] * 1e3, 3),
+                               "gbs": round(vb / vr["event_ms_per_call"] / 1e6, 1),
+                               "bytes": vb}
+            log(f"variant {vname}: {variants[vname]}")
+            del vsets
+            torch.cuda.empty_cache()
+
     traffic = traffic_entry(nbytes)
     out = {
         "metric": METRIC,
@@ -328,6 +357,7 @@ def main() -> int:
                    "rows_per_wave": pl.rows_per_wave, "tail_steps": pl.tail_steps},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "latency_us": latency,
+        "variants_at_headline_shape": variants,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,

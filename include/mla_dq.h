@@ -15,12 +15,14 @@
  * (rotation and FP8 off): q is cat(ql_nope, q_pe) and the cache rows at the
  * slots are cat(kv_c, k_pe); nothing else in the cache changes.
  *
- *   rope(x, p): NeoX half-split rotation; element i pairs with i+32, angle
- *     from row p of the caller's table; y[i] = x[i]c - x[i+32]s,
- *     y[i+32] = x[i+32]c + x[i]s in fp32, each product and sum rounded
- *     separately.  Identity (bit copy) when MLA_DQ_ROPE is off.
- *   enc (bf16 output): bit copy of untouched bf16 input, round-to-nearest-
- *     even bf16 of rotated fp32 values.
+ *   rope(x, p): NeoX half-split rotation; pair k (k < 32) is elements
+ *     (k, k+32), or (2k, 2k+1) with MLA_DQ_ROPE_GPTJ, and turns by the angle
+ *     whose cos and sin are columns k and 32+k of row p of the caller's
+ *     table: first = a*c - b*s, second = b*c + a*s for the pair (a, b), in
+ *     fp32, each product and sum rounded separately.  Identity (bit copy)
+ *     when MLA_DQ_ROPE is off.
+ *   enc (bf16 or fp16 output): bit copy of untouched input, round-to-
+ *     nearest-even of rotated fp32 values.
  *   enc (E4M3 output): OCP FP8 E4M3 of fl32(x * fl32(1/scale)) clamped to
  *     [-448, 448] (NaN stays NaN), rounded to nearest even.
  *
@@ -52,6 +54,14 @@ extern "C" {
 #define MLA_DQ_ROPE    (1u << 0) /* rotate the 64-wide tails of q and k     */
 #define MLA_DQ_Q_FP8   (1u << 1) /* q_out holds E4M3 codes (else bf16)      */
 #define MLA_DQ_KV_FP8  (1u << 2) /* cache holds E4M3 codes (else bf16)      */
+/* Variants (the page's kernel is templated on the element type; the other
+ * two are the common alternatives of the rotary embedding):              */
+#define MLA_DQ_FP16       (1u << 3) /* activations, and unquantised q_out and
+                                       cache, are fp16 instead of bf16     */
+#define MLA_DQ_ROPE_GPTJ  (1u << 4) /* interleaved pairs (2i, 2i+1) instead
+                                       of NeoX halves (i, i+32); needs ROPE */
+#define MLA_DQ_TABLE_BF16 (1u << 5) /* rope_cos_sin holds bf16 instead of
+                                       fp32; needs ROPE                    */
 /* Launch overrides for tests and sweeps; they never change the results.
  * By default the library picks the latency mapping (one latent row per
  * wavefront in 64-thread workgroups) while T * (H + 1) is small and the
@@ -98,20 +108,23 @@ typedef struct mla_dq_dims {
  * "implementation breakdown" item 3 and the op the test calls in "key source
  * snippets").  All pointers are DEVICE pointers except `dims`, a host pointer.
  *
- *   q_out         [T, H, 576] dense; bf16, or E4M3 bytes with MLA_DQ_Q_FP8.
- *                 16-byte aligned.  Written in full.
- *   ql_nope       bf16 [T, H, 512] (strided, see mla_dq_dims), 16-B aligned.
- *   q_pe          bf16 [T, H, 64]  (strided), 16-B aligned.
- *   kv_c          bf16 [T, 512]    (strided), 16-B aligned.
- *   k_pe          bf16 [T, 64]     (strided), 16-B aligned.
- *   cache         [num_blocks, block_size, 576] dense; bf16, or E4M3 bytes
- *                 with MLA_DQ_KV_FP8.  16-B aligned.  Only the rows at valid
- *                 slots are written.
+ *   q_out         [T, H, 576] dense; the activation type (bf16, or fp16 with
+ *                 MLA_DQ_FP16), or E4M3 bytes with MLA_DQ_Q_FP8.  16-byte
+ *                 aligned.  Written in full.
+ *   ql_nope       [T, H, 512] activations (strided, see mla_dq_dims), 16-B
+ *                 aligned.
+ *   q_pe          [T, H, 64]  activations (strided), 16-B aligned.
+ *   kv_c          [T, 512]    activations (strided), 16-B aligned.
+ *   k_pe          [T, 64]     activations (strided), 16-B aligned.
+ *   cache         [num_blocks, block_size, 576] dense; the activation type,
+ *                 or E4M3 bytes with MLA_DQ_KV_FP8.  16-B aligned.  Only the
+ *                 rows at valid slots are written.
  *   slot_mapping  int64 [T], 8-B aligned.
  *   positions     int64 [T], 8-B aligned; required with MLA_DQ_ROPE, else
  *                 ignored (may be NULL).
- *   rope_cos_sin  fp32 [max_position, 64]: row p = cos of the 32 angles, then
- *                 their sin.  16-B aligned; required with MLA_DQ_ROPE.
+ *   rope_cos_sin  [max_position, 64] fp32 (bf16 with MLA_DQ_TABLE_BF16): row p
+ *                 = cos of the 32 angles, then their sin.  16-B aligned;
+ *                 required with MLA_DQ_ROPE.
  *   q_scale       fp32 scalar; required with MLA_DQ_Q_FP8 (may be NULL else).
  *   kv_scale      fp32 scalar; required with MLA_DQ_KV_FP8 (may be NULL else).
  *   flags         MLA_DQ_* bits.

@@ -4,7 +4,7 @@ The work runs in a hand-written HIP kernel behind the C ABI of
 include/mla_dq.h (libmla_dq.so); this package is its Python binding.
 """
 from ._binding import (  # noqa: F401
-    ROPE, Q_FP8, KV_FP8, FORCE_SMALL_T, FORCE_LARGE_T, FORCE_STREAM, FORCE_CACHED,
+    ROPE, Q_FP8, KV_FP8, FP16, ROPE_GPTJ, TABLE_BF16, FORCE_SMALL_T, FORCE_LARGE_T, FORCE_STREAM, FORCE_CACHED,
     MlaDqError, Dims, LaunchPlan, fused_mla_decode_q_concat_kv_cache_insert,
     mla_decode_q_concat_kv_insert, PreparedInsert, plan, strerror, load,
 )

@@ -20,6 +20,9 @@ from . import build as _build
 ROPE = 1 << 0
 Q_FP8 = 1 << 1
 KV_FP8 = 1 << 2
+FP16 = 1 << 3
+ROPE_GPTJ = 1 << 4
+TABLE_BF16 = 1 << 5
 FORCE_SMALL_T = 1 << 8
 FORCE_LARGE_T = 1 << 9
 FORCE_STREAM = 1 << 10
@@ -166,25 +169,27 @@ def _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positi
            "q_out must be a contiguous [T, H, 576] tensor")
     _check(cache.dim() == 3 and cache.shape[2] == 576 and cache.is_contiguous(),
            "cache must be a contiguous [num_blocks, block_size, 576] tensor")
+    act = torch.float16 if flags & FP16 else torch.bfloat16
     for name, t in (("ql_nope", ql_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe)):
-        _check(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+        _check(t.dtype == act, f"{name} must be {act} (flag FP16 selects fp16)")
         _check(t.stride(-1) == 1, f"{name} must have unit inner stride")
     _check(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,)
            and slot_mapping.is_contiguous(), "slot_mapping must be a contiguous int64 [T]")
     q_fp8 = bool(flags & Q_FP8)
     kv_fp8 = bool(flags & KV_FP8)
-    _check((q_out.dtype in _FP8) == q_fp8 and (q_fp8 or q_out.dtype == torch.bfloat16),
-           "q_out dtype must be e4m3 with Q_FP8, bfloat16 without")
-    _check((cache.dtype in _FP8) == kv_fp8 and (kv_fp8 or cache.dtype == torch.bfloat16),
-           "cache dtype must be e4m3 with KV_FP8, bfloat16 without")
+    _check((q_out.dtype in _FP8) == q_fp8 and (q_fp8 or q_out.dtype == act),
+           "q_out dtype must be e4m3 with Q_FP8, the activation type without")
+    _check((cache.dtype in _FP8) == kv_fp8 and (kv_fp8 or cache.dtype == act),
+           "cache dtype must be e4m3 with KV_FP8, the activation type without")
     if flags & ROPE:
         _check(positions is not None and rope_cos_sin is not None,
                "ROPE needs positions and rope_cos_sin")
         _check(positions.dtype == torch.int64 and tuple(positions.shape) == (T,)
                and positions.is_contiguous(), "positions must be a contiguous int64 [T]")
-        _check(rope_cos_sin.dtype == torch.float32 and rope_cos_sin.dim() == 2
+        tdt = torch.bfloat16 if flags & TABLE_BF16 else torch.float32
+        _check(rope_cos_sin.dtype == tdt and rope_cos_sin.dim() == 2
                and rope_cos_sin.shape[1] == 64 and rope_cos_sin.is_contiguous(),
-               "rope_cos_sin must be a contiguous fp32 [max_position, 64]")
+               f"rope_cos_sin must be a contiguous {tdt} [max_position, 64]")
     if q_fp8:
         _check(q_scale is not None and q_scale.dtype == torch.float32 and q_scale.numel() >= 1,
                "Q_FP8 needs an fp32 q_scale")
@@ -252,20 +257,30 @@ def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch
                                               rope_cos_sin: torch.Tensor | None = None,
                                               q_scale: torch.Tensor | None = None,
                                               kv_scale: torch.Tensor | None = None,
-                                              q_fp8: bool = False) -> torch.Tensor:
+                                              q_fp8: bool = False,
+                                              rope_style: str = "neox") -> torch.Tensor:
     """The page's user-level call: allocates and returns q [T, H, 576] and
     updates ``cache`` in place.  RoPE is on when positions and a table are
-    given; the cache's FP8-ness follows its dtype."""
+    given (``rope_style`` "neox" or "gptj"); fp16 activations, a bf16 table
+    and an e4m3 cache follow from the tensors' dtypes."""
     T, H = ql_nope.shape[0], ql_nope.shape[1]
     flags = 0
     if positions is not None or rope_cos_sin is not None:
         flags |= ROPE
+        if rope_style == "gptj":
+            flags |= ROPE_GPTJ
+        elif rope_style != "neox":
+            raise ValueError("rope_style must be 'neox' or 'gptj'")
+        if rope_cos_sin is not None and rope_cos_sin.dtype == torch.bfloat16:
+            flags |= TABLE_BF16
+    if ql_nope.dtype == torch.float16:
+        flags |= FP16
     if q_fp8:
         flags |= Q_FP8
     if cache.dtype in _FP8:
         flags |= KV_FP8
     q = torch.empty((T, H, 576), device=ql_nope.device,
-                    dtype=torch.float8_e4m3fn if q_fp8 else torch.bfloat16)
+                    dtype=torch.float8_e4m3fn if q_fp8 else ql_nope.dtype)
     mla_decode_q_concat_kv_insert(q, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
                                   rope_cos_sin, q_scale, kv_scale, flags)
     return q

@@ -50,12 +50,14 @@ int64_t stream_bytes_min() {
     return v;
 }
 
-// Bytes one call reads and writes: each 576-wide input row once as bf16, each
-// output row once, plus slot, position and rope table row per token.
+// Bytes one call reads and writes: each 576-wide input row once (2-byte
+// elements), each output row once, plus slot, position and rope table row
+// per token.
 int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
     const int64_t T = d->num_tokens, H = d->num_heads;
     const bool rope = flags & MLA_DQ_ROPE;
-    const int64_t read = T * (H * 1152 + 1152 + 8 + (rope ? 8 + 256 : 0));
+    const int64_t table_row = (flags & MLA_DQ_TABLE_BF16) ? 128 : 256;
+    const int64_t read = T * (H * 1152 + 1152 + 8 + (rope ? 8 + table_row : 0));
     const int64_t write = T * 576 * (H * ((flags & MLA_DQ_Q_FP8) ? 1 : 2) +
                                      ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
     return read + write;
@@ -64,9 +66,12 @@ int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
 // Checks that do not need any pointer: flags and shapes.
 int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
     if (d == nullptr) return MLA_DQ_ERR_NULL;
-    const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FORCE_SMALL_T |
+    const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FP16 |
+                           MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16 | MLA_DQ_FORCE_SMALL_T |
                            MLA_DQ_FORCE_LARGE_T | MLA_DQ_FORCE_STREAM | MLA_DQ_FORCE_CACHED;
     if (flags & ~known) return MLA_DQ_ERR_FLAGS;
+    if ((flags & (MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16)) && !(flags & MLA_DQ_ROPE))
+        return MLA_DQ_ERR_FLAGS;
     if ((flags & MLA_DQ_FORCE_SMALL_T) && (flags & MLA_DQ_FORCE_LARGE_T)) return MLA_DQ_ERR_FLAGS;
     if ((flags & MLA_DQ_FORCE_STREAM) && (flags & MLA_DQ_FORCE_CACHED)) return MLA_DQ_ERR_FLAGS;
     const int64_t T = d->num_tokens, H = d->num_heads;
@@ -213,6 +218,9 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
     a.num_heads = uint32_t(dims->num_heads);
     a.total_rows = uint32_t(p.total_rows);
     a.tail_blocks = uint32_t(p.tail_blocks);
+    a.fp16 = (flags & MLA_DQ_FP16) ? 1u : 0u;
+    a.gptj = (flags & MLA_DQ_ROPE_GPTJ) ? 1u : 0u;
+    a.table_bf16 = (flags & MLA_DQ_TABLE_BF16) ? 1u : 0u;
     const hipError_t e = mla_dq::launch(a, p, flags, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
 }

@@ -108,6 +108,9 @@ struct KernelArgs {
     uint32_t num_heads;
     uint32_t total_rows;        // T * (H + 1)
     uint32_t tail_blocks;       // workgroups [0, tail_blocks) do the tails
+    uint32_t fp16;              // activations are fp16 (else bf16)
+    uint32_t gptj;              // interleaved rotation pairs
+    uint32_t table_bf16;        // rope table holds bf16 (else fp32)
 };
 
 // Host-side validation and planning (pure host code, no HIP calls).

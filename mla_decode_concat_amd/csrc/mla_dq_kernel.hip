@@ -54,6 +54,7 @@ namespace mla_dq {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -76,6 +77,23 @@ __device__ __forceinline__ void unpack_bf16(u32x4 d, float (&v)[8]) {
     for (int p = 0; p < 4; ++p) {
         v[2 * p] = bf16_lo(d[p]);
         v[2 * p + 1] = bf16_hi(d[p]);
+    }
+}
+
+// Eight activations (bf16 or fp16 bit patterns) -> eight exact fp32 values.
+__device__ __forceinline__ void unpack_act(u32x4 d, float (&v)[8], bool fp16) {
+    if (fp16) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            // through a scalar: a bit cast of the vector element expression
+            // itself reads element 0 whatever p is
+            const uint32_t word = d[p];
+            const f16x2 h = __builtin_bit_cast(f16x2, word);
+            v[2 * p] = (float)h.x;
+            v[2 * p + 1] = (float)h.y;
+        }
+    } else {
+        unpack_bf16(d, v);
     }
 }
 
@@ -123,6 +141,18 @@ __device__ __forceinline__ u32x4 pack_bf16(const float (&v)[8]) {
     return r;
 }
 
+// Eight fp32 values -> eight fp16 (round to nearest even), value 0 lowest.
+__device__ __forceinline__ u32x4 pack_f16(const float (&v)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        f32x2 f = {v[2 * p], v[2 * p + 1]};
+        f16x2 h = __builtin_convertvector(f, f16x2);
+        r[p] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
 template <bool STREAM, typename V>
 __device__ __forceinline__ void store_out(uint8_t* p, V v) {
     if constexpr (STREAM)
@@ -151,14 +181,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ u32x2 e4m3_of_bf16(u32x4 d, float inv) {
+__device__ __forceinline__ u32x2 e4m3_of_act(u32x4 d, float inv, bool fp16) {
     float v[8];
-    unpack_bf16(d, v);
+    unpack_act(d, v, fp16);
     return pack_e4m3(v, inv);
 }
 
-template <int BLOCK, int RPW, bool STREAM, bool LF, bool QF8, bool KVF8>
+template <int BLOCK, int RPW, bool STREAM, bool LF, bool VAR, bool QF8, bool KVF8>
 __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) {
+    const bool fp16 = VAR && a.fp16;
     constexpr int kAux = STREAM ? MLA_DQ_STREAM_AUX : 0;
     constexpr uint32_t kWaves = BLOCK / kWave;
     constexpr uint32_t kQRowBytes = QF8 ? 576u : 1152u;
@@ -221,12 +252,12 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
         if constexpr (QF8 == KVF8) {
             const __amdgpu_buffer_rsrc_t dst = is_q ? qdst : cdst;
             if constexpr (QF8)
-                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_bf16(d[k], is_q ? q_inv : kv_inv), dst,
+                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_act(d[k], is_q ? q_inv : kv_inv, fp16), dst,
                                                       lane * 8u, 0, kAux);
             else
                 __builtin_amdgcn_raw_buffer_store_b128(d[k], dst, lane * 16u, 0, kAux);
         } else {
-            const u32x2 f8 = e4m3_of_bf16(d[k], QF8 ? q_inv : kv_inv);
+            const u32x2 f8 = e4m3_of_act(d[k], QF8 ? q_inv : kv_inv, fp16);
             if constexpr (QF8) {
                 __builtin_amdgcn_raw_buffer_store_b64(f8, qdst, lane * 8u, 0, kAux);
                 __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst, lane * 16u, 0, kAux);
@@ -239,8 +270,13 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
 }
 
 // ---- positional tails: 8 rows' tails per wavefront step --------------------
-template <int BLOCK, int STEPS, bool STREAM, bool LF, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int STEPS, bool STREAM, bool LF, bool VAR, bool ROPE, bool QF8, bool KVF8>
 __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
+    // Variant modes are read only by the instances built for them; the
+    // page's configuration (bf16, NeoX pairs, fp32 table) checks nothing.
+    const bool fp16 = VAR && a.fp16;
+    const bool gptj = VAR && a.gptj;
+    const bool table_bf16 = VAR && a.table_bf16;
     constexpr uint32_t kRowsPerStep = BLOCK / 8;
     const uint32_t H = a.num_heads;
     const uint32_t j = threadIdx.x % 8u;           // tail chunk 0..7
@@ -280,17 +316,56 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         pos[k] = 0;
         if constexpr (ROPE) pos[k] = a.positions[t];
     }
-    f32x4 cs[ROPE ? STEPS : 1][4];
+    // Table values for this lane, widened to one per element: cos in c, sin
+    // in s.  NeoX: elements 8j..8j+7 of a half use angles 8(j&3)..+7.
+    // Interleaved: elements 8j..8j+7 are pairs 4j..4j+3.
+    float c[ROPE ? STEPS : 1][8], s[ROPE ? STEPS : 1][8];
     if constexpr (ROPE) {
 #pragma unroll
         for (int k = 0; k < STEPS; ++k) {
             int64_t p = pos[k];
             p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
-            const float* trow = a.rope_cos_sin + p * 64 + (j & 3u) * 8u;
-            cs[k][0] = *reinterpret_cast<const f32x4*>(trow);        // cos
-            cs[k][1] = *reinterpret_cast<const f32x4*>(trow + 4);
-            cs[k][2] = *reinterpret_cast<const f32x4*>(trow + 32);   // sin
-            cs[k][3] = *reinterpret_cast<const f32x4*>(trow + 36);
+            const uint32_t col = gptj ? 4u * j : 8u * (j & 3u);
+            if (table_bf16) {
+                const uint16_t* trow = reinterpret_cast<const uint16_t*>(a.rope_cos_sin) + p * 64 + col;
+                if (gptj) {
+                    const u32x2 cv = *reinterpret_cast<const u32x2*>(trow);
+                    const u32x2 sv = *reinterpret_cast<const u32x2*>(trow + 32);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        c[k][4 * q] = c[k][4 * q + 1] = bf16_lo(cv[q]);
+                        c[k][4 * q + 2] = c[k][4 * q + 3] = bf16_hi(cv[q]);
+                        s[k][4 * q] = s[k][4 * q + 1] = bf16_lo(sv[q]);
+                        s[k][4 * q + 2] = s[k][4 * q + 3] = bf16_hi(sv[q]);
+                    }
+                } else {
+                    unpack_bf16(*reinterpret_cast<const u32x4*>(trow), c[k]);
+                    unpack_bf16(*reinterpret_cast<const u32x4*>(trow + 32), s[k]);
+                }
+            } else {
+                const float* trow = a.rope_cos_sin + p * 64 + col;
+                if (gptj) {
+                    const f32x4 cv = *reinterpret_cast<const f32x4*>(trow);
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(trow + 32);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        c[k][2 * q] = c[k][2 * q + 1] = cv[q];
+                        s[k][2 * q] = s[k][2 * q + 1] = sv[q];
+                    }
+                } else {
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(trow);
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(trow + 4);
+                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(trow + 32);
+                    const f32x4 s1 = *reinterpret_cast<const f32x4*>(trow + 36);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        c[k][q] = c0[q];
+                        c[k][4 + q] = c1[q];
+                        s[k][q] = s0[q];
+                        s[k][4 + q] = s1[q];
+                    }
+                }
+            }
         }
     }
     if constexpr (LF) {
@@ -305,25 +380,29 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         const bool is_q = head[k] < H;
         float y[8];
         if constexpr (ROPE) {
-            // Every lane takes part in the exchange.  First half: y = x_i c -
-            // x_{i+32} s with own = x_i; second half: y = x_{i+32} c + x_i s
-            // with own = x_{i+32}.
-            const u32x4 partner = swap_lane4(d[k]);
+            // Each element e pairs with one partner: NeoX takes it from lane
+            // (lane ^ 4) (chunk j ^ 4, every lane takes part in the exchange),
+            // interleaved takes element e ^ 1 of the lane's own chunk.  The
+            // first element of a pair gets own*c - partner*s, the second
+            // own*c + partner*s.
+            const u32x4 other = swap_lane4(d[k]);
             float own[8], par[8];
-            unpack_bf16(d[k], own);
-            unpack_bf16(partner, par);
-            const float c[8] = {cs[k][0].x, cs[k][0].y, cs[k][0].z, cs[k][0].w,
-                                cs[k][1].x, cs[k][1].y, cs[k][1].z, cs[k][1].w};
-            const float s[8] = {cs[k][2].x, cs[k][2].y, cs[k][2].z, cs[k][2].w,
-                                cs[k][3].x, cs[k][3].y, cs[k][3].z, cs[k][3].w};
+            unpack_act(d[k], own, fp16);
+            if (gptj) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) par[e] = own[e ^ 1];
+            } else {
+                unpack_act(other, par, fp16);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float oc = own[e] * c[e];
-                const float ps = par[e] * s[e];
-                y[e] = first_half ? oc - ps : oc + ps;
+                const bool first = gptj ? (e & 1) == 0 : first_half;
+                const float oc = own[e] * c[k][e];
+                const float ps = par[e] * s[k][e];
+                y[e] = first ? oc - ps : oc + ps;
             }
         } else {
-            unpack_bf16(d[k], y);
+            unpack_act(d[k], y, fp16);
         }
         const bool slot_ok = slot[k] >= 0 && slot[k] < a.num_slots;
         if (!live[k] || (!is_q && !slot_ok)) continue;
@@ -334,13 +413,13 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         if (fp8)
             store_out<STREAM>(dst, pack_e4m3(y, is_q ? q_inv : kv_inv));
         else if (ROPE)
-            store_out<STREAM>(dst, pack_bf16(y));
+            store_out<STREAM>(dst, fp16 ? pack_f16(y) : pack_bf16(y));
         else
             store_out<STREAM>(dst, d[k]);
     }
 }
 
-template <int BLOCK, int RPW, int TAIL_STEPS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int RPW, int TAIL_STEPS, bool STREAM, bool VAR, bool ROPE, bool QF8, bool KVF8>
 __global__ void __launch_bounds__(BLOCK)
 mla_dq_epilogue_kernel(const KernelArgs a) {
     // The latency mapping issues the activation loads before anything the
@@ -351,14 +430,14 @@ mla_dq_epilogue_kernel(const KernelArgs a) {
     const uint32_t b = blockIdx.x;
 #if MLA_DQ_BLOCK_ORDER == 0
     if (b < a.tail_blocks) {
-        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, b);
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, b);
         return;
     }
     uint32_t tile = b - a.tail_blocks;
 #elif MLA_DQ_BLOCK_ORDER == 1
     const uint32_t latent_blocks = gridDim.x - a.tail_blocks;
     if (b >= latent_blocks) {
-        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, b - latent_blocks);
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, b - latent_blocks);
         return;
     }
     uint32_t tile = b;
@@ -371,7 +450,7 @@ mla_dq_epilogue_kernel(const KernelArgs a) {
     if (b < grouped) {
         const uint32_t grp = b / (run + 1), pos = b % (run + 1);
         if (pos == 0) {
-            tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, ROPE, QF8, KVF8>(a, grp);
+            tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, grp);
             return;
         }
         tile = grp * run + pos - 1;
@@ -383,47 +462,53 @@ mla_dq_epilogue_kernel(const KernelArgs a) {
     // tail_blocks is a multiple of 8, so tile and b share their XCD.
     tile = xcd_contiguous_tile(tile, gridDim.x - a.tail_blocks);
 #endif
-    latent_rows<BLOCK, RPW, STREAM, LATENT_LF, QF8, KVF8>(a, tile);
+    latent_rows<BLOCK, RPW, STREAM, LATENT_LF, VAR, QF8, KVF8>(a, tile);
 }
 
-template <int BLOCK, int RPW, int TS, bool STREAM, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int RPW, int TS, bool STREAM, bool VAR, bool ROPE, bool QF8, bool KVF8>
 static hipError_t launch_one(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((mla_dq_epilogue_kernel<BLOCK, RPW, TS, STREAM, ROPE, QF8, KVF8>),
+    hipLaunchKernelGGL((mla_dq_epilogue_kernel<BLOCK, RPW, TS, STREAM, VAR, ROPE, QF8, KVF8>),
                        dim3(grid), dim3(BLOCK), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int BLOCK, int RPW, int TS, bool STREAM>
+template <int BLOCK, int RPW, int TS, bool STREAM, bool VAR>
 static hipError_t launch_flags(const KernelArgs& a, uint32_t grid, uint32_t flags,
                                hipStream_t stream) {
     const bool r = flags & MLA_DQ_ROPE, q = flags & MLA_DQ_Q_FP8, kv = flags & MLA_DQ_KV_FP8;
     if (r) {
-        if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, true, true, true>(a, grid, stream)
-                         : launch_one<BLOCK, RPW, TS, STREAM, true, true, false>(a, grid, stream);
-        return kv ? launch_one<BLOCK, RPW, TS, STREAM, true, false, true>(a, grid, stream)
-                  : launch_one<BLOCK, RPW, TS, STREAM, true, false, false>(a, grid, stream);
+        if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, VAR, true, true, true>(a, grid, stream)
+                         : launch_one<BLOCK, RPW, TS, STREAM, VAR, true, true, false>(a, grid, stream);
+        return kv ? launch_one<BLOCK, RPW, TS, STREAM, VAR, true, false, true>(a, grid, stream)
+                  : launch_one<BLOCK, RPW, TS, STREAM, VAR, true, false, false>(a, grid, stream);
     }
-    if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, false, true, true>(a, grid, stream)
-                     : launch_one<BLOCK, RPW, TS, STREAM, false, true, false>(a, grid, stream);
-    return kv ? launch_one<BLOCK, RPW, TS, STREAM, false, false, true>(a, grid, stream)
-              : launch_one<BLOCK, RPW, TS, STREAM, false, false, false>(a, grid, stream);
+    if (q) return kv ? launch_one<BLOCK, RPW, TS, STREAM, VAR, false, true, true>(a, grid, stream)
+                     : launch_one<BLOCK, RPW, TS, STREAM, VAR, false, true, false>(a, grid, stream);
+    return kv ? launch_one<BLOCK, RPW, TS, STREAM, VAR, false, false, true>(a, grid, stream)
+              : launch_one<BLOCK, RPW, TS, STREAM, VAR, false, false, false>(a, grid, stream);
 }
 
-template <bool STREAM>
+template <bool STREAM, bool VAR>
 static hipError_t launch_mapping(const KernelArgs& a, const mla_dq_launch_plan& plan,
                                  uint32_t flags, hipStream_t stream) {
     const uint32_t grid = (uint32_t)plan.grid_blocks;
     if (plan.mapping == 0)
         return launch_flags<kSmallMapping.block, kSmallMapping.rows_per_wave,
-                            kSmallMapping.tail_steps, STREAM>(a, grid, flags, stream);
+                            kSmallMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
     return launch_flags<kLargeMapping.block, kLargeMapping.rows_per_wave,
-                        kLargeMapping.tail_steps, STREAM>(a, grid, flags, stream);
+                        kLargeMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
 }
 
 hipError_t launch(const KernelArgs& a, const mla_dq_launch_plan& plan, uint32_t flags,
                   hipStream_t stream) {
-    return plan.streaming ? launch_mapping<true>(a, plan, flags, stream)
-                          : launch_mapping<false>(a, plan, flags, stream);
+    // Instances for the variant modes (fp16, interleaved pairs, bf16 table)
+    // are separate, so that the page's configuration pays for none of them.
+    const bool var = flags & (MLA_DQ_FP16 | MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16);
+    if (plan.streaming)
+        return var ? launch_mapping<true, true>(a, plan, flags, stream)
+                   : launch_mapping<true, false>(a, plan, flags, stream);
+    return var ? launch_mapping<false, true>(a, plan, flags, stream)
+               : launch_mapping<false, false>(a, plan, flags, stream);
 }
 
 }  // namespace mla_dq

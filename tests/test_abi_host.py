@@ -44,6 +44,8 @@ def test_flag_and_code_values_match_header():
     assert val("MLA_DQ_KV_FP8") == M.KV_FP8
     assert val("MLA_DQ_FORCE_SMALL_T") == M.FORCE_SMALL_T
     assert val("MLA_DQ_FORCE_LARGE_T") == M.FORCE_LARGE_T
+    assert val("MLA_DQ_FP16") == M.FP16 and val("MLA_DQ_ROPE_GPTJ") == M.ROPE_GPTJ
+    assert val("MLA_DQ_TABLE_BF16") == M.TABLE_BF16
     assert val("MLA_DQ_FORCE_STREAM") == M.FORCE_STREAM
     assert val("MLA_DQ_FORCE_CACHED") == M.FORCE_CACHED
     for name, v in (("MLA_DQ_ERR_NULL", B.ERR_NULL), ("MLA_DQ_ERR_ALIGN", B.ERR_ALIGN),
@@ -92,8 +94,9 @@ def test_null_dims():
     assert _call(_ptrs(), 0, None) == B.ERR_NULL
 
 
-@pytest.mark.parametrize("flags", [1 << 3, 1 << 12, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
-                                   M.FORCE_STREAM | M.FORCE_CACHED])
+@pytest.mark.parametrize("flags", [1 << 6, 1 << 12, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+                                   M.FORCE_STREAM | M.FORCE_CACHED, M.ROPE_GPTJ, M.TABLE_BF16,
+                                   M.ROPE_GPTJ | M.TABLE_BF16 | M.FP16])
 def test_bad_flags(flags):
     assert _call(_ptrs(), flags, _dims()) == B.ERR_FLAGS
 
@@ -184,7 +187,8 @@ def test_cache_overlapping_input_is_rejected():
 
 def _bytes(T, H, flags):
     rope = bool(flags & M.ROPE)
-    read = T * (H * 1152 + 1152 + 8 + (264 if rope else 0))
+    table = 128 if flags & M.TABLE_BF16 else 256
+    read = T * (H * 1152 + 1152 + 8 + (8 + table if rope else 0))
     write = T * 576 * (H * (1 if flags & M.Q_FP8 else 2) + (1 if flags & M.KV_FP8 else 2))
     return read + write
 
@@ -192,7 +196,8 @@ def _bytes(T, H, flags):
 def test_plan_threshold_and_coverage():
     for T in (1, 2, 63, 64, 65, 135, 136, 256, 8192):
         for H in (1, 16, 128):
-            for flags in (0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8 | M.KV_FP8):
+            for flags in (0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8 | M.KV_FP8,
+                          M.ROPE | M.ROPE_GPTJ | M.TABLE_BF16 | M.FP16):
                 pl = M.plan(_dims(T=T, H=H), flags)
                 rows = T * (H + 1)
                 assert pl.total_rows == rows

@@ -32,7 +32,14 @@ def announce(case: str) -> None:
 
 
 def flags_of(w: I.Workload) -> int:
-    return (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+    f = (M.ROPE if w.rope else 0) | (M.Q_FP8 if w.q_fp8 else 0) | (M.KV_FP8 if w.kv_fp8 else 0)
+    if w.dtype == "fp16":
+        f |= M.FP16
+    if w.rope and w.rope_style == "gptj":
+        f |= M.ROPE_GPTJ
+    if w.rope and w.table_dtype == "bf16":
+        f |= M.TABLE_BF16
+    return f
 
 
 def run_gpu(w: I.Workload, inp: dict, extra_flags: int = 0, cache_init: np.ndarray | None = None,
@@ -40,8 +47,8 @@ def run_gpu(w: I.Workload, inp: dict, extra_flags: int = 0, cache_init: np.ndarr
     """Run the kernel; returns (q bits, cache bits) and checks the guards."""
     announce(f"{case} {w.describe()} flags+{extra_flags:#x}")
     T, H = w.tokens, w.heads
-    qdt = torch.float8_e4m3fn if w.q_fp8 else torch.bfloat16
-    kvdt = torch.float8_e4m3fn if w.kv_fp8 else torch.bfloat16
+    qdt = torch.float8_e4m3fn if w.q_fp8 else w.torch_dtype
+    kvdt = torch.float8_e4m3fn if w.kv_fp8 else w.torch_dtype
     n_q = T * H * I.ROW
     pad = 4096
     qbig = torch.empty(n_q + 2 * pad, dtype=qdt, device=DEV)
@@ -50,7 +57,7 @@ def run_gpu(w: I.Workload, inp: dict, extra_flags: int = 0, cache_init: np.ndarr
     if cache_init is None:
         cache_cpu = inp["cache"]
     elif cache_init.dtype == np.uint16:
-        cache_cpu = torch.from_numpy(cache_init.view(np.int16).copy()).view(torch.bfloat16)
+        cache_cpu = torch.from_numpy(cache_init.view(np.int16).copy()).view(kvdt)
     else:
         cache_cpu = torch.from_numpy(cache_init.copy()).view(kvdt)
     NB, BS = cache_cpu.shape[0], cache_cpu.shape[1]
@@ -80,15 +87,17 @@ def run_gpu(w: I.Workload, inp: dict, extra_flags: int = 0, cache_init: np.ndarr
     return bits(q_out.cpu()), bits(cache.cpu())
 
 
-def _nan_mask(x: np.ndarray) -> np.ndarray:
+def _nan_mask(x: np.ndarray, fp16: bool = False) -> np.ndarray:
     if x.dtype == np.uint8:
         return (x & 0x7F) == 0x7F
+    if fp16:
+        return ((x & 0x7C00) == 0x7C00) & ((x & 0x3FF) != 0)
     return ((x & 0x7F80) == 0x7F80) & ((x & 0x7F) != 0)
 
 
-def assert_same(got: np.ndarray, want: np.ndarray, what: str):
+def assert_same(got: np.ndarray, want: np.ndarray, what: str, fp16: bool = False):
     assert got.shape == want.shape and got.dtype == want.dtype, what
-    ng, nw = _nan_mask(got), _nan_mask(want)
+    ng, nw = _nan_mask(got, fp16), _nan_mask(want, fp16)
     bad = np.nonzero((ng != nw) | (~nw & (got != want)))
     if bad[0].size:
         idx = tuple(b[0] for b in bad)
@@ -96,19 +105,22 @@ def assert_same(got: np.ndarray, want: np.ndarray, what: str):
                              f"got {got[idx]:#x} want {want[idx]:#x}")
 
 
-def _bf16_value(x: np.ndarray) -> np.ndarray:
+def _act_value(x: np.ndarray, fp16: bool) -> np.ndarray:
+    if fp16:
+        return x.view(np.float16).astype(np.float32)
     return (x.astype(np.uint32) << 16).view(np.float32)
 
 
 def check_against_oracle(w: I.Workload, inp: dict, q, cache, cache_init=None):
     want_q, want_cache = oracle_run(w, inp, cache_init=cache_init)
+    fp16 = w.dtype == "fp16"
     if w.rope and not w.q_fp8:
-        # the stated bar on rotated bf16 outputs first
-        g, r = _bf16_value(q[..., 512:]), _bf16_value(want_q[..., 512:])
+        # the stated bar on rotated unquantised outputs first
+        g, r = _act_value(q[..., 512:], fp16), _act_value(want_q[..., 512:], fp16)
         fin = np.isfinite(r)
         assert np.all(np.abs(g[fin] - r[fin]) <= 1e-2), "rotated q beyond 1e-2"
-    assert_same(q, want_q, "q_out")
-    assert_same(cache, want_cache, "cache")
+    assert_same(q, want_q, "q_out", fp16 and not w.q_fp8)
+    assert_same(cache, want_cache, "cache", fp16 and not w.kv_fp8)
 
 
 @pytest.mark.parametrize("name", I.WORKLOAD_ORDER)
@@ -330,6 +342,82 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert_same(bits(q.cpu()), want_q, "q_out")
         assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
+
+
+VARIANTS = [("fp16", "neox", "f32"), ("bf16", "gptj", "f32"), ("bf16", "neox", "bf16"),
+            ("fp16", "gptj", "bf16")]
+
+
+@pytest.mark.parametrize("dtype,style,table", VARIANTS, ids=["-".join(v) for v in VARIANTS])
+@pytest.mark.parametrize("qf,kf", [(False, False), (True, False), (False, True), (True, True)],
+                         ids=["q-kv", "Q8-kv", "q-KV8", "Q8-KV8"])
+@pytest.mark.parametrize("T,H", [(37, 5), (300, 16)])
+def test_variants_match_oracle(dtype, style, table, qf, kf, T, H):
+    """fp16 activations, interleaved rotation and a bf16 table, in every FP8
+    mode, on both mappings (forced) and against the oracle."""
+    w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=True, q_fp8=qf, kv_fp8=kf,
+                 q_scale=0.04, kv_scale=0.3, dtype=dtype, rope_style=style, table_dtype=table)
+    inp = I.make_inputs(w, seed=T + H)
+    qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"variant {dtype}/{style}/{table} small")
+    ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T | M.FORCE_STREAM, case=f"variant {dtype}/{style}/{table} large")
+    assert np.array_equal(qs, ql) and np.array_equal(cs, cl)
+    check_against_oracle(w, inp, qs, cs)
+
+
+@pytest.mark.parametrize("T,H", [(1, 16), (65, 16)])
+def test_fp16_copy_path(T, H):
+    w = I.custom(T, H, dtype="fp16")
+    inp = I.make_inputs(w)
+    q, cache = run_gpu(w, inp, case=f"fp16 copy T={T}")
+    check_against_oracle(w, inp, q, cache)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.05, 3.7])
+def test_e4m3_exhaustive_all_fp16_inputs(scale):
+    T, H = 8, 16
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.float16)
+    for rope, style in ((False, "neox"), (True, "neox"), (True, "gptj")):
+        w = I.custom(T, H, num_blocks=1, rope=rope, q_fp8=True, kv_fp8=True, q_scale=scale,
+                     kv_scale=scale, dtype="fp16", rope_style=style)
+        inp = I.make_inputs(w, seed=19)
+        inp["ql_nope"] = allbits.view(T, H, 512).clone()
+        perm = torch.randperm(65536, generator=torch.Generator().manual_seed(4))
+        inp["q_pe"] = allbits[perm[:T * H * 64]].view(T, H, 64).clone()
+        inp["kv_c"] = allbits[perm[:T * 512]].view(T, 512).clone()
+        inp["k_pe"] = allbits[perm[-T * 64:]].view(T, 64).clone()
+        q, cache = run_gpu(w, inp, case=f"fp16 e4m3 exhaustive scale={scale} rope={rope} {style}")
+        check_against_oracle(w, inp, q, cache)
+
+
+@pytest.mark.parametrize("dtype,style", [("bf16", "gptj"), ("fp16", "neox"), ("fp16", "gptj")])
+def test_rotation_on_all_tails_variants(dtype, style):
+    """Every bit pattern of the activation type as a positional element
+    (unquantised output): rounding, signed zeros, infinities, NaN."""
+    T, H = 64, 16
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(tdt)
+    w = I.custom(T, H, num_blocks=1, rope=True, dtype=dtype, rope_style=style)
+    inp = I.make_inputs(w, seed=23)
+    inp["q_pe"] = allbits.view(T, H, 64).clone()
+    q, cache = run_gpu(w, inp, case=f"rope all tails {dtype} {style}")
+    want_q, want_cache = oracle_run(w, inp)
+    assert_same(q, want_q, "q_out", dtype == "fp16")
+    assert_same(cache, want_cache, "cache", dtype == "fp16")
+
+
+def test_page_call_with_variants():
+    announce("page call fp16 + gptj + bf16 table")
+    w = I.custom(33, 16, num_blocks=1, rope=True, q_fp8=True, dtype="fp16", rope_style="gptj",
+                 table_dtype="bf16")
+    inp = I.make_inputs(w, seed=31)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q = M.fused_mla_decode_q_concat_kv_cache_insert(
+        dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"], dev["cache"], dev["slot_mapping"],
+        dev["positions"], dev["rope_cos_sin"], dev["q_scale"], None, q_fp8=True, rope_style="gptj")
+    torch.cuda.synchronize()
+    want_q, want_cache = oracle_run(w, inp)
+    assert_same(bits(q.cpu()), want_q, "q_out")
+    assert_same(bits(dev["cache"].cpu()), want_cache, "cache", True)
 
 
 def test_binding_rejects_wrong_dtypes():
