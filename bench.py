@@ -167,6 +167,92 @@ def time_host(fn, calls: int = 2000) -> float:
     return (t1 - t0) * 1e6 / calls
 
 
+class DecodeSlice:
+    """One GPU's share (H heads) of the MLA q path around the epilogue, with
+    random weights: the q_b projection GEMM [T,1536] x [1536, H*192] and the
+    per-head W_UK product [H,T,128] x [H,128,512] produce ql_nope and q_pe;
+    kv_c and k_pe are the two parts of one [T,576] kv_a projection output.
+    The epilogue reads ql_nope, q_pe, kv_c and k_pe as strided views of those
+    outputs (no copies), or, for comparison, from contiguous copies."""
+
+    def __init__(self, T: int, H: int, dev: str, seed: int = 3):
+        g = torch.Generator(device="cpu").manual_seed(seed)
+
+        def rnd(*shape, scale=1.0):
+            return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16).to(dev)
+        self.T, self.H = T, H
+        self.x = rnd(T, 1536)
+        self.w_qb = rnd(1536, H * 192, scale=1536 ** -0.5)
+        self.w_uk = rnd(H, 128, 512, scale=128 ** -0.5)
+        self.kv_a = rnd(T, 576)
+        w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
+        host = I.make_inputs(w)
+        self.cache = host["cache"].to(dev)
+        self.slots = host["slot_mapping"].to(dev)
+        self.positions = host["positions"].to(dev)
+        self.table = host["rope_cos_sin"].to(dev)
+        self.q_scale = host["q_scale"].to(dev)
+        self.kv_scale = host["kv_scale"].to(dev)
+        self.q_out = torch.empty(T, H, 576, dtype=torch.float8_e4m3fn, device=dev)
+        self.flags = M.ROPE | M.Q_FP8 | M.KV_FP8
+
+    def producers(self):
+        q = (self.x @ self.w_qb).view(self.T, self.H, 192)
+        ql = torch.bmm(q[..., :128].transpose(0, 1).contiguous(), self.w_uk)   # [H, T, 512]
+        return ql.transpose(0, 1), q[..., 128:], self.kv_a[:, :512], self.kv_a[:, 512:]
+
+    def step(self, epilogue: bool = True, copies: bool = False):
+        ql_nope, q_pe, kv_c, k_pe = self.producers()
+        if not epilogue:
+            return
+        if copies:
+            ql_nope, q_pe = ql_nope.contiguous(), q_pe.contiguous()
+            kv_c, k_pe = kv_c.contiguous(), k_pe.contiguous()
+        M.mla_decode_q_concat_kv_insert(self.q_out, ql_nope, q_pe, kv_c, k_pe, self.cache,
+                                        self.slots, self.positions, self.table, self.q_scale,
+                                        self.kv_scale, self.flags)
+
+
+def time_graph_fn(fn, calls: int = 20, replays: int = 20) -> float:
+    """Device µs per call of fn when `calls` calls are captured in one graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
+def decode_slice_timings(dev: str) -> dict:
+    """Graph-replayed µs per decode-step slice: producers alone, producers +
+    epilogue on strided views, producers + copies + epilogue."""
+    out = {}
+    for T in (1, 64):
+        ds = DecodeSlice(T, 16, dev)
+        base = time_graph_fn(lambda: ds.step(epilogue=False))
+        strided = time_graph_fn(lambda: ds.step())
+        copies = time_graph_fn(lambda: ds.step(copies=True))
+        out[f"t{T}_h16"] = {"producers_us": round(base, 3), "with_epilogue_us": round(strided, 3),
+                            "with_copies_and_epilogue_us": round(copies, 3),
+                            "epilogue_increment_us": round(strided - base, 3),
+                            "copies_avoided_us": round(copies - strided, 3)}
+        log(f"decode slice T={T}: {out[f't{T}_h16']}")
+    return out
+
+
 def sources_digest() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -240,6 +326,7 @@ def main() -> int:
                     help="independent input/output sets rotated between calls (defeats the MALL)")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-decode-slice", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -333,6 +420,8 @@ def main() -> int:
             del vsets
             torch.cuda.empty_cache()
 
+    decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
+
     traffic = traffic_entry(nbytes)
     out = {
         "metric": METRIC,
@@ -358,6 +447,7 @@ def main() -> int:
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "latency_us": latency,
         "variants_at_headline_shape": variants,
+        "decode_step_slice_graph": decode_slice,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,

@@ -420,6 +420,40 @@ def test_page_call_with_variants():
     assert_same(bits(dev["cache"].cpu()), want_cache, "cache", True)
 
 
+def test_decode_slice_views_in_a_graph():
+    """The epilogue reads its inputs as strided views of upstream GEMM outputs
+    (q_pe inside [T,H,192], ql_nope as the transposed [H,T,512] product,
+    kv_c/k_pe inside one [T,576] row), captured with the producers in a HIP
+    graph; every replay equals the oracle on the materialised inputs."""
+    announce("decode slice in a graph")
+    import bench
+    ds = bench.DecodeSlice(64, 16, DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ds.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ql_nope, q_pe, kv_c, k_pe = ds.producers()
+    assert ql_nope.stride() == (512, 64 * 512, 1) and q_pe.stride() == (16 * 192, 192, 1)
+    w = I.custom(64, 16, num_blocks=1, rope=True, q_fp8=True, kv_fp8=True)
+    inp = I.make_inputs(w)
+    inp.update(ql_nope=ql_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(),
+               kv_c=kv_c.cpu().contiguous(), k_pe=k_pe.cpu().contiguous())
+    want_q, want_cache = oracle_run(w, inp)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.step()
+    for _ in range(3):
+        ds.q_out.view(torch.uint8).fill_(0xFF)
+        ds.cache.view(torch.uint8).fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(bits(ds.q_out.cpu()), want_q, "q_out")
+        assert_same(bits(ds.cache.cpu()), want_cache, "cache")
+
+
 def test_binding_rejects_wrong_dtypes():
     w = I.WORKLOADS["t1_h16_copy"]
     inp = I.make_inputs(w)
