@@ -46,11 +46,6 @@
 #define MLA_DQ_XCD_REMAP 0
 #endif
 
-// Order of the two kinds of workgroups in the grid: 0 = tails first,
-// 1 = latent parts first, 2 = one tail workgroup between runs of latent ones.
-#ifndef MLA_DQ_BLOCK_ORDER
-#define MLA_DQ_BLOCK_ORDER 0
-#endif
 // Load order per mapping and workgroup kind: 1 = activations (and
 // positions) first, slots and scales after them; 0 = slots and scales first.
 #ifndef MLA_DQ_SMALL_LATENT_LF
@@ -64,9 +59,6 @@
 #endif
 #ifndef MLA_DQ_LARGE_TAIL_LF
 #define MLA_DQ_LARGE_TAIL_LF 0
-#endif
-#if MLA_DQ_XCD_REMAP && MLA_DQ_BLOCK_ORDER != 0
-#error "the XCD remap assumes tail workgroups come first"
 #endif
 
 namespace mla_dq {

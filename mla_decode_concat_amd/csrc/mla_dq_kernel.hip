@@ -428,36 +428,11 @@ mla_dq_epilogue_kernel(const KernelArgs a) {
     constexpr bool LATENT_LF = kSmall ? MLA_DQ_SMALL_LATENT_LF : MLA_DQ_LARGE_LATENT_LF;
     constexpr bool TAIL_LF = kSmall ? MLA_DQ_SMALL_TAIL_LF : MLA_DQ_LARGE_TAIL_LF;
     const uint32_t b = blockIdx.x;
-#if MLA_DQ_BLOCK_ORDER == 0
     if (b < a.tail_blocks) {
         tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, b);
         return;
     }
     uint32_t tile = b - a.tail_blocks;
-#elif MLA_DQ_BLOCK_ORDER == 1
-    const uint32_t latent_blocks = gridDim.x - a.tail_blocks;
-    if (b >= latent_blocks) {
-        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, b - latent_blocks);
-        return;
-    }
-    uint32_t tile = b;
-#else
-    // groups of one tail workgroup followed by `run` latent workgroups
-    const uint32_t latent_blocks = gridDim.x - a.tail_blocks;
-    const uint32_t run = a.tail_blocks ? latent_blocks / a.tail_blocks : 0u;
-    const uint32_t grouped = a.tail_blocks * (run + 1);
-    uint32_t tile;
-    if (b < grouped) {
-        const uint32_t grp = b / (run + 1), pos = b % (run + 1);
-        if (pos == 0) {
-            tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, grp);
-            return;
-        }
-        tile = grp * run + pos - 1;
-    } else {
-        tile = a.tail_blocks * run + (b - grouped);
-    }
-#endif
 #if MLA_DQ_XCD_REMAP
     // tail_blocks is a multiple of 8, so tile and b share their XCD.
     tile = xcd_contiguous_tile(tile, gridDim.x - a.tail_blocks);
