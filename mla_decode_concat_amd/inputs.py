@@ -173,3 +173,82 @@ def custom(tokens: int, heads: int, num_blocks: int | None = None, block_size: i
     return Workload(name, tokens, heads, num_blocks, block_size, rope, q_fp8, kv_fp8,
                     slots, positions, q_scale, kv_scale, max_position, dtype, rope_style,
                     table_dtype)
+
+
+# ---- inputs of the downstream decode attention --------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One decode step of MLA attention over the paged latent cache: B
+    sequences with one query token each, H heads, seq_lens cached tokens."""
+    name: str
+    batch: int
+    heads: int
+    seq_lens: tuple            # one length per sequence
+    block_size: int = 64
+    q_fp8: bool = False
+    kv_fp8: bool = False
+    q_scale: float = 0.05
+    kv_scale: float = 0.05
+    sm_scale: float = 192 ** -0.5   # 1/sqrt(128 + 64): the head dims before absorption
+    spare_blocks: int = 3           # pages not used by any sequence
+
+    @property
+    def max_blocks(self) -> int:
+        return max(1, max((L + self.block_size - 1) // self.block_size for L in self.seq_lens))
+
+    @property
+    def num_blocks(self) -> int:
+        used = sum((L + self.block_size - 1) // self.block_size for L in self.seq_lens)
+        return used + self.spare_blocks
+
+    def describe(self) -> str:
+        Ls = self.seq_lens
+        lens = f"L={Ls[0]}" if len(set(Ls)) == 1 else f"L={min(Ls)}..{max(Ls)}"
+        bits = ["q_e4m3" if self.q_fp8 else "q_bf16", "kv_e4m3" if self.kv_fp8 else "kv_bf16"]
+        return f"B={self.batch} H={self.heads} {lens} bs={self.block_size} " + "+".join(bits)
+
+
+ATTN_WORKLOADS = {
+    "attn_b64_l4096_h16_kvfp8": AttnWorkload("attn_b64_l4096_h16_kvfp8", 64, 16, (4096,) * 64,
+                                             q_fp8=False, kv_fp8=True),
+    "attn_b64_l4096_h16_bf16": AttnWorkload("attn_b64_l4096_h16_bf16", 64, 16, (4096,) * 64),
+    "attn_b1_l1024_h16_kvfp8": AttnWorkload("attn_b1_l1024_h16_kvfp8", 1, 16, (1024,),
+                                            q_fp8=False, kv_fp8=True),
+}
+
+
+def make_attn_inputs(w: AttnWorkload, seed: int = DEFAULT_SEED) -> dict:
+    """q [B,H,576] and a paged cache [num_blocks, bs, 576] drawn N(0,1) (bf16,
+    or E4M3 codes of x / scale), a block table that hands each sequence a
+    random set of pages, and the sequence lengths."""
+    g = torch.Generator().manual_seed(seed)
+    B, H = w.batch, w.heads
+
+    def draw(shape, fp8, scale):
+        x = torch.randn(*shape, generator=g, dtype=torch.float32)
+        if fp8:
+            return torch.clamp(x / scale, -448, 448).to(torch.float8_e4m3fn)
+        return x.to(torch.bfloat16)
+
+    q = draw((B, H, ROW), w.q_fp8, w.q_scale)
+    cache = draw((w.num_blocks, w.block_size, ROW), w.kv_fp8, w.kv_scale)
+    perm = torch.randperm(w.num_blocks, generator=g, dtype=torch.int64)
+    block_table = torch.zeros(B, w.max_blocks, dtype=torch.int32)
+    k = 0
+    for b, L in enumerate(w.seq_lens):
+        n = (L + w.block_size - 1) // w.block_size
+        block_table[b, :n] = perm[k:k + n].to(torch.int32)
+        k += n
+    return dict(q=q, cache=cache, block_table=block_table,
+                seq_lens=torch.tensor(w.seq_lens, dtype=torch.int32),
+                q_scale=torch.tensor([w.q_scale], dtype=torch.float32) if w.q_fp8 else None,
+                kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32) if w.kv_fp8 else None)
+
+
+def attn_custom(batch: int, heads: int, seq_lens, block_size: int = 64, q_fp8: bool = False,
+                kv_fp8: bool = False, name: str = "attn_custom", **kw) -> AttnWorkload:
+    if isinstance(seq_lens, int):
+        seq_lens = (seq_lens,) * batch
+    return AttnWorkload(name, batch, heads, tuple(int(x) for x in seq_lens), block_size, q_fp8,
+                        kv_fp8, **kw)

@@ -114,3 +114,58 @@ def test_mutant_is_caught(workdir, name, old, new):
         text = f.read()
     assert text.count(old) == 1, f"mutation anchor for {name} not unique"
     assert _caught(_build(text.replace(old, new), workdir, name)), f"mutant {name} survived the pins"
+
+
+# ---- the attention oracle (Python): planted slips in a copy of its source ---
+
+from oracle import attention as ATT  # noqa: E402
+from tests import test_attention_oracle as AP  # noqa: E402
+
+ATT_SRC = ATT.__file__
+ATT_MUTANTS = [
+    ("page_index_swapped", "pages = np.asarray(block_table[b])[j // bs]",
+     "pages = np.asarray(block_table[b])[j % bs]"),
+    ("no_sm_scale", "s = (qd[b] @ rows.T) * sm_scale", "s = (qd[b] @ rows.T)"),
+    ("value_from_tail", "out[b] = p @ rows[:, :NOPE]", "out[b] = p @ rows[:, ROW - NOPE:]"),
+    ("softmax_over_heads", "p /= p.sum(axis=1, keepdims=True)", "p /= p.sum(axis=0, keepdims=True)"),
+    ("e4m3_bias", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("scale_ignored", "return e4m3_decode(x) * float(scale)", "return e4m3_decode(x)"),
+    ("last_key_dropped", "j = np.arange(L)", "j = np.arange(max(L - 1, 1))"),
+]
+ATT_CHECKS = [
+    AP.test_e4m3_decode_every_code_vs_torch,
+    AP.test_single_key_returns_its_value,
+    AP.test_two_keys_closed_form,
+    AP.test_page_order_invariance,
+    lambda: AP.test_matches_library_sdpa(False, False),
+    lambda: AP.test_matches_library_sdpa(True, True),
+    AP.test_zero_query_averages_values,
+]
+
+
+def _att_caught(text: str) -> bool:
+    import types
+    mod = types.ModuleType("attention_mutant")
+    exec(compile(text, "attention_mutant.py", "exec"), mod.__dict__)
+    saved = (ATT.mla_decode_attention, ATT.e4m3_decode)
+    ATT.mla_decode_attention, ATT.e4m3_decode = mod.mla_decode_attention, mod.e4m3_decode
+    try:
+        for check in ATT_CHECKS:
+            try:
+                check()
+            except (AssertionError, IndexError):   # a wrong index may also fall off the table
+                return True
+        return False
+    finally:
+        ATT.mla_decode_attention, ATT.e4m3_decode = saved
+
+
+def test_attention_unmutated_copy_passes():
+    assert not _att_caught(open(ATT_SRC).read())
+
+
+@pytest.mark.parametrize("name,old,new", ATT_MUTANTS, ids=[m[0] for m in ATT_MUTANTS])
+def test_attention_mutant_is_caught(name, old, new):
+    text = open(ATT_SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    assert _att_caught(text.replace(old, new)), f"mutant {name} survived the pins"
