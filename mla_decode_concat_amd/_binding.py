@@ -284,3 +284,158 @@ def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch
     mla_decode_q_concat_kv_insert(q, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
                                   rope_cos_sin, q_scale, kv_scale, flags)
     return q
+
+
+# ---- MLA decode attention over the paged latent cache (include/mla_attn.h) ----
+
+ATTN_Q_FP8 = 1 << 0
+ATTN_KV_FP8 = 1 << 1
+ERR_WORKSPACE = -7
+
+ATTN_EXPORTED_SYMBOLS = ("mla_decode_attention", "mla_decode_attention_workspace_size",
+                         "mla_decode_attention_plan")
+
+
+class AttnDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "batch", "num_heads", "num_blocks", "block_size", "max_blocks_per_seq", "max_seq_len")]
+
+
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int32), ("keys_per_split", ctypes.c_int32),
+                ("head_tiles", ctypes.c_int32), ("combine", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("target_workgroups", ctypes.c_int64), ("xcd_remap", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32)]
+
+
+def _attn_lib() -> ctypes.CDLL:
+    lib = load()
+    if not getattr(lib, "_attn_configured", False):
+        vp = ctypes.c_void_p
+        lib.mla_decode_attention.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_uint32,
+            ctypes.POINTER(AttnDims), vp]
+        lib.mla_decode_attention.restype = ctypes.c_int
+        lib.mla_decode_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDims),
+                                                            ctypes.c_uint32]
+        lib.mla_decode_attention_workspace_size.restype = ctypes.c_size_t
+        lib.mla_decode_attention_plan.argtypes = [ctypes.POINTER(AttnDims), ctypes.c_uint32,
+                                                  ctypes.POINTER(AttnPlan)]
+        lib.mla_decode_attention_plan.restype = ctypes.c_int
+        lib._attn_configured = True
+    return lib
+
+
+def attn_plan(dims: AttnDims, flags: int) -> AttnPlan:
+    p = AttnPlan()
+    rc = _attn_lib().mla_decode_attention_plan(ctypes.byref(dims), ctypes.c_uint32(flags),
+                                               ctypes.byref(p))
+    if rc != OK:
+        raise MlaDqError(rc, strerror(rc))
+    return p
+
+
+def attn_workspace_size(dims: AttnDims, flags: int) -> int:
+    return int(_attn_lib().mla_decode_attention_workspace_size(ctypes.byref(dims),
+                                                               ctypes.c_uint32(flags)))
+
+
+def _attn_flags(q: torch.Tensor, cache: torch.Tensor) -> int:
+    return (ATTN_Q_FP8 if q.dtype in _FP8 else 0) | (ATTN_KV_FP8 if cache.dtype in _FP8 else 0)
+
+
+def _attn_dims(q, cache, block_table, max_seq_len) -> AttnDims:
+    d = AttnDims()
+    d.batch, d.num_heads = q.shape[0], q.shape[1]
+    d.num_blocks, d.block_size = cache.shape[0], cache.shape[1]
+    d.max_blocks_per_seq = block_table.shape[1]
+    d.max_seq_len = (block_table.shape[1] * cache.shape[1] if max_seq_len is None
+                     else int(max_seq_len))
+    return d
+
+
+def _attn_validate(out, q, cache, block_table, seq_lens, q_scale, kv_scale) -> None:
+    _check(q.dim() == 3 and q.shape[2] == 576 and q.is_contiguous(),
+           "q must be a contiguous [B, H, 576] tensor")
+    B_, H = q.shape[0], q.shape[1]
+    _check(tuple(out.shape) == (B_, H, 512) and out.dtype == torch.bfloat16
+           and out.is_contiguous(), "out must be a contiguous bf16 [B, H, 512] tensor")
+    _check(cache.dim() == 3 and cache.shape[2] == 576 and cache.is_contiguous(),
+           "cache must be a contiguous [num_blocks, block_size, 576] tensor")
+    _check(q.dtype in _FP8 or q.dtype == torch.bfloat16, "q must be bf16 or e4m3")
+    _check(cache.dtype in _FP8 or cache.dtype == torch.bfloat16, "cache must be bf16 or e4m3")
+    _check(block_table.dtype == torch.int32 and block_table.dim() == 2
+           and block_table.shape[0] == B_ and block_table.is_contiguous(),
+           "block_table must be a contiguous int32 [B, max_blocks_per_seq]")
+    _check(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B_,)
+           and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 [B]")
+    if q.dtype in _FP8:
+        _check(q_scale is not None and q_scale.dtype == torch.float32, "e4m3 q needs q_scale")
+    if cache.dtype in _FP8:
+        _check(kv_scale is not None and kv_scale.dtype == torch.float32,
+               "e4m3 cache needs kv_scale")
+    dev = out.device
+    _check(dev.type == "cuda", "tensors must be on a GPU")
+    for t in (q, cache, block_table, seq_lens, q_scale, kv_scale):
+        if t is not None:
+            _check(t.device == dev, "all tensors must be on the same GPU")
+
+
+class PreparedAttention:
+    """Decode attention bound to fixed tensors and a workspace: checked and
+    marshalled once, each call only enqueues the kernels (for loops over
+    static buffers, e.g. under stream capture).  ``max_seq_len`` bounds every
+    seq_lens entry (default: the block table's capacity); the key split is
+    planned from it."""
+
+    def __init__(self, out, q, cache, block_table, seq_lens, sm_scale: float, q_scale=None,
+                 kv_scale=None, max_seq_len: int | None = None,
+                 workspace: torch.Tensor | None = None):
+        _attn_validate(out, q, cache, block_table, seq_lens, q_scale, kv_scale)
+        self._dims = _attn_dims(q, cache, block_table, max_seq_len)
+        self._flags = _attn_flags(q, cache)
+        self.plan = attn_plan(self._dims, self._flags)
+        need = int(self.plan.workspace_bytes)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+        if need > 0:
+            _check(workspace.device == out.device and workspace.is_contiguous()
+                   and workspace.numel() * workspace.element_size() >= need,
+                   f"workspace must be a contiguous buffer of at least {need} bytes")
+        self._tensors = (out, q, cache, block_table, seq_lens, q_scale, kv_scale, workspace)
+        self._args = (_ptr(out), _ptr(q), _ptr(cache), _ptr(block_table), _ptr(seq_lens),
+                      _ptr(q_scale), _ptr(kv_scale))
+        self._sm_scale = float(sm_scale)
+        self._ws = _ptr(workspace) if need > 0 else None
+        self._ws_bytes = workspace.numel() * workspace.element_size() if need > 0 else 0
+        self._index = out.device.index
+
+    def __call__(self, stream=None) -> None:
+        fn = _attn_lib().mla_decode_attention
+        args = (*self._args, ctypes.c_float(self._sm_scale), self._ws,
+                ctypes.c_size_t(self._ws_bytes), ctypes.c_uint32(self._flags),
+                ctypes.byref(self._dims))
+        if self._index == torch.cuda.current_device():
+            rc = fn(*args, _raw_stream(self._index, stream))
+        else:
+            with torch.cuda.device(self._index):
+                rc = fn(*args, _raw_stream(self._index, stream))
+        if rc != OK:
+            raise MlaDqError(rc, strerror(rc))
+
+
+def mla_decode_attention(q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, sm_scale: float,
+                         q_scale: torch.Tensor | None = None,
+                         kv_scale: torch.Tensor | None = None,
+                         max_seq_len: int | None = None,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention of q [B, H, 576] over the paged latent cache; returns
+    bf16 [B, H, 512].  E4M3 q or cache follow from the dtypes (with their
+    fp32 scales)."""
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    PreparedAttention(out, q, cache, block_table, seq_lens, sm_scale, q_scale, kv_scale,
+                      max_seq_len)()
+    return out

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "mla_attn.h"
 #include "mla_dq.h"
 #include "mla_dq_internal.h"
 
@@ -238,6 +239,7 @@ const char* mla_dq_strerror(int code) {
         case MLA_DQ_ERR_FLAGS: return "unknown flag bit or contradictory launch overrides";
         case MLA_DQ_ERR_LAUNCH: return "HIP kernel launch failed";
         case MLA_DQ_ERR_ALIAS: return "q_out overlaps an input or the cache, or the cache overlaps an input";
+        case MLA_ATTN_ERR_WORKSPACE: return "workspace smaller than mla_decode_attention_workspace_size()";
         default: return "unknown mla_dq error code";
     }
 }

@@ -17,10 +17,11 @@ from mla_decode_concat_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_dq.h")
+ATTN_HEADER = os.path.join(ROOT, "include", "mla_attn.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
@@ -32,6 +33,16 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(B.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_library_exports_every_attention_function():
+    names = _declared_functions(ATTN_HEADER)
+    assert set(names) == {"mla_decode_attention", "mla_decode_attention_workspace_size",
+                          "mla_decode_attention_plan"}
+    lib = ctypes.CDLL(B.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.ATTN_EXPORTED_SYMBOLS) == set(names)
 
 
 def test_flag_and_code_values_match_header():
@@ -56,7 +67,7 @@ def test_flag_and_code_values_match_header():
 
 def test_strerror_every_code():
     seen = set()
-    for c in (0, -1, -2, -3, -4, -5, -6):
+    for c in (0, -1, -2, -3, -4, -5, -6, -7):
         s = M.strerror(c)
         assert s and s not in seen
         seen.add(s)

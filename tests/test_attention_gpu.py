@@ -1,0 +1,210 @@
+"""GPU parity of MLA decode attention (include/mla_attn.h): the gfx950
+kernels, called through the C ABI, against the float64 oracle
+(oracle/attention.py) on the same seeded inputs.
+
+Tolerance, from the kernel's arithmetic.  Scores are exact bf16 products
+summed in fp32 (E4M3 operands convert to bf16 exactly), so their error is
+~1e-6 relative and moves each softmax weight by far less than the next term.
+The value product uses the weights rounded to bf16: p_j (1 + d_j) with
+|d_j| <= 2^-9, while the normaliser sums the unrounded fp32 weights.  The
+numerator therefore errs by at most 2^-9 sum_j p_j |v_j| <= 2^-9 l vmax, i.e.
+2^-9 vmax after the division, vmax being the largest |value| in the
+sequence.  The bf16 output adds at most 2^-9 |out|.  The test allows twice
+both: |gpu - ref| <= 2^-8 (vmax + |ref|) elementwise.  The output buffer is
+poisoned with NaN first, so every element must be written.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_decode_concat_amd as M
+from mla_decode_concat_amd import inputs as I
+from oracle import attention as A
+from tests._util import bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def announce(case: str) -> None:
+    sys.__stderr__.write(f"[gpu-case] {case}\n")
+    sys.__stderr__.flush()
+
+
+def _decoded_values(cache: np.ndarray, kv_scale):
+    if cache.dtype == np.uint8:
+        return A.e4m3_decode(cache) * float(kv_scale)
+    return A.bf16_decode(cache)
+
+
+def oracle_out(w: I.AttnWorkload, inp: dict, seq_lens=None, block_table=None):
+    lens = inp["seq_lens"].numpy() if seq_lens is None else np.asarray(seq_lens)
+    table = inp["block_table"].numpy() if block_table is None else np.asarray(block_table)
+    return A.mla_decode_attention(bits(inp["q"]), bits(inp["cache"]), table, lens, w.sm_scale,
+                                  q_scale=w.q_scale if w.q_fp8 else None,
+                                  kv_scale=w.kv_scale if w.kv_fp8 else None)
+
+
+def bound(w: I.AttnWorkload, inp: dict, ref: np.ndarray, seq_lens=None, block_table=None):
+    """2^-8 (vmax_b + |ref|) per element; vmax_b over sequence b's keys."""
+    lens = inp["seq_lens"].numpy() if seq_lens is None else np.asarray(seq_lens)
+    table = inp["block_table"].numpy() if block_table is None else np.asarray(block_table)
+    cache = bits(inp["cache"])
+    bs = cache.shape[1]
+    vmax = np.zeros(ref.shape[0])
+    for b, L in enumerate(lens):
+        L = int(L)
+        if L <= 0:
+            continue
+        j = np.arange(L)
+        rows = cache[table[b][j // bs], j % bs, :A.NOPE]
+        vmax[b] = np.abs(_decoded_values(rows, w.kv_scale)).max()
+    return 2.0 ** -8 * (vmax[:, None, None] + np.abs(ref))
+
+
+def to_device(inp: dict) -> dict:
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run_gpu(w: I.AttnWorkload, inp: dict, case: str, max_seq_len=None, stream=None,
+            seq_lens=None, block_table=None) -> np.ndarray:
+    d = to_device(inp)
+    if seq_lens is not None:
+        d["seq_lens"] = torch.as_tensor(np.asarray(seq_lens), dtype=torch.int32).to(DEV)
+    if block_table is not None:
+        d["block_table"] = torch.as_tensor(np.asarray(block_table), dtype=torch.int32).to(DEV)
+    out = torch.empty(w.batch, w.heads, 512, dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(-1)                       # 0xFFFF: a bf16 NaN
+    prep = M.PreparedAttention(out, d["q"], d["cache"], d["block_table"], d["seq_lens"],
+                               w.sm_scale, d["q_scale"], d["kv_scale"], max_seq_len=max_seq_len)
+    announce(f"{case} {w.describe()} splits={prep.plan.splits} kps={prep.plan.keys_per_split} "
+             f"wgs={prep.plan.workgroups} combine={prep.plan.combine}")
+    prep(stream)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, ref, tol, case):
+    assert np.isfinite(got).all(), f"{case}: unwritten or non-finite outputs"
+    err = np.abs(got - ref)
+    bad = err > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{case}: {bad.sum()} elements outside the bound; first {idx.tolist()}"
+                             f" got {got[bad][:5]} ref {ref[bad][:5]} tol {tol[bad][:5]}")
+    rel = err.max() / max(np.abs(ref).max(), 1e-30)
+    sys.__stderr__.write(f"[gpu-case] {case}: max |err| {err.max():.3g} (max/ref {rel:.3g})\n")
+
+
+def check(w: I.AttnWorkload, case: str, seed: int = I.DEFAULT_SEED, **kw):
+    inp = I.make_attn_inputs(w, seed)
+    got = run_gpu(w, inp, case, **kw)
+    seq_lens = kw.get("seq_lens")
+    block_table = kw.get("block_table")
+    ref_lens = None
+    if seq_lens is not None:
+        cap = kw.get("max_seq_len") or w.max_blocks * w.block_size
+        ref_lens = np.clip(np.asarray(seq_lens), 0, cap)
+    ref_table = None
+    if block_table is not None:
+        ref_table = np.clip(np.asarray(block_table), 0, w.num_blocks - 1)
+    ref = oracle_out(w, inp, ref_lens, ref_table)
+    assert_close(got, ref, bound(w, inp, ref, ref_lens, ref_table), case)
+    return got, ref
+
+
+@pytest.mark.parametrize("name", list(I.ATTN_WORKLOADS))
+def test_workloads(name):
+    check(I.ATTN_WORKLOADS[name], name)
+
+
+RAGGED = (0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 1000, 4096)
+
+
+@pytest.mark.parametrize("q_fp8,kv_fp8", [(False, False), (False, True), (True, False), (True, True)])
+def test_ragged_lengths_all_modes(q_fp8, kv_fp8):
+    w = I.attn_custom(len(RAGGED), 16, RAGGED, q_fp8=q_fp8, kv_fp8=kv_fp8, name="ragged")
+    check(w, f"ragged q_fp8={q_fp8} kv_fp8={kv_fp8}")
+
+
+@pytest.mark.parametrize("heads", [1, 20, 128])
+def test_head_counts(heads):
+    w = I.attn_custom(6, heads, (5, 64, 200, 1, 700, 0), kv_fp8=True, name=f"h{heads}")
+    check(w, f"heads={heads}")
+
+
+@pytest.mark.parametrize("block_size", [1, 5, 16, 128])
+def test_block_sizes(block_size):
+    w = I.attn_custom(4, 16, (3, 130, 517, 64), block_size=block_size, kv_fp8=True,
+                      name=f"bs{block_size}")
+    check(w, f"block_size={block_size}")
+
+
+def test_single_range_writes_output_directly():
+    """Enough (sequence, head tile) pairs that each sequence is one range:
+    the partial kernel normalises and writes bf16 itself (no combine)."""
+    w = I.attn_custom(32, 256, tuple(range(1, 320, 10)), kv_fp8=True, name="direct")
+    inp = I.make_attn_inputs(w)
+    d = to_device(inp)
+    out = torch.empty(w.batch, w.heads, 512, dtype=torch.bfloat16, device=DEV)
+    prep = M.PreparedAttention(out, d["q"], d["cache"], d["block_table"], d["seq_lens"],
+                               w.sm_scale, d["q_scale"], d["kv_scale"])
+    assert prep.plan.splits == 1 and prep.plan.combine == 0
+    check(w, "direct")
+
+
+def test_short_sequences_single_step():
+    w = I.attn_custom(9, 16, (1, 2, 3, 8, 16, 31, 33, 63, 64), name="short")
+    check(w, "short")
+
+
+def test_all_empty_sequences_give_zeros():
+    w = I.attn_custom(3, 16, (0, 0, 0), name="empty")
+    inp = I.make_attn_inputs(w)
+    got = run_gpu(w, inp, "empty", max_seq_len=0)
+    assert (got == 0).all()
+    got = run_gpu(w, inp, "empty-capacity")
+    assert (got == 0).all()
+
+
+def test_lengths_are_clamped():
+    """Negative lengths count as 0; lengths past max_seq_len count as
+    max_seq_len (the header's contract)."""
+    w = I.attn_custom(4, 16, (64, 64, 64, 64), name="clamp")
+    check(w, "clamp", seq_lens=[-5, 70, 10 ** 6, 33])
+
+
+def test_explicit_max_seq_len_changes_the_split():
+    w = I.attn_custom(2, 16, (900, 1000), kv_fp8=True, name="maxlen")
+    got_a, ref = check(w, "maxlen-capacity")
+    got_b, _ = check(w, "maxlen-1000", max_seq_len=1000)
+    assert np.array_equal(np.isfinite(got_a), np.isfinite(got_b))
+
+
+def test_out_of_range_pages_are_clamped():
+    w = I.attn_custom(2, 16, (200, 130), name="pages")
+    inp = I.make_attn_inputs(w)
+    table = inp["block_table"].numpy().copy()
+    table[0, 1] = -7
+    table[1, 2] = w.num_blocks + 100
+    check(w, "pages", block_table=table)
+
+
+def test_side_stream_and_repeat_are_identical():
+    w = I.attn_custom(5, 16, (100, 2000, 3, 4096, 65), kv_fp8=True, name="stream")
+    inp = I.make_attn_inputs(w)
+    a = run_gpu(w, inp, "default-stream")
+    s = torch.cuda.Stream()
+    b = run_gpu(w, inp, "side-stream", stream=s)
+    assert np.array_equal(a, b)
+
+
+def test_seeds():
+    for seed in (1, 2):
+        w = I.attn_custom(3, 16, (333, 64, 1500), q_fp8=True, kv_fp8=True, name=f"seed{seed}")
+        check(w, f"seed={seed}", seed=seed)

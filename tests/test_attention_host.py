@@ -1,0 +1,168 @@
+"""Host-side tests of the decode-attention C ABI (include/mla_attn.h), no
+GPU: flag and code values, the key-split plan, workspace sizing, and the
+argument checks that return before anything is launched."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_decode_concat_amd as M
+from mla_decode_concat_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_attn.h")
+
+
+def test_flag_and_code_values_match_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define MLA_ATTN_Q_FP8\s+\(1u << 0\)", text) and M.ATTN_Q_FP8 == 1
+    assert re.search(r"#define MLA_ATTN_KV_FP8\s+\(1u << 1\)", text) and M.ATTN_KV_FP8 == 2
+    assert int(re.search(r"#define MLA_ATTN_ERR_WORKSPACE\s+(-?\d+)", text).group(1)) == \
+        B.ERR_WORKSPACE
+
+
+def test_plan_struct_matches_header_layout():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct mla_attn_plan \{(.*?)\} mla_attn_plan;", text, re.S).group(1)
+    fields = re.findall(r"(int32_t|int64_t)\s+(\w+);", body)
+    want = [(n, ctypes.c_int32 if t == "int32_t" else ctypes.c_int64) for t, n in fields]
+    assert [(n, t) for n, t in B.AttnPlan._fields_] == want
+    body = re.search(r"typedef struct mla_attn_dims \{(.*?)\} mla_attn_dims;", text, re.S).group(1)
+    assert [n for n, _ in B.AttnDims._fields_] == re.findall(r"int64_t\s+(\w+);", body)
+
+
+def dims(B_=4, H=16, NB=64, BS=64, MB=16, L=None):
+    d = M.AttnDims()
+    d.batch, d.num_heads, d.num_blocks, d.block_size = B_, H, NB, BS
+    d.max_blocks_per_seq = MB
+    d.max_seq_len = MB * BS if L is None else L
+    return d
+
+
+@pytest.mark.parametrize("B_,H,L", [(1, 16, 1), (1, 16, 64), (1, 16, 65), (1, 16, 1024),
+                                    (64, 16, 4096), (64, 128, 4096), (13, 20, 4096),
+                                    (512, 16, 300), (32, 256, 311), (3, 1, 0), (0, 16, 100)])
+def test_plan_covers_every_key_once(B_, H, L):
+    MB = max(1, (L + 63) // 64)
+    for flags in (0, M.ATTN_KV_FP8, M.ATTN_Q_FP8 | M.ATTN_KV_FP8):
+        p = M.attn_plan(dims(B_, H, MB=MB, L=L), flags)
+        assert p.keys_per_split % 64 == 0 and p.keys_per_split >= 64
+        assert p.splits >= 1
+        # the ranges cover [0, L) and none starts past it (no idle split)
+        assert p.splits * p.keys_per_split >= L
+        assert L == 0 and p.splits == 1 or (p.splits - 1) * p.keys_per_split < L
+        assert p.head_tiles == (H + 15) // 16
+        assert p.workgroups == B_ * p.head_tiles * p.splits
+        assert p.combine == (1 if p.splits > 1 else 0)
+        ws = B_ * H * p.splits * (512 + 2) * 4 if p.combine else 0
+        assert p.workspace_bytes == ws
+        assert M.attn_workspace_size(dims(B_, H, MB=MB, L=L), flags) == ws
+        assert p.block_threads == 256 and p.target_workgroups == 512
+        assert p.xcd_remap == (1 if p.head_tiles > 1 and p.workgroups % 8 == 0 else 0)
+
+
+def test_plan_aims_at_the_target_workgroup_count():
+    p = M.attn_plan(dims(64, 16, MB=64, L=4096), M.ATTN_KV_FP8)
+    assert (p.splits, p.keys_per_split, p.workgroups) == (8, 512, 512)
+    p = M.attn_plan(dims(1, 16, MB=16, L=1024), M.ATTN_KV_FP8)
+    assert (p.splits, p.keys_per_split) == (16, 64)
+
+
+def test_target_env_override_in_fresh_process():
+    code = ("import mla_decode_concat_amd as M; d=M.AttnDims(); d.batch=64; d.num_heads=16;"
+            "d.num_blocks=4096; d.block_size=64; d.max_blocks_per_seq=64; d.max_seq_len=4096;"
+            "p=M.attn_plan(d,0); print(p.target_workgroups, p.splits, p.keys_per_split)")
+    env = dict(os.environ, MLA_ATTN_TARGET_WGS="256", PYTHONPATH=ROOT)
+    out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["256", "4", "1024"]
+
+
+BASE = 1 << 36
+GAP = 1 << 32
+
+
+def _ptrs():
+    names = ["out", "q", "cache", "bt", "lens", "qs", "ks", "ws"]
+    return {n: BASE + i * GAP for i, n in enumerate(names)}
+
+
+def _call(p, flags, d, ws_bytes=1 << 30, sm=0.07):
+    lib = B._attn_lib()
+    return lib.mla_decode_attention(p["out"], p["q"], p["cache"], p["bt"], p["lens"], p["qs"],
+                                    p["ks"], ctypes.c_float(sm), p["ws"], ctypes.c_size_t(ws_bytes),
+                                    ctypes.c_uint32(flags),
+                                    ctypes.byref(d) if d is not None else None, None)
+
+
+def test_null_dims_and_plan():
+    assert _call(_ptrs(), 0, None) == B.ERR_NULL
+    lib = B._attn_lib()
+    assert lib.mla_decode_attention_plan(ctypes.byref(dims()), 0, None) == B.ERR_NULL
+    assert lib.mla_decode_attention_workspace_size(None, 0) == 0
+
+
+@pytest.mark.parametrize("flags", [1 << 2, 1 << 8, 1 << 31])
+def test_bad_flags(flags):
+    assert _call(_ptrs(), flags, dims()) == B.ERR_FLAGS
+
+
+@pytest.mark.parametrize("field,value", [("batch", -1), ("num_heads", 0), ("num_blocks", 0),
+                                         ("block_size", 0), ("max_blocks_per_seq", 0),
+                                         ("max_seq_len", -1), ("max_seq_len", 16 * 64 + 1)])
+def test_bad_dims(field, value):
+    d = dims()
+    setattr(d, field, value)
+    assert _call(_ptrs(), 0, d) == B.ERR_DIM
+    assert M.attn_workspace_size(d, 0) == 0
+
+
+def test_zero_batch_is_a_no_op_even_with_null_pointers():
+    p = {k: None for k in _ptrs()}
+    assert _call(p, M.ATTN_Q_FP8 | M.ATTN_KV_FP8, dims(B_=0), ws_bytes=0) == B.OK
+
+
+@pytest.mark.parametrize("name", ["out", "q", "cache", "bt", "lens", "ws"])
+def test_null_required_pointer(name):
+    p = _ptrs()
+    p[name] = None
+    assert _call(p, 0, dims()) == B.ERR_NULL
+
+
+@pytest.mark.parametrize("flags,name", [(M.ATTN_Q_FP8, "qs"), (M.ATTN_KV_FP8, "ks")])
+def test_null_scale_needed_by_flag(flags, name):
+    p = _ptrs()
+    p[name] = None
+    assert _call(p, flags, dims()) == B.ERR_NULL
+
+
+def test_workspace_too_small():
+    d = dims()
+    need = M.attn_workspace_size(d, 0)
+    assert need > 0
+    assert _call(_ptrs(), 0, d, ws_bytes=need - 1) == B.ERR_WORKSPACE
+
+
+def test_workspace_may_be_null_when_none_is_needed():
+    d = dims(B_=600, L=64, MB=1)          # one key range per sequence
+    assert M.attn_workspace_size(d, 0) == 0
+    p = _ptrs()
+    p["ws"] = None
+    p["out"] += 8                         # stop at the alignment check, before any launch
+    assert _call(p, 0, d, ws_bytes=0) == B.ERR_ALIGN
+
+
+@pytest.mark.parametrize("name,off", [("out", 8), ("q", 8), ("cache", 4), ("bt", 2), ("lens", 2),
+                                      ("ws", 4)])
+def test_misaligned_pointer(name, off):
+    p = _ptrs()
+    p[name] += off
+    assert _call(p, 0, dims()) == B.ERR_ALIGN
+
+
+@pytest.mark.parametrize("sm", [float("nan"), float("inf"), -float("inf")])
+def test_bad_softmax_scale(sm):
+    assert _call(_ptrs(), 0, dims(), sm=sm) == B.ERR_DIM
