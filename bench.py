@@ -41,6 +41,9 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
                   for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_dq_epilogue_t8192_h16_traffic.json")
+ATTN_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", "mla_attn.hip"),
+                os.path.join(ROOT, "include", "mla_attn.h")]
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_attn_decode_traffic.json")
 
 
 def log(msg: str) -> None:
@@ -253,6 +256,94 @@ def decode_slice_timings(dev: str) -> dict:
     return out
 
 
+def attn_algorithmic_bytes(w: I.AttnWorkload) -> int:
+    """Bytes decode attention must move per call: every cached row of every
+    sequence read once (576 elements), the queries read and the bf16
+    outputs written once, the block-table entries in use and the lengths."""
+    kv = 1 if w.kv_fp8 else 2
+    q = 1 if w.q_fp8 else 2
+    rows = sum(w.seq_lens)
+    pages = sum((L + w.block_size - 1) // w.block_size for L in w.seq_lens)
+    return rows * 576 * kv + w.batch * w.heads * (576 * q + 512 * 2) + pages * 4 + w.batch * 4
+
+
+def attn_sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_traffic_entry(name: str):
+    """Measured HBM bytes per call (partial + combine kernels) from the
+    committed counter summary, if taken on the current attention sources."""
+    if not os.path.exists(ATTN_TRAFFIC_FILE):
+        return None
+    with open(ATTN_TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("sources_digest") != attn_sources_digest():
+        return None
+    return t.get("workloads", {}).get(name, {}).get("hbm_bytes_per_call")
+
+
+def attn_plan_for(w: I.AttnWorkload):
+    d = M.AttnDims()
+    d.batch, d.num_heads, d.num_blocks, d.block_size = w.batch, w.heads, w.num_blocks, w.block_size
+    d.max_blocks_per_seq, d.max_seq_len = w.max_blocks, max(w.seq_lens)
+    return M.attn_plan(d, (M.ATTN_Q_FP8 if w.q_fp8 else 0) | (M.ATTN_KV_FP8 if w.kv_fp8 else 0))
+
+
+class AttnSet:
+    """One device-resident batch (queries, cache, tables, output) of a
+    decode-attention workload, bound to the library call."""
+
+    def __init__(self, w: I.AttnWorkload, host: dict, dev: str):
+        self.t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in host.items()}
+        t = self.t
+        self.out = torch.empty(w.batch, w.heads, 512, dtype=torch.bfloat16, device=dev)
+        self.prepared = M.PreparedAttention(self.out, t["q"], t["cache"], t["block_table"],
+                                            t["seq_lens"], w.sm_scale, t["q_scale"],
+                                            t["kv_scale"], max_seq_len=max(w.seq_lens))
+
+    def call(self):
+        self.prepared()
+
+
+def attention_timings(dev: str, steps: int) -> dict:
+    """Decode attention over the paged latent cache, per workload: device
+    time per call (events around back-to-back calls on the launch stream),
+    with enough independent cache copies rotated that their total exceeds
+    twice the 256 MB MALL (cold), and with one copy (warm)."""
+    out = {}
+    for name, w in I.ATTN_WORKLOADS.items():
+        host = I.make_attn_inputs(w)
+        cache_bytes = host["cache"].numel() * host["cache"].element_size()
+        n_cold = max(1, min(8, -(-(600 << 20) // cache_bytes)))
+        sets = [AttnSet(w, host, dev) for _ in range(n_cold)]
+        torch.cuda.synchronize()
+        calls = max(20, steps // 4)
+        cold = time_calls(sets, calls, 5)
+        warm = time_calls(sets[:1], calls, 5)
+        nb = attn_algorithmic_bytes(w)
+        pl = sets[0].prepared.plan
+        out[name] = {
+            "config": w.describe(), "bytes": nb, "cold_sets": n_cold,
+            "us_per_call": round(cold["event_ms_per_call"] * 1e3, 3),
+            "gbs": round(nb / cold["event_ms_per_call"] / 1e6, 1),
+            "pct_of_hbm_peak": round(100.0 * nb / cold["event_ms_per_call"] / 1e6 / HBM_PEAK_GBS, 2),
+            "us_per_call_warm": round(warm["event_ms_per_call"] * 1e3, 3),
+            "gbs_warm": round(nb / warm["event_ms_per_call"] / 1e6, 1),
+            "splits": pl.splits, "keys_per_split": pl.keys_per_split,
+            "workgroups": pl.workgroups, "combine": bool(pl.combine),
+            "traffic_bytes": attn_traffic_entry(name),
+        }
+        log(f"attention {name}: {out[name]}")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def sources_digest() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -327,6 +418,9 @@ def main() -> int:
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-decode-slice", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="time only the decode-attention workloads (prints their JSON)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -354,6 +448,9 @@ def main() -> int:
         return 0
 
     M.load()
+    if args.only_attention:
+        print(json.dumps({"decode_attention": attention_timings(dev, args.steps)}), flush=True)
+        return 0
     w = I.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.describe()}")
     host = I.make_inputs(w)
@@ -421,6 +518,7 @@ def main() -> int:
             torch.cuda.empty_cache()
 
     decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
+    attention = {} if args.no_attention else attention_timings(dev, args.steps)
 
     traffic = traffic_entry(nbytes)
     out = {
@@ -448,6 +546,7 @@ def main() -> int:
         "latency_us": latency,
         "variants_at_headline_shape": variants,
         "decode_step_slice_graph": decode_slice,
+        "decode_attention": attention,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,

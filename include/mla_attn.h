@@ -50,8 +50,8 @@ typedef struct mla_attn_dims {
 
 /* Workspace bytes needed for these dims and flags (0 if none is needed, or
  * if dims are invalid).  The split, and so the size, follows the policy read
- * once per process (environment variable MLA_ATTN_TARGET_WGS, else 512
- * workgroups). */
+ * once per process (environment variable MLA_ATTN_TARGET_WGS, else 256
+ * workgroups: one per CU). */
 size_t mla_decode_attention_workspace_size(const mla_attn_dims* dims, uint32_t flags);
 
 /*
@@ -81,7 +81,7 @@ typedef struct mla_attn_plan {
     int32_t combine;            /* 1 = a second pass merges the splits             */
     int64_t workgroups;         /* B * head_tiles * splits                          */
     int64_t workspace_bytes;    /* = mla_decode_attention_workspace_size()         */
-    int64_t target_workgroups;  /* policy: 512, or MLA_ATTN_TARGET_WGS if set      */
+    int64_t target_workgroups;  /* policy: 256, or MLA_ATTN_TARGET_WGS if set      */
     int32_t xcd_remap;          /* 1 = head tiles of one key range share an XCD   */
     int32_t block_threads;      /* 256: four wavefronts per workgroup             */
 } mla_attn_plan;

@@ -1,30 +1,36 @@
 // MLA decode attention over the paged latent cache for gfx950 (MI355X).
 //
 // The definition is in include/mla_attn.h.  Split-KV decoding: a workgroup of
-// four wavefronts handles one (sequence, tile of 16 heads, range of keys) and
-// walks the range 64 keys at a time.
+// four wavefronts handles one (sequence, tile of 16 heads, range of keys).
+// The wavefronts work independently on interleaved tiles of 16 keys (wave w
+// takes tiles w, w+4, w+8, ... of the range), each with its own online
+// softmax and its own accumulator for all 512 value dimensions, and meet
+// once at the end to merge their four partial results through LDS.
 //
-//  * Scores on the matrix cores, transposed: wave w takes keys 16w .. 16w+15
-//    of the step and forms S^T[key][head] = K Q^T with v_mfma_f32_16x16x32_bf16
-//    over 18 steps of 32 of the 576 dimensions.  Lane l (c = l % 16,
-//    g = l / 16) loads 16 bytes of key c at dimensions 32s + 8g (operand A)
-//    and holds head c's query at the same dimensions (operand B, loaded once);
-//    the result leaves lane l with head c's scores for keys 4g .. 4g+3.
-//  * The value part (first 512 elements) of the 64 key rows goes to LDS in
-//    the cache's own row-major layout, and the scores to a small LDS table
-//    indexed by lane: every wave then holds, in the same lane, head c's scores
-//    for keys {16w' + 4g + i}, i.e. all 64 keys between the four lanes
-//    c, c+16, c+32, c+48.  Each wave runs the same online softmax (base 2)
-//    on them, so the running max and sum agree across the wavefronts.
-//  * Values on the matrix cores: wave w owns value dimensions 128w .. 128w+127
-//    and accumulates O^T[dim][head] += V^T P^T with v_mfma_f32_16x16x32_bf16,
-//    32 keys per instruction.  The K index of that product is ordered so that
-//    the B operand (P^T) is the lane's own probabilities as they are, and the
-//    A operand (V^T) comes from two ds_read_b64_tr_b16 of the row-major value
-//    tile: in each 16-lane group, lane i reads four values of row 4g + i/4 at
-//    columns 4(i % 4), and the load hands lane j the four rows of column j.
+// Per pair of 16-key tiles, in one wavefront (lane l: c = l % 16, g = l / 16):
+//  * scores on the matrix cores, transposed: S^T[key][head] = K Q^T with
+//    v_mfma_f32_16x16x32_bf16 over 18 steps of 32 of the 576 dimensions.
+//    Lane l holds 16 bytes of key c at dimensions 32s + 8g (operand A) and
+//    reads head c's query at the same dimensions from the workgroup's query
+//    tile in LDS (operand B); the result leaves lane l with head c's scores
+//    for keys 4g .. 4g+3 of the tile.
+//  * each tile's value part (first 512 elements) goes, as bf16, to a
+//    wavefront-private LDS tile in the cache's row-major layout, and the
+//    tile's registers reload with the next pair's keys.
+//  * online softmax in base 2.  The running max only moves when a pair's
+//    max exceeds it by more than 8 (the weights then stay below 2^8; exact
+//    ratios are unaffected), so the 128 accumulators are rarely rescaled.
+//  * values on the matrix cores: O^T[dim][head] += V^T P^T with
+//    v_mfma_f32_16x16x32_bf16 over 32 tiles of 16 dimensions, 32 keys per
+//    product.  K index 8g + e is key 4g + e of the first tile (e < 4) or
+//    key 4g + e - 4 of the second, so operand B (P^T) is the lane's own
+//    eight weights, and operand A (V^T) is two ds_read_b64_tr_b16 of the
+//    row-major tiles: in each 16-lane group that load hands lane j column j
+//    of the four rows the group's lanes address (lane i: row i / 4,
+//    columns 4(i % 4) .. +3).
 //
-// E4M3 operands convert exactly to bf16 (3 mantissa bits); their scales are
+// E4M3 operands convert exactly to bf16 (3 mantissa bits, two values per
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1); their scales are
 // applied in fp32 to the scores and to the result.  With one range per
 // sequence the workgroup writes the bf16 output itself; otherwise it writes
 // (max, sum, unnormalised output) to the workspace and a second kernel merges
@@ -55,15 +61,26 @@ constexpr int kRow = 576;           // latent row: 512 value + 64 positional ele
 constexpr int kValue = 512;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStepKeys = 16 * kWaves;   // keys per loop step
+constexpr int kTile = 16;                // keys per wavefront tile
+constexpr int kStepKeys = kTile * kWaves;  // keys the workgroup covers per round
 constexpr int kSteps = kRow / 32;        // 18 score products of 32 dimensions
 constexpr int kVSteps = kValue / 32;     // 16 of them cover the value part
-constexpr int kDimsPerWave = kValue / kWaves;
-constexpr int kDimTiles = kDimsPerWave / 16;
-// bf16 elements per LDS row of the value tile: 512 + 16 of padding puts the
+constexpr int kDimTiles = kValue / 16;   // 32 value products of 16 dimensions
+// bf16 elements per LDS row of a value tile: 512 + 16 of padding puts the
 // four rows a 16-lane group reads in one transpose load on disjoint banks.
 constexpr int kVStride = kValue + 16;
-constexpr int kTargetWorkgroupsDefault = 512;  // two resident workgroups per CU
+constexpr int kWaveTile = 2 * kTile * kVStride;       // bf16 elements per wavefront (two tiles)
+// bf16 elements per LDS row of the query tile: 576 + 8 of padding keeps the
+// 16 rows one instruction reads on disjoint banks.
+constexpr int kQStride = kRow + 8;
+constexpr int kMergeDims = 256;                       // value dims merged per pass
+constexpr int kMergeStride = kMergeDims + 4;          // floats per LDS row (one head)
+constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merge buffer too
+static_assert(kWaves * 16 * kMergeStride * 4 <= kLdsBytes, "merge buffer");
+constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
+constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
+// The running max moves only when a tile exceeds it by more than this (log2).
+constexpr float kRebase = 8.0f;
 
 struct Args {
     uint16_t* out;
@@ -81,17 +98,18 @@ struct Args {
     int32_t splits, keys_per_split, head_tiles, xcd_remap;
 };
 
-// Eight E4M3 codes -> eight bf16 (exact: E4M3 values fit bf16).
+// Eight E4M3 codes -> eight bf16, two per v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1 (exact: every E4M3 value is a bf16 value).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
     bf16x8 r;
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);
-        r[4 * w + 0] = (__bf16)lo.x;
-        r[4 * w + 1] = (__bf16)lo.y;
-        r[4 * w + 2] = (__bf16)hi.x;
-        r[4 * w + 3] = (__bf16)hi.y;
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], 1.0f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], 1.0f, true);
+        r[4 * w + 0] = lo[0];
+        r[4 * w + 1] = lo[1];
+        r[4 * w + 2] = hi[0];
+        r[4 * w + 3] = hi[1];
     }
     return r;
 }
@@ -154,206 +172,311 @@ __device__ __forceinline__ void decode_wg(const Args& a, int& b, int& split, int
     b = rest / a.splits;
 }
 
+template <bool FP8>
+__device__ __forceinline__ void load_tile(Chunk<FP8> (&kc)[kSteps], const uint8_t* row, int g) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) kc[s] = load_chunk<FP8>(row, 32 * s + 8 * g);
+}
+
+template <bool FP8>
+struct PairRegs {
+    Chunk<FP8> t[2][kSteps];
+};
+
 template <bool QF8, bool KVF8, bool DIRECT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_attn_partial_kernel(const Args a) {
-    __shared__ __attribute__((aligned(16))) __bf16 vtile[kStepKeys * kVStride];
-    __shared__ f32x4 sbuf[kWaves * 64];
+    // Pairs of key tiles held in registers per wavefront.  Each tile of the
+    // pair reloads (with the pair kPB ahead) as soon as its scores and value
+    // rows are out of its registers.  More pairs in flight make the compiler
+    // park key rows in accumulator registers and copy them back (measured
+    // slower).
+    constexpr int kPB = 1;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) __bf16 qlds[16 * kQStride];
+    __shared__ float mls[2][kWaves][16];
 
     int b, split, ht;
     decode_wg(a, b, split, ht);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
+    const int head = ht * 16 + c;
+    const int k0 = split * a.keys_per_split;
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-    const int k0 = split * a.keys_per_split;
     const int k1 = (k0 + a.keys_per_split < L) ? k0 + a.keys_per_split : L;
-    const int head = ht * 16 + c;
-    const bool head_ok = head < a.H;
-    const int dim0 = w * kDimsPerWave;
-
-    if (k0 >= k1) {
-        if constexpr (DIRECT) {
-            if (head_ok) {
-                uint16_t* o = a.out + ((size_t)b * a.H + head) * kValue + dim0;
-#pragma unroll
-                for (int dt = 0; dt < kDimTiles; ++dt)
-                    *reinterpret_cast<u32x2*>(o + 16 * dt + 4 * g) = u32x2{0u, 0u};
-            }
-        } else if (head_ok && w == 0 && g == 0) {
-            const size_t p = ((size_t)b * a.H + head) * a.splits + split;
-            a.part_m[p] = -INFINITY;
-            a.part_l[p] = 0.0f;
-        }
-        return;
-    }
-
-    // Head c's query at dimensions 32s + 8g .. +7 (zero for heads past H).
-    const uint8_t* qrow = a.q + ((size_t)b * a.H + (head_ok ? head : 0)) * kRow * (QF8 ? 1 : 2);
-    bf16x8 qv[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        qv[s] = to_bf16<QF8>(load_chunk<QF8>(qrow, 32 * s + 8 * g));
-        if (!head_ok) qv[s] = bf16x8{};
-    }
-    float sc = a.score_scale;
-    if constexpr (QF8) sc *= *a.q_scale;
-    if constexpr (KVF8) sc *= *a.kv_scale;
+    // Tiles of this wavefront: keys k0 + 16 (w + 4t) .. +15; pair p is tiles
+    // 2p and 2p + 1.
+    const int first = k0 + kTile * w;
+    const int nt = k1 > first ? (k1 - first + kStepKeys - 1) / kStepKeys : 0;
+    const int np = (nt + 1) / 2;
 
     const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
     const size_t row_bytes = (size_t)kRow * (KVF8 ? 1 : 2);
-    auto key_row = [&](int it0) -> const uint8_t* {
-        // Key c of this wave's 16 (past the range: the range's first key, masked).
-        int key = it0 + 16 * w + c;
-        key = key < k1 ? key : k0;
-        int page = bt[key / a.block_size];
+    // Key c of tile t; past the range it is the range's last key (finite
+    // data of this sequence, given zero weight below).
+    const int last = k1 > 0 ? k1 - 1 : 0;
+    auto tile_key = [&](int t) -> int {
+        const int key = first + kStepKeys * t + c;
+        return key < last ? key : last;
+    };
+    auto page_of = [&](int t) -> int { return bt[tile_key(t) / a.block_size]; };
+    auto row_of = [&](int t, int page) -> const uint8_t* {
         page = page < 0 ? 0 : (page >= a.num_blocks ? a.num_blocks - 1 : page);
-        return a.cache + ((size_t)page * a.block_size + key % a.block_size) * row_bytes;
+        return a.cache + ((size_t)page * a.block_size + tile_key(t) % a.block_size) * row_bytes;
     };
 
-    Chunk<KVF8> kc[kSteps];
-    {
-        const uint8_t* krow = key_row(k0);
+    PairRegs<KVF8> kc[kPB];
+    int pg[kPB][2];
+    if (np > 0) {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) kc[s] = load_chunk<KVF8>(krow, 32 * s + 8 * g);
+        for (int j = 0; j < kPB; ++j) {
+            pg[j][0] = page_of(2 * j);
+            pg[j][1] = page_of(2 * j + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < kPB; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                load_tile<KVF8>(kc[j].t[h], row_of(2 * j + h, pg[j][h]), g);
+                pg[j][h] = page_of(2 * (j + kPB) + h);
+            }
+        }
     }
+
+    // The tile's 16 query rows, as bf16, in LDS (zero rows for heads past H):
+    // operand B of the score products is read from there.
+    {
+        const size_t q_row_bytes = (size_t)kRow * (QF8 ? 1 : 2);
+        for (int idx = threadIdx.x; idx < 16 * (kRow / 8); idx += kThreads) {
+            const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
+            const int hh = ht * 16 + hq;
+            bf16x8 v = {};
+            if (hh < a.H)
+                v = to_bf16<QF8>(load_chunk<QF8>(a.q + ((size_t)b * a.H + hh) * q_row_bytes, 8 * ch));
+            *reinterpret_cast<bf16x8*>(qlds + hq * kQStride + 8 * ch) = v;
+        }
+    }
+    __syncthreads();
+    const __bf16* qrow = qlds + c * kQStride + 8 * g;
+    float sc = a.score_scale;
+    if constexpr (QF8) sc *= *a.q_scale;
+    if constexpr (KVF8) sc *= *a.kv_scale;
 
     f32x4 o[kDimTiles];
 #pragma unroll
     for (int dt = 0; dt < kDimTiles; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.0f;
-    __bf16* vrow = vtile + (16 * w + c) * kVStride;
+    __bf16* vt = reinterpret_cast<__bf16*>(smem) + w * kWaveTile;
+    // Rows 0..15: the pair's first tile, rows 16..31: its second.
+    const __bf16* trow = vt + (4 * g + (c >> 2)) * kVStride + 4 * (c & 3);
 
-    for (int it0 = k0; it0 < k1; it0 += kStepKeys) {
-        // Every wave is done reading the previous step's tiles.
-        __syncthreads();
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    auto process = [&](int j, int p) {
+        f32x4 sc2[2];
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const bf16x8 kb = to_bf16<KVF8>(kc[s]);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qv[s], sacc, 0, 0, 0);
-            if (s < kVSteps) *reinterpret_cast<bf16x8*>(vrow + 32 * s + 8 * g) = kb;
-        }
-        f32x4 sv;
+        for (int h = 0; h < 2; ++h) {
+            __bf16* vrow = vt + (16 * h + c) * kVStride;
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sv[i] = (it0 + 16 * w + 4 * g + i < k1) ? sacc[i] * sc : -INFINITY;
-        sbuf[w * 64 + lane] = sv;
-
-        // The next step's keys stream in while this one finishes.
-        if (it0 + kStepKeys < k1) {
-            const uint8_t* krow = key_row(it0 + kStepKeys);
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) kc[s] = load_chunk<KVF8>(krow, 32 * s + 8 * g);
-        }
-        __syncthreads();
-
-        // Head c's scores for keys 16w' + 4g + i, w' = 0..3.
-        f32x4 st[kWaves];
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) st[v] = sbuf[v * 64 + lane];
-        float bm = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v)
-            bm = fmaxf(bm, fmaxf(fmaxf(st[v][0], st[v][1]), fmaxf(st[v][2], st[v][3])));
-        bm = fmaxf(bm, xor_lanes(bm, 16));
-        bm = fmaxf(bm, xor_lanes(bm, 32));
-        const float mn = fmaxf(m, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        float ps = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(st[v][i] - mn);
-                ps += p;
-                pb[v >> 1][4 * (v & 1) + i] = (__bf16)p;
+            for (int s = 0; s < kSteps; ++s) {
+                const bf16x8 kb = to_bf16<KVF8>(kc[j].t[h][s]);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+                if (s & 1)
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
+                else
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s0, 0, 0, 0);
+                if (s < kVSteps) *reinterpret_cast<bf16x8*>(vrow + 32 * s + 8 * g) = kb;
             }
+            sc2[h] = s0 + s1;
+            // This tile's registers are free: the pair kPB ahead streams in.
+            if (p + kPB < np)
+                load_tile<KVF8>(kc[j].t[h], row_of(2 * (p + kPB) + h, pg[j][h]), g);
+            pg[j][h] = page_of(2 * (p + 2 * kPB) + h);
+        }
+        float sv[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key0 = first + kStepKeys * (2 * p + h) + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sv[4 * h + i] = key0 + i < k1 ? sc2[h][i] * sc : -INFINITY;
+        }
+        float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        tm = fmaxf(tm, xor_lanes(tm, 16));
+        tm = fmaxf(tm, xor_lanes(tm, 32));
+        if (__builtin_amdgcn_ballot_w64(tm > m + kRebase) != 0) {
+            const float mn = tm > m + kRebase ? tm : m;
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) o[dt] *= alpha;
+            lsum *= alpha;
+            m = mn;
+        }
+        // Operand B of the value product: K index 8g + e is key 4g + e of the
+        // pair's first tile (e < 4) or key 4g + e - 4 of its second.
+        float ps = 0.0f;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(sv[e] - m);
+            ps += pe;
+            pb[e] = (__bf16)pe;
         }
         ps += xor_lanes(ps, 16);
         ps += xor_lanes(ps, 32);
-        lsum = lsum * alpha + ps;
-        m = mn;
-
-        // O^T[dim][head c] for this wave's dimensions; K index 8g + e of
-        // product kk is key 32kk + 4g + e (e < 4) or 32kk + 16 + 4g + e - 4.
-        const int trow = 4 * g + (c >> 2);
-        const int tcol = dim0 + 4 * (c & 3);
+        lsum += ps;
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int dt = 0; dt < kDimTiles; ++dt) {
-            f32x4 acc = o[dt] * alpha;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const __bf16* base = vtile + (32 * kk + trow) * kVStride + tcol + 16 * dt;
-                const bf16x4 lo = read_tr(base);
-                const bf16x4 hi = read_tr(base + 16 * kVStride);
-                const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[kk], acc, 0, 0, 0);
-            }
-            o[dt] = acc;
+            const bf16x4 lo = read_tr(trow + 16 * dt);
+            const bf16x4 hi = read_tr(trow + 16 * kVStride + 16 * dt);
+            const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
         }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    for (int p0 = 0; p0 < np; p0 += kPB) {
+#pragma unroll
+        for (int j = 0; j < kPB; ++j)
+            if (p0 + j < np) process(j, p0 + j);
     }
 
-    if (!head_ok) return;
+    // Merge the four wavefronts: weights 2^(m_w - M) over the workgroup max M.
+    if (g == 0) {
+        mls[0][w][c] = m;
+        mls[1][w][c] = lsum;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+        if (mls[1][v][c] > 0.0f) M = fmaxf(M, mls[0][v][c]);
+    const float own = lsum > 0.0f ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+    // Reducer thread: head rh, value dims 16 rq .. 16 rq + 15 of the pass.
+    const int rh = threadIdx.x >> 4, rq = threadIdx.x & 15;
+    float Ltot = 0.0f, Mh = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float lv = mls[1][v][rh];
+        if (lv > 0.0f) Mh = fmaxf(Mh, mls[0][v][rh]);
+    }
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float lv = mls[1][v][rh];
+        if (lv > 0.0f) Ltot += lv * __builtin_amdgcn_exp2f(mls[0][v][rh] - Mh);
+    }
+    const bool rh_ok = ht * 16 + rh < a.H;
+    float fin = 1.0f;
     if constexpr (DIRECT) {
-        float f = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-        if constexpr (KVF8) f *= *a.kv_scale;
-        uint16_t* orow = a.out + ((size_t)b * a.H + head) * kValue + dim0;
+        fin = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+        if constexpr (KVF8) fin *= *a.kv_scale;
+    }
+    float* mb = reinterpret_cast<float*>(smem);
+    const size_t p = ((size_t)b * a.H + ht * 16 + rh) * a.splits + split;
 #pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt) {
-            const f32x4 v = o[dt] * f;
-            const bf16x2 lo = {(__bf16)v.x, (__bf16)v.y}, hi = {(__bf16)v.z, (__bf16)v.w};
-            *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * g) =
-                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    for (int half = 0; half < kValue / kMergeDims; ++half) {
+        __syncthreads();   // value tiles (or the previous pass) no longer read
+#pragma unroll
+        for (int dt = 0; dt < kMergeDims / 16; ++dt)
+            *reinterpret_cast<f32x4*>(mb + (w * 16 + c) * kMergeStride + 16 * dt + 4 * g) =
+                o[half * (kMergeDims / 16) + dt] * own;
+        __syncthreads();
+        f32x4 acc[4] = {};
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[q] += *reinterpret_cast<const f32x4*>(mb + (v * 16 + rh) * kMergeStride +
+                                                          16 * rq + 4 * q);
         }
-    } else {
-        const size_t p = ((size_t)b * a.H + head) * a.splits + split;
-        float* po = a.part_o + p * kValue + dim0;
+        if (rh_ok) {
+            const int d0 = half * kMergeDims + 16 * rq;
+            if constexpr (DIRECT) {
+                uint16_t* orow = a.out + ((size_t)b * a.H + ht * 16 + rh) * kValue + d0;
+                u32x4 pk[2];
 #pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt)
-            *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
-        if (w == 0 && g == 0) {
-            a.part_m[p] = m;
-            a.part_l[p] = lsum;
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = acc[q] * fin;
+                    const bf16x2 lo = {(__bf16)v.x, (__bf16)v.y}, hi = {(__bf16)v.z, (__bf16)v.w};
+                    pk[q >> 1][2 * (q & 1)] = __builtin_bit_cast(uint32_t, lo);
+                    pk[q >> 1][2 * (q & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
+                }
+                *reinterpret_cast<u32x4*>(orow) = pk[0];
+                *reinterpret_cast<u32x4*>(orow + 8) = pk[1];
+            } else {
+                float* po = a.part_o + p * kValue + d0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(po + 4 * q) = acc[q];
+            }
+        }
+    }
+    if constexpr (!DIRECT) {
+        if (rh_ok && rq == 0) {
+            a.part_m[p] = Mh;
+            a.part_l[p] = Ltot;
         }
     }
 }
 
 // Merge the key ranges of one (sequence, head): one wavefront, 8 value
-// dimensions per lane.  Ranges without keys (sum 0) carry no weight.
+// dimensions per lane.  The lanes first turn the ranges' (max, sum) pairs
+// into weights (zero for ranges without keys) in LDS, then every range's
+// partial output is read with independent loads.
 template <bool KVF8>
 __global__ void __launch_bounds__(64) mla_attn_combine_kernel(const Args a) {
+    __shared__ float wts[kMaxSplits];
     const int bh = blockIdx.x;              // b * H + h
     const int lane = threadIdx.x;
     const size_t p0 = (size_t)bh * a.splits;
     float mx = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
+    for (int s = lane; s < a.splits; s += 64)
         if (a.part_l[p0 + s] > 0.0f) mx = fmaxf(mx, a.part_m[p0 + s]);
-    float den = 0.0f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.splits; ++s) {
-        const float l = a.part_l[p0 + s];
-        if (!(l > 0.0f)) continue;
-        const float w = __builtin_amdgcn_exp2f(a.part_m[p0 + s] - mx);
-        den += l * w;
-        const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + (p0 + s) * kValue + 8 * lane);
-        const f32x4 v0 = po[0], v1 = po[1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[e] += w * v0[e];
-            acc[4 + e] += w * v1[e];
+    for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, xor_lanes(mx, k));
+    float den = 0.0f;
+    for (int s = lane; s < a.splits; s += 64) {
+        const float l = a.part_l[p0 + s];
+        const float wgt = l > 0.0f ? __builtin_amdgcn_exp2f(a.part_m[p0 + s] - mx) : 0.0f;
+        wts[s] = wgt;
+        den += wgt * l;
+    }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) den += xor_lanes(den, k);
+    __syncthreads();
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const float* po = a.part_o + p0 * kValue + 8 * lane;
+    int s = 0;
+    for (; s + 4 <= a.splits; s += 4) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + u) * kValue);
+            v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + u) * kValue + 4);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc0 += wts[s + u] * v[2 * u];
+            acc1 += wts[s + u] * v[2 * u + 1];
+        }
+    }
+    for (; s < a.splits; ++s) {
+        acc0 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue);
+        acc1 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
     }
     float f = den > 0.0f ? 1.0f / den : 0.0f;
     if constexpr (KVF8) f *= *a.kv_scale;
     uint16_t r[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = bf16_bits(acc[e] * f);
+    for (int e = 0; e < 4; ++e) {
+        r[e] = bf16_bits(acc0[e] * f);
+        r[4 + e] = bf16_bits(acc1[e] * f);
+    }
     u32x4 packed;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) packed[w] = uint32_t(r[2 * w]) | (uint32_t(r[2 * w + 1]) << 16);
+    for (int k = 0; k < 4; ++k) packed[k] = uint32_t(r[2 * k]) | (uint32_t(r[2 * k + 1]) << 16);
     *reinterpret_cast<u32x4*>(a.out + (size_t)bh * kValue + 8 * lane) = packed;
 }
 
@@ -399,6 +522,7 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
     int64_t splits = base > 0 ? (target + base - 1) / base : 1;
     if (splits < 1) splits = 1;
     if (splits > steps) splits = steps;
+    if (splits > kMaxSplits) splits = kMaxSplits;
     const int64_t kps = ((steps + splits - 1) / splits) * kStepKeys;
     splits = d->max_seq_len > 0 ? (d->max_seq_len + kps - 1) / kps : 1;
     if (base * splits > INT32_MAX) return MLA_DQ_ERR_DIM;

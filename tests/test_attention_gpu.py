@@ -208,3 +208,47 @@ def test_seeds():
     for seed in (1, 2):
         w = I.attn_custom(3, 16, (333, 64, 1500), q_fp8=True, kv_fp8=True, name=f"seed{seed}")
         check(w, f"seed={seed}", seed=seed)
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_nan_in_unused_cache_slots_is_ignored(kv_fp8):
+    """Slots past a sequence's length (the tail of its last page, other
+    pages) hold NaN; no output may see them."""
+    w = I.attn_custom(4, 16, (70, 1, 129, 3000), kv_fp8=kv_fp8, name="nan-slots")
+    inp = I.make_attn_inputs(w)
+    cache = inp["cache"]
+    raw = cache.view(torch.uint8) if kv_fp8 else cache.view(torch.int16)
+    used = torch.zeros(w.num_blocks, w.block_size, dtype=torch.bool)
+    for b, L in enumerate(w.seq_lens):
+        j = torch.arange(L)
+        used[inp["block_table"][b, (j // w.block_size).long()].long(), j % w.block_size] = True
+    raw[~used] = 0x7F if kv_fp8 else 0x7FC0
+    got = run_gpu(w, inp, f"nan-slots kv_fp8={kv_fp8}")
+    ref = oracle_out(w, inp)
+    assert_close(got, ref, bound(w, inp, ref), "nan-slots")
+
+
+@pytest.mark.parametrize("q_fp8", [False, True])
+def test_every_e4m3_code_reaches_the_output_exactly(q_fp8):
+    """With one key per sequence the softmax weight is exactly 1 and the
+    output is that key's value part, rounded to bf16.  With scale 1 every
+    finite E4M3 code (all 254) is a bf16 value, so the output must equal
+    its decoded value bit for bit: the kernel's E4M3 -> bf16 conversion is
+    exact for every code, including subnormals and +-448."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    n = len(codes)                                   # 254
+    B = (n + 511) // 512 * 2                         # 2 sequences of one key
+    w = I.attn_custom(B, 16, 1, q_fp8=q_fp8, kv_fp8=True, kv_scale=1.0, q_scale=1.0,
+                      name="codes")
+    inp = I.make_attn_inputs(w)
+    raw = inp["cache"].view(torch.uint8)
+    vals = np.resize(codes, 2 * 512)
+    for b in range(B):
+        page = int(inp["block_table"][b, 0])
+        raw[page, 0, :512] = torch.from_numpy(vals[512 * b:512 * (b + 1)].copy()) if b < 2 \
+            else raw[page, 0, :512]
+    got = run_gpu(w, inp, f"e4m3 codes q_fp8={q_fp8}")
+    for b in range(min(B, 2)):
+        want = A.e4m3_decode(vals[512 * b:512 * (b + 1)])
+        for h in range(16):
+            assert np.array_equal(got[b, h], want), (b, h)

@@ -61,13 +61,13 @@ def test_plan_covers_every_key_once(B_, H, L):
         ws = B_ * H * p.splits * (512 + 2) * 4 if p.combine else 0
         assert p.workspace_bytes == ws
         assert M.attn_workspace_size(dims(B_, H, MB=MB, L=L), flags) == ws
-        assert p.block_threads == 256 and p.target_workgroups == 512
+        assert p.block_threads == 256 and p.target_workgroups == 256
         assert p.xcd_remap == (1 if p.head_tiles > 1 and p.workgroups % 8 == 0 else 0)
 
 
 def test_plan_aims_at_the_target_workgroup_count():
     p = M.attn_plan(dims(64, 16, MB=64, L=4096), M.ATTN_KV_FP8)
-    assert (p.splits, p.keys_per_split, p.workgroups) == (8, 512, 512)
+    assert (p.splits, p.keys_per_split, p.workgroups) == (4, 1024, 256)
     p = M.attn_plan(dims(1, 16, MB=16, L=1024), M.ATTN_KV_FP8)
     assert (p.splits, p.keys_per_split) == (16, 64)
 
@@ -76,9 +76,9 @@ def test_target_env_override_in_fresh_process():
     code = ("import mla_decode_concat_amd as M; d=M.AttnDims(); d.batch=64; d.num_heads=16;"
             "d.num_blocks=4096; d.block_size=64; d.max_blocks_per_seq=64; d.max_seq_len=4096;"
             "p=M.attn_plan(d,0); print(p.target_workgroups, p.splits, p.keys_per_split)")
-    env = dict(os.environ, MLA_ATTN_TARGET_WGS="256", PYTHONPATH=ROOT)
+    env = dict(os.environ, MLA_ATTN_TARGET_WGS="128", PYTHONPATH=ROOT)
     out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
-    assert out.stdout.split() == ["256", "4", "1024"]
+    assert out.stdout.split() == ["128", "2", "2048"]
 
 
 BASE = 1 << 36
