@@ -216,6 +216,38 @@ class DecodeSlice:
                                         self.kv_scale, self.flags)
 
 
+class DecodeStep(DecodeSlice):
+    """The slice above followed by the decode attention that consumes its
+    output: B sequences each gain one token (T = B) at position L - 1, the
+    epilogue writes that token's E4M3 latent row into the paged cache at its
+    slot and its E4M3 query rows, and the attention reads the B queries over
+    all L cached rows of each sequence (the other L - 1 rows are synthetic
+    E4M3 context)."""
+
+    def __init__(self, B: int, H: int, L: int, dev: str, seed: int = 3):
+        super().__init__(B, H, dev, seed)
+        w = I.attn_custom(B, H, L, q_fp8=True, kv_fp8=True, name="decode_step")
+        host = I.make_attn_inputs(w, seed)
+        self.w = w
+        self.cache = host["cache"].to(dev)
+        self.block_table = host["block_table"].to(dev)
+        self.seq_lens = host["seq_lens"].to(dev)
+        last = L - 1
+        bt = host["block_table"]
+        self.slots = (bt[:, last // w.block_size].to(torch.int64) * w.block_size
+                      + last % w.block_size).to(dev)
+        self.positions = torch.full((B,), last, dtype=torch.int64, device=dev)
+        self.out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
+        self.attn = M.PreparedAttention(self.out, self.q_out, self.cache, self.block_table,
+                                        self.seq_lens, w.sm_scale, self.q_scale, self.kv_scale,
+                                        max_seq_len=L)
+
+    def step(self, epilogue: bool = True, copies: bool = False, attention: bool = True):
+        super().step(epilogue, copies)
+        if epilogue and attention:
+            self.attn()
+
+
 def time_graph_fn(fn, calls: int = 20, replays: int = 20) -> float:
     """Device µs per call of fn when `calls` calls are captured in one graph."""
     side = torch.cuda.Stream()
@@ -241,7 +273,8 @@ def time_graph_fn(fn, calls: int = 20, replays: int = 20) -> float:
 
 def decode_slice_timings(dev: str) -> dict:
     """Graph-replayed µs per decode-step slice: producers alone, producers +
-    epilogue on strided views, producers + copies + epilogue."""
+    epilogue on strided views, producers + copies + epilogue; and the whole
+    step with the decode attention over 4096 cached tokens per sequence."""
     out = {}
     for T in (1, 64):
         ds = DecodeSlice(T, 16, dev)
@@ -253,6 +286,17 @@ def decode_slice_timings(dev: str) -> dict:
                             "epilogue_increment_us": round(strided - base, 3),
                             "copies_avoided_us": round(copies - strided, 3)}
         log(f"decode slice T={T}: {out[f't{T}_h16']}")
+    for B in (1, 64):
+        st = DecodeStep(B, 16, 4096, dev)
+        base = time_graph_fn(lambda: st.step(epilogue=False), calls=10)
+        epi = time_graph_fn(lambda: st.step(attention=False), calls=10)
+        full = time_graph_fn(lambda: st.step(), calls=10)
+        out[f"b{B}_h16_l4096_with_attention"] = {
+            "producers_us": round(base, 3), "with_epilogue_us": round(epi, 3),
+            "with_epilogue_and_attention_us": round(full, 3),
+            "attention_increment_us": round(full - epi, 3)}
+        log(f"decode step B={B} L=4096: {out[f'b{B}_h16_l4096_with_attention']}")
+        del st
     return out
 
 

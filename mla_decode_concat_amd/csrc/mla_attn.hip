@@ -146,6 +146,28 @@ __device__ __forceinline__ float xor_lanes(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane
+// row): v_permlane16_swap and v_permlane32_swap hand each lane its partner
+// row's value without going through LDS.
+__device__ __forceinline__ float max_rows(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]),
+                          __builtin_bit_cast(float, (unsigned)a[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, m);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+__device__ __forceinline__ float sum_rows(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+    const unsigned w = __builtin_bit_cast(unsigned, m);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -270,7 +292,12 @@ mla_attn_partial_kernel(const Args a) {
     float m = -INFINITY, lsum = 0.0f;
     __bf16* vt = reinterpret_cast<__bf16*>(smem) + w * kWaveTile;
     // Rows 0..15: the pair's first tile, rows 16..31: its second.
-    const __bf16* trow = vt + (4 * g + (c >> 2)) * kVStride + 4 * (c & 3);
+    // The tile's 16-byte chunk j of row r sits at chunk j ^ ((r >> 3) & 1): the
+    // 16 rows one store instruction writes then cover all 64 banks, and the
+    // four rows of a transpose load keep theirs (the swap stays inside each
+    // row's 32-byte column block).
+    const __bf16* trow = vt + (4 * g + (c >> 2)) * kVStride +
+                         8 * (((c & 3) >> 1) ^ ((g >> 1) & 1)) + 4 * (c & 1);
 
     auto process = [&](int j, int p) {
         f32x4 sc2[2];
@@ -286,7 +313,8 @@ mla_attn_partial_kernel(const Args a) {
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
                 else
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s0, 0, 0, 0);
-                if (s < kVSteps) *reinterpret_cast<bf16x8*>(vrow + 32 * s + 8 * g) = kb;
+                if (s < kVSteps)
+                    *reinterpret_cast<bf16x8*>(vrow + 32 * s + 8 * (g ^ (c >> 3))) = kb;
             }
             sc2[h] = s0 + s1;
             // This tile's registers are free: the pair kPB ahead streams in.
@@ -304,8 +332,7 @@ mla_attn_partial_kernel(const Args a) {
         }
         float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        tm = fmaxf(tm, xor_lanes(tm, 16));
-        tm = fmaxf(tm, xor_lanes(tm, 32));
+        tm = max_rows(tm);
         if (__builtin_amdgcn_ballot_w64(tm > m + kRebase) != 0) {
             const float mn = tm > m + kRebase ? tm : m;
             const float alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -324,9 +351,7 @@ mla_attn_partial_kernel(const Args a) {
             ps += pe;
             pb[e] = (__bf16)pe;
         }
-        ps += xor_lanes(ps, 16);
-        ps += xor_lanes(ps, 32);
-        lsum += ps;
+        lsum += sum_rows(ps);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int dt = 0; dt < kDimTiles; ++dt) {

@@ -252,3 +252,46 @@ def test_every_e4m3_code_reaches_the_output_exactly(q_fp8):
         want = A.e4m3_decode(vals[512 * b:512 * (b + 1)])
         for h in range(16):
             assert np.array_equal(got[b, h], want), (b, h)
+
+
+def test_decode_step_graph_epilogue_then_attention():
+    """One decode step captured in a HIP graph: the q-path GEMMs, the
+    epilogue (writes each sequence's new E4M3 cache row and E4M3 queries),
+    then the attention over all L rows.  Every replay equals the epilogue
+    oracle followed by the attention oracle (within the attention bound)."""
+    import bench
+    import oracle
+    from tests._util import oracle_run
+    B, H, L = 6, 16, 333
+    st = bench.DecodeStep(B, H, L, DEV)
+    announce(f"decode step graph B={B} H={H} L={L}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # the epilogue's inputs, materialised, and the oracle's epilogue
+    ql_nope, q_pe, kv_c, k_pe = st.producers()
+    ew = I.custom(B, H, num_blocks=st.w.num_blocks, rope=True, q_fp8=True, kv_fp8=True)
+    einp = dict(ql_nope=ql_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(),
+                kv_c=kv_c.cpu().contiguous(), k_pe=k_pe.cpu().contiguous(),
+                cache=st.cache.cpu(), slot_mapping=st.slots.cpu(), positions=st.positions.cpu(),
+                rope_cos_sin=st.table.cpu(), q_scale=st.q_scale.cpu(), kv_scale=st.kv_scale.cpu())
+    want_q, want_cache = oracle_run(ew, einp)
+    ainp = dict(q=torch.from_numpy(want_q).view(torch.float8_e4m3fn),
+                cache=torch.from_numpy(want_cache).view(torch.float8_e4m3fn),
+                block_table=st.block_table.cpu(), seq_lens=st.seq_lens.cpu())
+    ref = oracle_out(st.w, ainp)
+    tol = bound(st.w, ainp, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step()
+    for _ in range(3):
+        st.out.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(st.q_out.cpu()), want_q)
+        assert np.array_equal(bits(st.cache.cpu()), want_cache)
+        assert_close(st.out.float().cpu().numpy().astype(np.float64), ref, tol, "decode step")
