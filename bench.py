@@ -320,7 +320,7 @@ def attn_sources_digest() -> str:
 
 
 def attn_traffic_entry(name: str):
-    """Measured HBM bytes per call (partial + combine kernels) from the
+    """Measured HBM bytes per call (the partial kernel and its range merge) from the
     committed counter summary, if taken on the current attention sources."""
     if not os.path.exists(ATTN_TRAFFIC_FILE):
         return None

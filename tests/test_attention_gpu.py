@@ -295,3 +295,49 @@ def test_decode_step_graph_epilogue_then_attention():
         assert np.array_equal(bits(st.q_out.cpu()), want_q)
         assert np.array_equal(bits(st.cache.cpu()), want_cache)
         assert_close(st.out.float().cpu().numpy().astype(np.float64), ref, tol, "decode step")
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One workspace serves repeated calls and a different problem (it is
+    scratch between calls): every result is the same as the first and
+    matches the oracle."""
+    w1 = I.attn_custom(5, 16, (100, 2000, 3, 4096, 65), kv_fp8=True, name="ws1")
+    w2 = I.attn_custom(3, 20, (700, 10, 1500), q_fp8=True, kv_fp8=True, name="ws2")
+    d1, d2 = to_device(I.make_attn_inputs(w1)), to_device(I.make_attn_inputs(w2))
+    o1 = torch.empty(w1.batch, w1.heads, 512, dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty(w2.batch, w2.heads, 512, dtype=torch.bfloat16, device=DEV)
+    sizes = []
+    for w, d in ((w1, d1), (w2, d2)):
+        dims = M.AttnDims()
+        dims.batch, dims.num_heads = w.batch, w.heads
+        dims.num_blocks, dims.block_size = w.num_blocks, w.block_size
+        dims.max_blocks_per_seq = w.max_blocks
+        dims.max_seq_len = w.max_blocks * w.block_size
+        sizes.append(M.attn_workspace_size(dims, (M.ATTN_Q_FP8 if w.q_fp8 else 0) | M.ATTN_KV_FP8))
+    assert min(sizes) > 0
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=DEV)
+    p1 = M.PreparedAttention(o1, d1["q"], d1["cache"], d1["block_table"], d1["seq_lens"],
+                             w1.sm_scale, d1["q_scale"], d1["kv_scale"], workspace=ws)
+    p2 = M.PreparedAttention(o2, d2["q"], d2["cache"], d2["block_table"], d2["seq_lens"],
+                             w2.sm_scale, d2["q_scale"], d2["kv_scale"], workspace=ws)
+    announce("workspace reuse")
+    p1()
+    torch.cuda.synchronize()
+    first = o1.clone()
+    for _ in range(2):
+        o1.view(torch.int16).fill_(-1)
+        p1()
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), first.view(torch.int16))
+    p2()
+    torch.cuda.synchronize()
+    inp2 = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d2.items()}
+    ref2 = oracle_out(w2, inp2)
+    assert_close(o2.float().cpu().numpy().astype(np.float64), ref2, bound(w2, inp2, ref2), "ws2")
+    o1.view(torch.int16).fill_(-1)
+    p1()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), first.view(torch.int16))
+    inp1 = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d1.items()}
+    ref1 = oracle_out(w1, inp1)
+    assert_close(first.float().cpu().numpy().astype(np.float64), ref1, bound(w1, inp1, ref1), "ws1")
