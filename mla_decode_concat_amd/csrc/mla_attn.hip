@@ -223,7 +223,6 @@ mla_attn_partial_kernel(const Args a) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int head = ht * 16 + c;
     const int k0 = split * a.keys_per_split;
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
