@@ -53,7 +53,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -79,7 +78,8 @@ constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merg
 static_assert(kWaves * 16 * kMergeStride * 4 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
-// The running max moves only when a tile exceeds it by more than this (log2).
+// The running max moves only when a pair of tiles exceeds it by more than
+// this (log2 units).
 constexpr float kRebase = 8.0f;
 
 struct Args {
