@@ -9,6 +9,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import mla_decode_concat_amd as M
 from mla_decode_concat_amd import _binding as B
@@ -166,3 +167,60 @@ def test_misaligned_pointer(name, off):
 @pytest.mark.parametrize("sm", [float("nan"), float("inf"), -float("inf")])
 def test_bad_softmax_scale(sm):
     assert _call(_ptrs(), 0, dims(), sm=sm) == B.ERR_DIM
+
+
+# ---- Python binding: argument checks that run before anything is launched ----
+
+def _cpu_args(B_=2, H=16, NB=4, BS=64, MB=2, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16):
+    return dict(out=torch.empty(B_, H, 512, dtype=torch.bfloat16),
+                q=torch.zeros(B_, H, 576, dtype=q_dtype),
+                cache=torch.zeros(NB, BS, 576, dtype=kv_dtype),
+                block_table=torch.zeros(B_, MB, dtype=torch.int32),
+                seq_lens=torch.ones(B_, dtype=torch.int32),
+                q_scale=None, kv_scale=None)
+
+
+def _validate(a):
+    B._attn_validate(a["out"], a["q"], a["cache"], a["block_table"], a["seq_lens"],
+                     a["q_scale"], a["kv_scale"])
+
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("q", torch.zeros(2, 16, 512, dtype=torch.bfloat16), "q must be"),
+    ("q", torch.zeros(2, 16, 576, dtype=torch.float16), "q must be bf16 or e4m3"),
+    ("out", torch.empty(2, 16, 512, dtype=torch.float32), "out must be"),
+    ("out", torch.empty(2, 8, 512, dtype=torch.bfloat16), "out must be"),
+    ("cache", torch.zeros(4, 64, 512, dtype=torch.bfloat16), "cache must be"),
+    ("cache", torch.zeros(4, 64, 576, dtype=torch.float32), "cache must be bf16 or e4m3"),
+    ("block_table", torch.zeros(2, 2, dtype=torch.int64), "block_table must be"),
+    ("block_table", torch.zeros(3, 2, dtype=torch.int32), "block_table must be"),
+    ("seq_lens", torch.ones(2, dtype=torch.int64), "seq_lens must be"),
+    ("seq_lens", torch.ones(3, dtype=torch.int32), "seq_lens must be"),
+])
+def test_binding_rejects_bad_arguments(field, value, msg):
+    a = _cpu_args()
+    a[field] = value
+    with pytest.raises(ValueError, match=msg):
+        _validate(a)
+
+
+def test_binding_rejects_views_and_missing_scales():
+    a = _cpu_args()
+    a["q"] = torch.zeros(2, 576, 16, dtype=torch.bfloat16).transpose(1, 2)
+    with pytest.raises(ValueError, match="contiguous"):
+        _validate(a)
+    a = _cpu_args(kv_dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="kv_scale"):
+        _validate(a)
+    a = _cpu_args(q_dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="q_scale"):
+        _validate(a)
+
+
+def test_binding_requires_gpu_tensors():
+    a = _cpu_args(q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn)
+    a["q_scale"] = torch.ones(1)
+    a["kv_scale"] = torch.ones(1)
+    with pytest.raises(ValueError, match="GPU"):
+        _validate(a)
