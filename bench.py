@@ -354,7 +354,37 @@ class AttnSet:
         self.prepared()
 
 
-def attention_timings(dev: str, steps: int) -> dict:
+def attn_cpu_oracle(w: I.AttnWorkload, host: dict, seconds: float) -> dict:
+    """The float64 attention oracle as it stands, on the first sequences of
+    the workload (as many as fit in about `seconds`), scaled to the whole
+    batch."""
+    import numpy as np
+    from oracle import attention as A
+
+    def bits(t):
+        t = t.contiguous()
+        return (t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16
+                else t.view(torch.uint8).numpy())
+    q, cache = bits(host["q"]), bits(host["cache"])
+    bt, lens = host["block_table"].numpy(), host["seq_lens"].numpy()
+    done, t0 = 0, time.perf_counter()
+    while done < w.batch and time.perf_counter() - t0 < seconds:
+        A.mla_decode_attention(q[done:done + 1], cache, bt[done:done + 1], lens[done:done + 1],
+                               w.sm_scale, w.q_scale if w.q_fp8 else None,
+                               w.kv_scale if w.kv_fp8 else None)
+        done += 1
+    el = time.perf_counter() - t0
+    per_call_us = el / done * w.batch * 1e6
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"us_per_call": round(per_call_us, 1), "sample": f"{done} of {w.batch} sequences",
+            "kind": "oracle", "cores": cores}
+
+
+def attention_timings(dev: str, steps: int, cpu_seconds: float = 0.0) -> dict:
     """Decode attention over the paged latent cache, per workload: device
     time per call (events around back-to-back calls on the launch stream),
     with enough independent cache copies rotated that their total exceeds
@@ -382,6 +412,8 @@ def attention_timings(dev: str, steps: int) -> dict:
             "workgroups": pl.workgroups, "combine": bool(pl.combine),
             "traffic_bytes": attn_traffic_entry(name),
         }
+        if cpu_seconds > 0:
+            out[name]["cpu_oracle"] = attn_cpu_oracle(w, host, cpu_seconds)
         log(f"attention {name}: {out[name]}")
         del sets
         torch.cuda.empty_cache()
@@ -465,6 +497,8 @@ def main() -> int:
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--only-attention", action="store_true",
                     help="time only the decode-attention workloads (prints their JSON)")
+    ap.add_argument("--only-decode-slice", action="store_true",
+                    help="time only the decode-step slices in HIP graphs (prints their JSON)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -494,6 +528,9 @@ def main() -> int:
     M.load()
     if args.only_attention:
         print(json.dumps({"decode_attention": attention_timings(dev, args.steps)}), flush=True)
+        return 0
+    if args.only_decode_slice:
+        print(json.dumps({"decode_step_slice_graph": decode_slice_timings(dev)}), flush=True)
         return 0
     w = I.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.describe()}")
@@ -562,7 +599,8 @@ def main() -> int:
             torch.cuda.empty_cache()
 
     decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
-    attention = {} if args.no_attention else attention_timings(dev, args.steps)
+    attention = {} if args.no_attention else attention_timings(
+        dev, args.steps, 0.0 if args.no_cpu_baseline else 3.0)
 
     traffic = traffic_entry(nbytes)
     out = {
