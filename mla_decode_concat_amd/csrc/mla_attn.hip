@@ -78,6 +78,7 @@ constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merg
 static_assert(kWaves * 16 * kMergeStride * 4 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
+constexpr int kMinSplitSteps = 2;              // 64-key rounds per range, at least
 // The running max moves only when a pair of tiles exceeds it by more than
 // this (log2 units).
 constexpr float kRebase = 8.0f;
@@ -445,50 +446,83 @@ mla_attn_partial_kernel(const Args a) {
     }
 }
 
-// Merge the key ranges of one (sequence, head): one wavefront, 8 value
-// dimensions per lane.  The lanes first turn the ranges' (max, sum) pairs
-// into weights (zero for ranges without keys) in LDS, then every range's
-// partial output is read with independent loads.
+// Merge the key ranges of one (sequence, head): four wavefronts, each lane
+// 8 value dimensions of every fourth range.  The threads turn the ranges'
+// (max, sum) pairs into weights (zero for ranges without keys) in LDS, sum
+// their share of the weighted partial outputs with independent loads, and
+// wavefront 0 adds the other three sums.
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) v = fmaxf(v, xor_lanes(v, k));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) v += xor_lanes(v, k);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return v;
+}
+
 template <bool KVF8>
-__global__ void __launch_bounds__(64) mla_attn_combine_kernel(const Args a) {
+__global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
     __shared__ float wts[kMaxSplits];
+    __shared__ float red[4];
+    __shared__ f32x4 part[3][64][2];
     const int bh = blockIdx.x;              // b * H + h
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
     const size_t p0 = (size_t)bh * a.splits;
     float mx = -INFINITY;
-    for (int s = lane; s < a.splits; s += 64)
+    for (int s = threadIdx.x; s < a.splits; s += kCombineThreads)
         if (a.part_l[p0 + s] > 0.0f) mx = fmaxf(mx, a.part_m[p0 + s]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, xor_lanes(mx, k));
+    mx = block_max(mx, red);
     float den = 0.0f;
-    for (int s = lane; s < a.splits; s += 64) {
+    for (int s = threadIdx.x; s < a.splits; s += kCombineThreads) {
         const float l = a.part_l[p0 + s];
         const float wgt = l > 0.0f ? __builtin_amdgcn_exp2f(a.part_m[p0 + s] - mx) : 0.0f;
         wts[s] = wgt;
         den += wgt * l;
     }
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) den += xor_lanes(den, k);
-    __syncthreads();
+    den = block_sum(den, red);   // its barrier also publishes wts
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     const float* po = a.part_o + p0 * kValue + 8 * lane;
-    int s = 0;
-    for (; s + 4 <= a.splits; s += 4) {
+    int s = grp;
+    for (; s + 12 < a.splits; s += 16) {
         f32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + u) * kValue);
-            v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + u) * kValue + 4);
+            v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + 4 * u) * kValue);
+            v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + 4 * u) * kValue + 4);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            acc0 += wts[s + u] * v[2 * u];
-            acc1 += wts[s + u] * v[2 * u + 1];
+            acc0 += wts[s + 4 * u] * v[2 * u];
+            acc1 += wts[s + 4 * u] * v[2 * u + 1];
         }
     }
-    for (; s < a.splits; ++s) {
+    for (; s < a.splits; s += 4) {
         acc0 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue);
         acc1 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
+    }
+    if (grp > 0) {
+        part[grp - 1][lane][0] = acc0;
+        part[grp - 1][lane][1] = acc1;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        acc0 += part[k][lane][0];
+        acc1 += part[k][lane][1];
     }
     float f = den > 0.0f ? 1.0f / den : 0.0f;
     if constexpr (KVF8) f *= *a.kv_scale;
@@ -545,7 +579,11 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
     const int64_t target = target_workgroups();
     int64_t splits = base > 0 ? (target + base - 1) / base : 1;
     if (splits < 1) splits = 1;
-    if (splits > steps) splits = steps;
+    // at least two 64-key rounds per range: a range's fixed cost (first loads,
+    // merge of its four wavefronts, its partial results) then stays small
+    // against its keys
+    const int64_t most = (steps + kMinSplitSteps - 1) / kMinSplitSteps;
+    if (splits > most) splits = most;
     if (splits > kMaxSplits) splits = kMaxSplits;
     const int64_t kps = ((steps + splits - 1) / splits) * kStepKeys;
     splits = d->max_seq_len > 0 ? (d->max_seq_len + kps - 1) / kps : 1;
@@ -574,8 +612,8 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, KVF8, false>), grid, block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3(uint32_t(a.B * a.H)), dim3(64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3(uint32_t(a.B * a.H)),
+                       dim3(kCombineThreads), 0, stream, a);
     return hipGetLastError();
 }
 
