@@ -1,19 +1,27 @@
 // MLA decode attention over the paged latent cache for gfx950 (MI355X).
 //
-// The definition is in include/mla_attn.h.  Split-KV decoding: a workgroup of
-// four wavefronts handles one (sequence, tile of 16 heads, range of keys).
-// The wavefronts work independently on interleaved tiles of 16 keys (wave w
-// takes tiles w, w+4, w+8, ... of the range), each with its own online
+// The definition is in include/mla_attn.h.  Split-KV decoding: a workgroup
+// handles one (sequence, tile of 16 heads, range of keys) with four compute
+// wavefronts.  They work independently on interleaved tiles of 16 keys (wave
+// w takes tiles w, w+4, w+8, ... of the range), each with its own online
 // softmax and its own accumulator for all 512 value dimensions, and meet
 // once at the end to merge their four partial results through LDS.
+//
+// Two kernels share that scheme.  With a bf16 cache each compute wavefront
+// loads its own keys into registers (mla_attn_partial_kernel, described
+// next).  With an E4M3 cache four loader wavefronts stream the keys into an
+// LDS ring for their compute partners (mla_attn_ring_kernel, further down).
 //
 // Per pair of 16-key tiles, in one wavefront (lane l: c = l % 16, g = l / 16):
 //  * scores on the matrix cores, transposed: S^T[key][head] = K Q^T with
 //    v_mfma_f32_16x16x32_bf16 over 18 steps of 32 of the 576 dimensions.
-//    Lane l holds 16 bytes of key c at dimensions 32s + 8g (operand A) and
-//    reads head c's query at the same dimensions from the workgroup's query
-//    tile in LDS (operand B); the result leaves lane l with head c's scores
-//    for keys 4g .. 4g+3 of the tile.
+//    Lane l loads 16 bytes of key c per instruction: bf16 dimensions
+//    32s + 8g .. +7 for step s, or E4M3 dimensions 64i + 16g .. +15, which
+//    feed steps 2i (first eight) and 2i + 1 (last eight).  The sum over the
+//    576 dimensions does not care how they are dealt to steps and K slots,
+//    so operand B is head c's query at the same dimensions, read from the
+//    workgroup's query tile in LDS.  The result leaves lane l with head c's
+//    scores for keys 4g .. 4g+3 of the tile.
 //  * each tile's value part (first 512 elements) goes, as bf16, to a
 //    wavefront-private LDS tile in the cache's row-major layout, and the
 //    tile's registers reload with the next pair's keys.
@@ -55,6 +63,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRow = 576;           // latent row: 512 value + 64 positional elements
 constexpr int kValue = 512;
@@ -73,9 +82,8 @@ constexpr int kWaveTile = 2 * kTile * kVStride;       // bf16 elements per wavef
 // 16 rows one instruction reads on disjoint banks.
 constexpr int kQStride = kRow + 8;
 constexpr int kMergeDims = 256;                       // value dims merged per pass
-constexpr int kMergeStride = kMergeDims + 4;          // floats per LDS row (one head)
 constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merge buffer too
-static_assert(kWaves * 16 * kMergeStride * 4 <= kLdsBytes, "merge buffer");
+static_assert(kWaves * 16 * 64 * 16 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
 constexpr int kMinSplitSteps = 2;              // 64-key rounds per range, at least
@@ -143,6 +151,27 @@ __device__ __forceinline__ bf16x8 to_bf16(Chunk<FP8> c) {
         return __builtin_bit_cast(bf16x8, c.v);
 }
 
+// A key tile in registers: 16 bytes per load instruction and lane, 18
+// instructions for a bf16 row, 9 for an E4M3 row.
+template <bool FP8>
+struct KeyTile {
+    static constexpr int kLoads = FP8 ? kSteps / 2 : kSteps;
+    u32x4 r[kLoads];
+    // first element of load i for lane group g
+    static __device__ __forceinline__ int dim(int i, int g) { return FP8 ? 64 * i + 16 * g : 32 * i + 8 * g; }
+    // operand A of score step s, as bf16
+    __device__ __forceinline__ bf16x8 step(int s) const {
+        if constexpr (FP8)
+            return e4m3x8_to_bf16(s & 1 ? u32x2{r[s >> 1][2], r[s >> 1][3]} : u32x2{r[s >> 1][0], r[s >> 1][1]});
+        else
+            return __builtin_bit_cast(bf16x8, r[s]);
+    }
+    // Score step s takes the 8-element chunk 8(s / 2) + 2g + s % 2 (E4M3) or
+    // 4s + g (bf16) of the row: the lane part plus a constant offset.
+    static __device__ __forceinline__ int lane_dim(int g) { return FP8 ? 16 * g : 8 * g; }
+    static constexpr int step_dim(int s) { return FP8 ? 64 * (s >> 1) + 8 * (s & 1) : 32 * s; }
+};
+
 __device__ __forceinline__ float xor_lanes(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
@@ -196,15 +225,135 @@ __device__ __forceinline__ void decode_wg(const Args& a, int& b, int& split, int
 }
 
 template <bool FP8>
-__device__ __forceinline__ void load_tile(Chunk<FP8> (&kc)[kSteps], const uint8_t* row, int g) {
+__device__ __forceinline__ void load_tile(KeyTile<FP8>& kt, const uint8_t* row, int g) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) kc[s] = load_chunk<FP8>(row, 32 * s + 8 * g);
+    for (int i = 0; i < KeyTile<FP8>::kLoads; ++i)
+        kt.r[i] = *reinterpret_cast<const u32x4*>(row + KeyTile<FP8>::dim(i, g) * (FP8 ? 1 : 2));
 }
 
 template <bool FP8>
 struct PairRegs {
-    Chunk<FP8> t[2][kSteps];
+    KeyTile<FP8> t[2];
 };
+
+// The workgroup's 16 query rows (heads 16 ht .. 16 ht + 15 of sequence b) as
+// bf16 in LDS, row stride kQStride; rows for heads past H are zero.  The NT
+// staging threads first issue all their loads (unconditionally, at clamped
+// rows) and only then write, so the loads share one memory latency.
+template <bool QF8, int NT>
+__device__ __forceinline__ void stage_queries(const Args& a, int b, int ht, __bf16* qlds, int tid) {
+    constexpr int kChunks = 16 * (kRow / 8);   // 8-element chunks of the tile
+    constexpr int kIter = (kChunks + NT - 1) / NT;
+    const size_t q_row_bytes = (size_t)kRow * (QF8 ? 1 : 2);
+    Chunk<QF8> v[kIter];
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+        int idx = tid + NT * k;
+        idx = idx < kChunks ? idx : kChunks - 1;
+        const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
+        int hh = ht * 16 + hq;
+        hh = hh < a.H ? hh : a.H - 1;
+        v[k] = load_chunk<QF8>(a.q + ((size_t)b * a.H + hh) * q_row_bytes, 8 * ch);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+        const int idx = tid + NT * k;
+        if (idx < kChunks) {
+            const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
+            const bf16x8 x = ht * 16 + hq < a.H ? to_bf16<QF8>(v[k]) : bf16x8{};
+            *reinterpret_cast<bf16x8*>(qlds + hq * kQStride + 8 * ch) = x;
+        }
+    }
+}
+
+// Workgroup barrier for LDS traffic only: this wavefront's LDS operations are
+// complete, global loads and stores may still be in flight (__syncthreads
+// would also wait for those).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Merge the four compute wavefronts' (max, sum, output) through LDS with
+// weights 2^(m_w - M) over the workgroup max M, then write the range's result:
+// bf16 output when the range is the whole sequence, else the unnormalised
+// output with its max and sum.  Threads 0..255 are the compute wavefronts;
+// all NT threads of the workgroup share the reduction.  Two passes of 256
+// value dims: wavefront w stores its 16 accumulator tiles lane-major
+// (tile j, lane l at 16 B * (64 (16 w + j) + l)), so every store and every
+// reducer load of an instruction covers 1 KB of consecutive LDS.  mb is LDS
+// scratch of at least 64 KB that no wavefront reads any more.
+template <bool KVF8, bool DIRECT, int NT>
+__device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDimTiles], float m, float lsum,
+                                            bool compute, int b, int split, int ht, float* mb,
+                                            float (&mls)[2][kWaves][16]) {
+    const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+    const int w = (threadIdx.x >> 6) & (kWaves - 1);
+    if (compute && g == 0) {
+        mls[0][w][c] = m;
+        mls[1][w][c] = lsum;
+    }
+    lds_barrier();
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+        if (mls[1][v][c] > 0.0f) M = fmaxf(M, mls[0][v][c]);
+    const float own = lsum > 0.0f ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+    // Every reducer item of a thread belongs to head c (items step by NT, a
+    // multiple of 64); its total weight and, with one range, 1 / sum.
+    float Ltot = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float lv = mls[1][v][c];
+        if (lv > 0.0f) Ltot += lv * __builtin_amdgcn_exp2f(mls[0][v][c] - M);
+    }
+    const bool head_ok = ht * 16 + c < a.H;
+    float fin = 1.0f;
+    if constexpr (DIRECT) {
+        fin = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+        if constexpr (KVF8) fin *= *a.kv_scale;
+    }
+    const size_t row = (size_t)b * a.H + ht * 16 + c;       // (sequence, head) of this thread's items
+    const size_t p = row * a.splits + split;
+    f32x4* lm = reinterpret_cast<f32x4*>(mb);
+#pragma unroll
+    for (int half = 0; half < kValue / kMergeDims; ++half) {
+        lds_barrier();   // LDS tiles (or the previous pass) no longer read
+        if (compute) {
+#pragma unroll
+            for (int j = 0; j < kMergeDims / 16; ++j)
+                lm[64 * (16 * w + j) + lane] = o[half * (kMergeDims / 16) + j] * own;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < (16 * 64) / NT; ++it) {
+            const int item = threadIdx.x + NT * it;              // (tile j, lane): lane == this lane
+            const int j = item >> 6;
+            f32x4 acc = lm[64 * j + lane];
+#pragma unroll
+            for (int v = 1; v < kWaves; ++v) acc += lm[64 * (16 * v + j) + lane];
+            if (head_ok) {
+                const int d0 = 16 * (half * (kMergeDims / 16) + j) + 4 * g;
+                if constexpr (DIRECT) {
+                    const f32x4 r = acc * fin;
+                    const bf16x2 lo = {(__bf16)r.x, (__bf16)r.y}, hi = {(__bf16)r.z, (__bf16)r.w};
+                    *reinterpret_cast<u32x2*>(a.out + row * kValue + d0) =
+                        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                } else {
+                    *reinterpret_cast<f32x4*>(a.part_o + p * kValue + d0) = acc;
+                }
+            }
+        }
+    }
+    if constexpr (!DIRECT) {
+        if (threadIdx.x < 16 && head_ok) {
+            a.part_m[p] = M;
+            a.part_l[p] = Ltot;
+        }
+    }
+}
 
 template <bool QF8, bool KVF8, bool DIRECT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -267,21 +416,11 @@ mla_attn_partial_kernel(const Args a) {
         }
     }
 
-    // The tile's 16 query rows, as bf16, in LDS (zero rows for heads past H):
-    // operand B of the score products is read from there.
-    {
-        const size_t q_row_bytes = (size_t)kRow * (QF8 ? 1 : 2);
-        for (int idx = threadIdx.x; idx < 16 * (kRow / 8); idx += kThreads) {
-            const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
-            const int hh = ht * 16 + hq;
-            bf16x8 v = {};
-            if (hh < a.H)
-                v = to_bf16<QF8>(load_chunk<QF8>(a.q + ((size_t)b * a.H + hh) * q_row_bytes, 8 * ch));
-            *reinterpret_cast<bf16x8*>(qlds + hq * kQStride + 8 * ch) = v;
-        }
-    }
+    // The tile's 16 query rows, as bf16, in LDS: operand B of the score
+    // products is read from there.
+    stage_queries<QF8, kThreads>(a, b, ht, qlds, threadIdx.x);
     __syncthreads();
-    const __bf16* qrow = qlds + c * kQStride + 8 * g;
+    const __bf16* qrow = qlds + c * kQStride + KeyTile<KVF8>::lane_dim(g);
     float sc = a.score_scale;
     if constexpr (QF8) sc *= *a.q_scale;
     if constexpr (KVF8) sc *= *a.kv_scale;
@@ -296,6 +435,12 @@ mla_attn_partial_kernel(const Args a) {
     // 16 rows one store instruction writes then cover all 64 banks, and the
     // four rows of a transpose load keep theirs (the swap stays inside each
     // row's 32-byte column block).
+    // Where score step s's 8 value elements go in row c: chunk index j (the
+    // lane part plus step_dim(s) / 8) becomes j ^ (c >> 3).
+    int vsw[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        vsw[par] = 8 * ((KeyTile<KVF8>::lane_dim(g) / 8 + (KVF8 ? par : 0)) ^ (c >> 3));
     const __bf16* trow = vt + (4 * g + (c >> 2)) * kVStride +
                          8 * (((c & 3) >> 1) ^ ((g >> 1) & 1)) + 4 * (c & 1);
 
@@ -307,14 +452,14 @@ mla_attn_partial_kernel(const Args a) {
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const bf16x8 kb = to_bf16<KVF8>(kc[j].t[h][s]);
-                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+                const bf16x8 kb = kc[j].t[h].step(s);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + KeyTile<KVF8>::step_dim(s));
                 if (s & 1)
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
                 else
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s0, 0, 0, 0);
                 if (s < kVSteps)
-                    *reinterpret_cast<bf16x8*>(vrow + 32 * s + 8 * (g ^ (c >> 3))) = kb;
+                    *reinterpret_cast<bf16x8*>(vrow + (KeyTile<KVF8>::step_dim(s) & ~15) + vsw[s & 1]) = kb;
             }
             sc2[h] = s0 + s1;
             // This tile's registers are free: the pair kPB ahead streams in.
@@ -369,81 +514,229 @@ mla_attn_partial_kernel(const Args a) {
             if (p0 + j < np) process(j, p0 + j);
     }
 
-    // Merge the four wavefronts: weights 2^(m_w - M) over the workgroup max M.
-    if (g == 0) {
-        mls[0][w][c] = m;
-        mls[1][w][c] = lsum;
+    merge_waves<KVF8, DIRECT, kThreads>(a, o, m, lsum, true, b, split, ht, reinterpret_cast<float*>(smem), mls);
+}
+
+// ---- E4M3 cache: loader and compute wavefronts over an LDS ring -------------
+//
+// With an E4M3 cache a compute wavefront spends most of its time blocked on
+// issuing its own key loads when it is the only wavefront on its SIMD.  Here
+// each SIMD runs one compute wavefront and one loader wavefront.  The loader
+// streams the raw E4M3 key tiles of its compute partner (the same tiles
+// w, w + 4, ... of the range) through registers into a three-slot LDS ring
+// and never computes; the compute wavefront only reads LDS.
+//
+// Ring slot layout: one 16-key tile as 9 blocks of 1 KB; block i holds, at
+// 16 l, the 16 bytes of key c = l % 16 at row bytes 64 i + 16 (l / 16): the
+// loader's lane l writes what its own 16-byte load i returned, and the score
+// step reads it back with the same lane mapping (both 1 KB contiguous).
+// Byte d of key k therefore sits at 256 (d / 16) + 16 k + d % 16.
+//
+// The value product takes one 16-key tile with v_mfma_f32_16x16x16_bf16:
+// lane (c, g) needs dims 16 dt + c of keys 4g .. 4g+3.  One ds_read_b64_tr_b8
+// serves two dim tiles: in each 16-lane group it hands lane j byte j % 8 of
+// the 8-byte chunks of lanes 2e + j / 8 (e = 0..7).  Lane i = c of group g
+// therefore addresses key 4g + (i / 2) % 4 at dims 16 (2dd + i / 8) + 8 (i % 2):
+// lane j receives keys 4g .. 4g+3 at dim 32 dd + j in bytes 0..3 and at dim
+// 32 dd + 16 + j in bytes 4..7.
+//
+// Handshake (LDS counters, one pair per compute wavefront): ready = tiles
+// written, done = tiles consumed.  A tile goes to slot t % 3 once done
+// reaches t - 2.  LDS executes each wavefront's operations in order, so a
+// counter written after the data (or after the reads of a slot) is seen no
+// earlier than them; the explicit lgkmcnt(0) waits make that hold across
+// wavefronts too.
+constexpr int kRingSlots = 3;
+constexpr int kTileBytes = kTile * kRow;                       // 9216 bytes of E4M3
+constexpr int kRingBytes = kWaves * kRingSlots * kTileBytes;   // 110592
+constexpr int kRingThreads = 2 * kThreads;
+static_assert(kWaves * 16 * 64 * 16 <= kRingBytes, "merge buffer inside the ring");
+
+__device__ __forceinline__ int lds_counter(const int* p) {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+
+__device__ __forceinline__ void lds_publish(int* p, int v) {
+    // this wavefront's earlier LDS operations are done (and stay before the store)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Four E4M3 codes -> four bf16 (exact).
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(uint32_t word) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+    return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <bool QF8, bool DIRECT>
+__global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+    __shared__ __attribute__((aligned(16))) __bf16 qlds[16 * kQStride];
+    __shared__ float mls[2][kWaves][16];
+    __shared__ int ready[kWaves], done[kWaves];
+
+    int b, split, ht;
+    decode_wg(a, b, split, ht);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = wave & (kWaves - 1);          // compute wavefront served or run
+    const bool loader = wave >= kWaves;
+    const int c = lane & 15, g = lane >> 4;
+    const int k0 = split * a.keys_per_split;
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    const int k1 = (k0 + a.keys_per_split < L) ? k0 + a.keys_per_split : L;
+    const int first = k0 + kTile * w;
+    const int nt = k1 > first ? (k1 - first + kStepKeys - 1) / kStepKeys : 0;
+    uint8_t* const slots = ring + w * kRingSlots * kTileBytes;
+
+    if (threadIdx.x < kWaves) {
+        ready[threadIdx.x] = 0;
+        done[threadIdx.x] = 0;
     }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-        if (mls[1][v][c] > 0.0f) M = fmaxf(M, mls[0][v][c]);
-    const float own = lsum > 0.0f ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-    // Reducer thread: head rh, value dims 16 rq .. 16 rq + 15 of the pass.
-    const int rh = threadIdx.x >> 4, rq = threadIdx.x & 15;
-    float Ltot = 0.0f, Mh = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        const float lv = mls[1][v][rh];
-        if (lv > 0.0f) Mh = fmaxf(Mh, mls[0][v][rh]);
-    }
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        const float lv = mls[1][v][rh];
-        if (lv > 0.0f) Ltot += lv * __builtin_amdgcn_exp2f(mls[0][v][rh] - Mh);
-    }
-    const bool rh_ok = ht * 16 + rh < a.H;
-    float fin = 1.0f;
-    if constexpr (DIRECT) {
-        fin = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
-        if constexpr (KVF8) fin *= *a.kv_scale;
-    }
-    float* mb = reinterpret_cast<float*>(smem);
-    const size_t p = ((size_t)b * a.H + ht * 16 + rh) * a.splits + split;
-#pragma unroll
-    for (int half = 0; half < kValue / kMergeDims; ++half) {
-        __syncthreads();   // value tiles (or the previous pass) no longer read
-#pragma unroll
-        for (int dt = 0; dt < kMergeDims / 16; ++dt)
-            *reinterpret_cast<f32x4*>(mb + (w * 16 + c) * kMergeStride + 16 * dt + 4 * g) =
-                o[half * (kMergeDims / 16) + dt] * own;
-        __syncthreads();
-        f32x4 acc[4] = {};
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[q] += *reinterpret_cast<const f32x4*>(mb + (v * 16 + rh) * kMergeStride +
-                                                          16 * rq + 4 * q);
+
+    // Loader state.  Its first pages and keys are requested before the
+    // workgroup barrier, while the compute wavefronts stage the queries.
+    // Block-table entries are read at keys clamped to max_seq_len - 1, which
+    // needs no sequence length, so they go out together with the length.
+    // A lane whose key lies past the range's last key reads the tile's first
+    // key instead (lane 0's row and page): still a row of this sequence, so
+    // its data are finite, and its weight is zero.  Tiles past the range
+    // (requested only to keep the loads unconditional, never handed over)
+    // repeat the range's last tile, which is still in cache.
+    const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+    const int last = k1 > 0 ? k1 - 1 : 0;
+    const int kmax = a.max_seq_len > 0 ? a.max_seq_len - 1 : 0;
+    auto in_range = [&](int t) -> int { return t < nt ? t : (nt > 0 ? nt - 1 : 0); };
+    auto page_of = [&](int t) -> int {
+        const int key = first + kStepKeys * in_range(t) + c;
+        return bt[(key < kmax ? key : kmax) / a.block_size];
+    };
+    auto row_of = [&](int t, int page) -> const uint8_t* {
+        t = in_range(t);
+        const int raw = first + kStepKeys * t + c, raw0 = first + kStepKeys * t;
+        const int page0 = __builtin_amdgcn_readlane(page, 0);
+        int key = raw < kmax ? raw : kmax;
+        if (raw > last && raw0 <= last) {
+            key = raw0;
+            page = page0;
         }
-        if (rh_ok) {
-            const int d0 = half * kMergeDims + 16 * rq;
-            if constexpr (DIRECT) {
-                uint16_t* orow = a.out + ((size_t)b * a.H + ht * 16 + rh) * kValue + d0;
-                u32x4 pk[2];
+        page = page < 0 ? 0 : (page >= a.num_blocks ? a.num_blocks - 1 : page);
+        return a.cache + ((size_t)page * a.block_size + key % a.block_size) * kRow;
+    };
+    // Loads are unconditional (tiles past the range read its last key, so
+    // they stay in bounds and hit in cache): with no load on a branch the
+    // compiler's load counters stay exact and it never waits for more
+    // than the data it needs.
+    KeyTile<true> r0, r1;
+    int pga = 0, pgb = 0;
+    if (loader) {
+        pga = page_of(0);
+        pgb = page_of(1);
+        load_tile<true>(r0, row_of(0, pga), g);
+    } else {
+        stage_queries<QF8, kThreads>(a, b, ht, qlds, threadIdx.x);
+    }
+    lds_barrier();
+
+    f32x4 o[kDimTiles];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = acc[q] * fin;
-                    const bf16x2 lo = {(__bf16)v.x, (__bf16)v.y}, hi = {(__bf16)v.z, (__bf16)v.w};
-                    pk[q >> 1][2 * (q & 1)] = __builtin_bit_cast(uint32_t, lo);
-                    pk[q >> 1][2 * (q & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
-                }
-                *reinterpret_cast<u32x4*>(orow) = pk[0];
-                *reinterpret_cast<u32x4*>(orow + 8) = pk[1];
-            } else {
-                float* po = a.part_o + p * kValue + d0;
+    for (int dt = 0; dt < kDimTiles; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.0f;
+
+    if (loader) {
+        auto put = [&](int u, const KeyTile<true>& cur) {
+            while (lds_counter(&done[w]) < u - (kRingSlots - 1)) __builtin_amdgcn_s_sleep(1);
+            asm volatile("" ::: "memory");
+            uint8_t* dst = slots + (u % kRingSlots) * kTileBytes + 16 * lane;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(po + 4 * q) = acc[q];
+            for (int i = 0; i < KeyTile<true>::kLoads; ++i)
+                *reinterpret_cast<u32x4*>(dst + 1024 * i) = cur.r[i];
+            lds_publish(&ready[w], u + 1);
+        };
+        for (int u = 0; u < nt; u += 2) {
+            // tile u is in r0; tile u + 1 streams into r1, page u + 2 into pga
+            pga = page_of(u + 2);
+            load_tile<true>(r1, row_of(u + 1, pgb), g);
+            put(u, r0);
+            // tile u + 1 is in r1; tile u + 2 streams into r0, page u + 3 into pgb
+            pgb = page_of(u + 3);
+            load_tile<true>(r0, row_of(u + 2, pga), g);
+            if (u + 1 < nt) put(u + 1, r1);
+        }
+    } else {
+        float sc = a.score_scale * *a.kv_scale;
+        if constexpr (QF8) sc *= *a.q_scale;
+        const __bf16* qrow = qlds + c * kQStride + 16 * g;
+        const int vlane = 256 * (c >> 3) + 64 * g + 8 * (c & 7);
+        for (int t = 0; t < nt; ++t) {
+            while (lds_counter(&ready[w]) <= t) __builtin_amdgcn_s_sleep(1);
+            asm volatile("" ::: "memory");
+            const uint8_t* base = slots + (t % kRingSlots) * kTileBytes;
+            // All of the tile's LDS reads go out first (keys for the scores,
+            // transposed values for the value product), so their latency
+            // overlaps instead of stalling each product in turn.
+            typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+            u32x4 kraw[kSteps / 2];
+            i32x2 vraw[kDimTiles / 2];
+#pragma unroll
+            for (int i = 0; i < kSteps / 2; ++i)
+                kraw[i] = *reinterpret_cast<const u32x4*>(base + 1024 * i + 16 * lane);
+#pragma unroll
+            for (int dd = 0; dd < kDimTiles / 2; ++dd)
+                vraw[dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + vlane + 512 * dd));
+            __builtin_amdgcn_sched_barrier(0);
+            // scores: S^T = K Q^T over 18 steps of 32 dims
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kSteps / 2; ++i) {
+                const u32x4 raw = kraw[i];
+                const bf16x8 ka = e4m3x8_to_bf16(u32x2{raw[0], raw[1]});
+                const bf16x8 kb = e4m3x8_to_bf16(u32x2{raw[2], raw[3]});
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 64 * i);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 64 * i + 8);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qa, s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
             }
+            const f32x4 st = s0 + s1;
+            const int key0 = first + kStepKeys * t + 4 * g;
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = key0 + i < k1 ? st[i] * sc : -INFINITY;
+            float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            tm = max_rows(tm);
+            if (__builtin_amdgcn_ballot_w64(tm > m + kRebase) != 0) {
+                const float mn = tm > m + kRebase ? tm : m;
+                const float alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+                for (int dt = 0; dt < kDimTiles; ++dt) o[dt] *= alpha;
+                lsum *= alpha;
+                m = mn;
+            }
+            float ps = 0.0f;
+            bf16x4 pb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(sv[e] - m);
+                ps += pe;
+                pb[e] = (__bf16)pe;
+            }
+            lsum += sum_rows(ps);
+            // values: O^T += V^T P^T, two dim tiles per transpose load
+#pragma unroll
+            for (int dd = 0; dd < kDimTiles / 2; ++dd) {
+                const i32x2 v = vraw[dd];
+                o[2 * dd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[0])), pb,
+                                                                      o[2 * dd], 0, 0, 0);
+                o[2 * dd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[1])), pb,
+                                                                          o[2 * dd + 1], 0, 0, 0);
+            }
+            lds_publish(&done[w], t + 1);
         }
     }
-    if constexpr (!DIRECT) {
-        if (rh_ok && rq == 0) {
-            a.part_m[p] = Mh;
-            a.part_l[p] = Ltot;
-        }
-    }
+
+    merge_waves<true, DIRECT, kRingThreads>(a, o, m, lsum, !loader, b, split, ht, reinterpret_cast<float*>(ring), mls);
 }
 
 // Merge the key ranges of one (sequence, head): four wavefronts, each lane
@@ -596,7 +889,7 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
     p->workspace_bytes = p->combine ? d->batch * d->num_heads * splits * (kValue + 2) * 4 : 0;
     p->target_workgroups = target;
     p->xcd_remap = (head_tiles > 1 && p->workgroups % 8 == 0) ? 1 : 0;
-    p->block_threads = kThreads;
+    p->block_threads = (flags & MLA_ATTN_KV_FP8) ? kRingThreads : kThreads;
     return MLA_DQ_OK;
 }
 
@@ -604,12 +897,20 @@ bool aligned(const void* x, uintptr_t n) { return (reinterpret_cast<uintptr_t>(x
 
 template <bool QF8, bool KVF8>
 hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream) {
-    const dim3 grid(uint32_t(p.workgroups)), block(kThreads);
-    if (!p.combine) {
-        hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, KVF8, true>), grid, block, 0, stream, a);
-        return hipGetLastError();
+    const dim3 grid(uint32_t(p.workgroups)), block(uint32_t(p.block_threads));
+    if constexpr (KVF8) {
+        if (!p.combine) {
+            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, true>), grid, block, 0, stream, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false>), grid, block, 0, stream, a);
+    } else {
+        if (!p.combine) {
+            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, true>), grid, block, 0, stream, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, false>), grid, block, 0, stream, a);
     }
-    hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, KVF8, false>), grid, block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3(uint32_t(a.B * a.H)),
