@@ -597,38 +597,30 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
     }
 
     // Loader state.  Its first pages and keys are requested before the
-    // workgroup barrier, while the compute wavefronts stage the queries.
-    // Block-table entries are read at keys clamped to max_seq_len - 1, which
-    // needs no sequence length, so they go out together with the length.
-    // A lane whose key lies past the range's last key reads the tile's first
-    // key instead (lane 0's row and page): still a row of this sequence, so
-    // its data are finite, and its weight is zero.  Tiles past the range
-    // (requested only to keep the loads unconditional, never handed over)
-    // repeat the range's last tile, which is still in cache.
+    // workgroup barrier, while the compute wavefronts stage the queries, and
+    // before the sequence length is known: keys are clamped to
+    // max_seq_len - 1 only, so every block-table entry and row read stays in
+    // bounds.  Rows of keys past the range may hold anything (NaN included);
+    // the loader writes zeros for them into the ring (only the range's last
+    // tile has such keys), so a zero weight always meets finite data.  Tiles
+    // from 2 on that lie past the range (requested only to keep the loads
+    // unconditional, never handed over) repeat the range's last tile, which
+    // is still in cache.
     const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
     const int last = k1 > 0 ? k1 - 1 : 0;
     const int kmax = a.max_seq_len > 0 ? a.max_seq_len - 1 : 0;
-    auto in_range = [&](int t) -> int { return t < nt ? t : (nt > 0 ? nt - 1 : 0); };
-    auto page_of = [&](int t) -> int {
-        const int key = first + kStepKeys * in_range(t) + c;
-        return bt[(key < kmax ? key : kmax) / a.block_size];
+    auto tile_at = [&](int t) -> int { return t < 2 || t < nt ? t : (nt > 0 ? nt - 1 : 0); };
+    auto key_of = [&](int t) -> int {
+        const int key = first + kStepKeys * tile_at(t) + c;
+        return key < kmax ? key : kmax;
     };
+    auto page_of = [&](int t) -> int { return bt[key_of(t) / a.block_size]; };
     auto row_of = [&](int t, int page) -> const uint8_t* {
-        t = in_range(t);
-        const int raw = first + kStepKeys * t + c, raw0 = first + kStepKeys * t;
-        const int page0 = __builtin_amdgcn_readlane(page, 0);
-        int key = raw < kmax ? raw : kmax;
-        if (raw > last && raw0 <= last) {
-            key = raw0;
-            page = page0;
-        }
         page = page < 0 ? 0 : (page >= a.num_blocks ? a.num_blocks - 1 : page);
-        return a.cache + ((size_t)page * a.block_size + key % a.block_size) * kRow;
+        return a.cache + ((size_t)page * a.block_size + key_of(t) % a.block_size) * kRow;
     };
-    // Loads are unconditional (tiles past the range read its last key, so
-    // they stay in bounds and hit in cache): with no load on a branch the
-    // compiler's load counters stay exact and it never waits for more
-    // than the data it needs.
+    // Loads are unconditional: with no load on a branch the compiler's load
+    // counters stay exact and it never waits for more than the data it needs.
     KeyTile<true> r0, r1;
     int pga = 0, pgb = 0;
     if (loader) {
@@ -650,9 +642,10 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
             while (lds_counter(&done[w]) < u - (kRingSlots - 1)) __builtin_amdgcn_s_sleep(1);
             asm volatile("" ::: "memory");
             uint8_t* dst = slots + (u % kRingSlots) * kTileBytes + 16 * lane;
+            const bool past = first + kStepKeys * u + c > last;   // key past the range
 #pragma unroll
             for (int i = 0; i < KeyTile<true>::kLoads; ++i)
-                *reinterpret_cast<u32x4*>(dst + 1024 * i) = cur.r[i];
+                *reinterpret_cast<u32x4*>(dst + 1024 * i) = past ? u32x4{0u, 0u, 0u, 0u} : cur.r[i];
             lds_publish(&ready[w], u + 1);
         };
         for (int u = 0; u < nt; u += 2) {
@@ -739,83 +732,53 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
     merge_waves<true, DIRECT, kRingThreads>(a, o, m, lsum, !loader, b, split, ht, reinterpret_cast<float*>(ring), mls);
 }
 
-// Merge the key ranges of one (sequence, head): four wavefronts, each lane
-// 8 value dimensions of every fourth range.  The threads turn the ranges'
-// (max, sum) pairs into weights (zero for ranges without keys) in LDS, sum
-// their share of the weighted partial outputs with independent loads, and
-// wavefront 0 adds the other three sums.
+// Merge the key ranges of one (sequence, head): one wavefront, lane l owns
+// value dims 8l .. 8l+7.  Ranges go eight at a time; the partial outputs,
+// maxima and sums of a group are all requested before any is used, so a
+// sequence split into at most eight ranges costs one memory round trip.
+// A running maximum rescales what is already summed when a later group
+// raises it (ranges without keys weigh zero).
 constexpr int kCombineThreads = 256;
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) v = fmaxf(v, xor_lanes(v, k));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return v;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) v += xor_lanes(v, k);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    return v;
-}
+constexpr int kCombineGroup = 8;
 
 template <bool KVF8>
 __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
-    __shared__ float wts[kMaxSplits];
-    __shared__ float red[4];
-    __shared__ f32x4 part[3][64][2];
-    const int bh = blockIdx.x;              // b * H + h
-    const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);   // b * H + h
+    if (bh >= a.B * a.H) return;
     const size_t p0 = (size_t)bh * a.splits;
-    float mx = -INFINITY;
-    for (int s = threadIdx.x; s < a.splits; s += kCombineThreads)
-        if (a.part_l[p0 + s] > 0.0f) mx = fmaxf(mx, a.part_m[p0 + s]);
-    mx = block_max(mx, red);
-    float den = 0.0f;
-    for (int s = threadIdx.x; s < a.splits; s += kCombineThreads) {
-        const float l = a.part_l[p0 + s];
-        const float wgt = l > 0.0f ? __builtin_amdgcn_exp2f(a.part_m[p0 + s] - mx) : 0.0f;
-        wts[s] = wgt;
-        den += wgt * l;
-    }
-    den = block_sum(den, red);   // its barrier also publishes wts
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     const float* po = a.part_o + p0 * kValue + 8 * lane;
-    int s = grp;
-    for (; s + 12 < a.splits; s += 16) {
-        f32x4 v[8];
+    float M = -INFINITY, den = 0.0f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.splits; s0 += kCombineGroup) {
+        f32x4 v[2 * kCombineGroup];
+        float ms[kCombineGroup], ls[kCombineGroup];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + 4 * u) * kValue);
-            v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)(s + 4 * u) * kValue + 4);
+        for (int u = 0; u < kCombineGroup; ++u) {
+            const int s = s0 + u < a.splits ? s0 + u : a.splits - 1;
+            v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue);
+            v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
+            ms[u] = a.part_m[p0 + s];
+            ls[u] = s0 + u < a.splits ? a.part_l[p0 + s] : 0.0f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < kCombineGroup; ++u)
+            if (ls[u] > 0.0f) Mn = fmaxf(Mn, ms[u]);
+        if (Mn > M) {   // uniform: every lane reads the same maxima
+            const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+            acc0 *= r;
+            acc1 *= r;
+            den *= r;
+            M = Mn;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc0 += wts[s + 4 * u] * v[2 * u];
-            acc1 += wts[s + 4 * u] * v[2 * u + 1];
+        for (int u = 0; u < kCombineGroup; ++u) {
+            const float wgt = ls[u] > 0.0f ? __builtin_amdgcn_exp2f(ms[u] - M) : 0.0f;
+            acc0 += wgt * v[2 * u];
+            acc1 += wgt * v[2 * u + 1];
+            den += wgt * ls[u];
         }
-    }
-    for (; s < a.splits; s += 4) {
-        acc0 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue);
-        acc1 += wts[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
-    }
-    if (grp > 0) {
-        part[grp - 1][lane][0] = acc0;
-        part[grp - 1][lane][1] = acc1;
-    }
-    __syncthreads();
-    if (grp > 0) return;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        acc0 += part[k][lane][0];
-        acc1 += part[k][lane][1];
     }
     float f = den > 0.0f ? 1.0f / den : 0.0f;
     if constexpr (KVF8) f *= *a.kv_scale;
@@ -913,7 +876,8 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3(uint32_t(a.B * a.H)),
+    const uint32_t heads = uint32_t(a.B * a.H), per_block = kCombineThreads / 64;
+    hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3((heads + per_block - 1) / per_block),
                        dim3(kCombineThreads), 0, stream, a);
     return hipGetLastError();
 }
