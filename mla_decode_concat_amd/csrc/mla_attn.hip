@@ -732,38 +732,34 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
     merge_waves<true, DIRECT, kRingThreads>(a, o, m, lsum, !loader, b, split, ht, reinterpret_cast<float*>(ring), mls);
 }
 
-// Merge the key ranges of one (sequence, head): one wavefront, lane l owns
-// value dims 8l .. 8l+7.  Ranges go eight at a time; the partial outputs,
-// maxima and sums of a group are all requested before any is used, so a
-// sequence split into at most eight ranges costs one memory round trip.
-// A running maximum rescales what is already summed when a later group
-// raises it (ranges without keys weigh zero).
+// Merge the key ranges of one (sequence, head).  A wavefront's lane l owns
+// value dims 8l .. 8l+7.  Ranges go G at a time (G = 4, 8 or 16); the
+// partial outputs, maxima and sums of a group are all requested before any
+// is used, so a group costs one memory round trip.  A running maximum
+// rescales what is already summed when a later group raises it (ranges
+// without keys weigh zero).
 constexpr int kCombineThreads = 256;
-constexpr int kCombineGroup = 8;
 
-template <bool KVF8>
-__global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
-    const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);   // b * H + h
-    if (bh >= a.B * a.H) return;
-    const size_t p0 = (size_t)bh * a.splits;
+// Ranges [s_begin, s_end) of one (sequence, head) into one wavefront's
+// running (max M, weight sum den, weighted output acc over dims 8l .. 8l+7).
+template <int G>
+__device__ __forceinline__ void combine_ranges(const Args& a, size_t p0, int s_begin, int s_end, int lane,
+                                               float& M, float& den, f32x4& acc0, f32x4& acc1) {
     const float* po = a.part_o + p0 * kValue + 8 * lane;
-    float M = -INFINITY, den = 0.0f;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.splits; s0 += kCombineGroup) {
-        f32x4 v[2 * kCombineGroup];
-        float ms[kCombineGroup], ls[kCombineGroup];
+    for (int s0 = s_begin; s0 < s_end; s0 += G) {
+        f32x4 v[2 * G];
+        float ms[G], ls[G];
 #pragma unroll
-        for (int u = 0; u < kCombineGroup; ++u) {
-            const int s = s0 + u < a.splits ? s0 + u : a.splits - 1;
+        for (int u = 0; u < G; ++u) {
+            const int s = s0 + u < s_end ? s0 + u : s_end - 1;
             v[2 * u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue);
             v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
             ms[u] = a.part_m[p0 + s];
-            ls[u] = s0 + u < a.splits ? a.part_l[p0 + s] : 0.0f;
+            ls[u] = s0 + u < s_end ? a.part_l[p0 + s] : 0.0f;
         }
         float Mn = M;
 #pragma unroll
-        for (int u = 0; u < kCombineGroup; ++u)
+        for (int u = 0; u < G; ++u)
             if (ls[u] > 0.0f) Mn = fmaxf(Mn, ms[u]);
         if (Mn > M) {   // uniform: every lane reads the same maxima
             const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
@@ -773,13 +769,17 @@ __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const
             M = Mn;
         }
 #pragma unroll
-        for (int u = 0; u < kCombineGroup; ++u) {
+        for (int u = 0; u < G; ++u) {
             const float wgt = ls[u] > 0.0f ? __builtin_amdgcn_exp2f(ms[u] - M) : 0.0f;
             acc0 += wgt * v[2 * u];
             acc1 += wgt * v[2 * u + 1];
             den += wgt * ls[u];
         }
     }
+}
+
+template <bool KVF8>
+__device__ __forceinline__ void combine_write(const Args& a, int bh, int lane, float den, f32x4 acc0, f32x4 acc1) {
     float f = den > 0.0f ? 1.0f / den : 0.0f;
     if constexpr (KVF8) f *= *a.kv_scale;
     uint16_t r[8];
@@ -792,6 +792,59 @@ __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const
 #pragma unroll
     for (int k = 0; k < 4; ++k) packed[k] = uint32_t(r[2 * k]) | (uint32_t(r[2 * k + 1]) << 16);
     *reinterpret_cast<u32x4*>(a.out + (size_t)bh * kValue + 8 * lane) = packed;
+}
+
+// Up to sixteen ranges: one wavefront per (sequence, head), four per workgroup.
+template <bool KVF8, int G>
+__global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);   // b * H + h
+    if (bh >= a.B * a.H) return;
+    float M = -INFINITY, den = 0.0f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    combine_ranges<G>(a, (size_t)bh * a.splits, 0, a.splits, lane, M, den, acc0, acc1);
+    combine_write<KVF8>(a, bh, lane, den, acc0, acc1);
+}
+
+// More ranges: one workgroup per (sequence, head); its four wavefronts take
+// a quarter of the ranges each and meet once in LDS.
+template <bool KVF8>
+__global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_wide_kernel(const Args a) {
+    __shared__ f32x4 part[kCombineThreads / 64][64][2];
+    __shared__ float pm[kCombineThreads / 64][2];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int bh = blockIdx.x;
+    const int per = (a.splits + 3) / 4;
+    const int sb = w * per < a.splits ? w * per : a.splits;
+    const int se = sb + per < a.splits ? sb + per : a.splits;
+    float M = -INFINITY, den = 0.0f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (per <= 8)
+        combine_ranges<8>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1);
+    else
+        combine_ranges<16>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1);
+    part[w][lane][0] = acc0;
+    part[w][lane][1] = acc1;
+    if (lane == 0) {
+        pm[w][0] = M;
+        pm[w][1] = den;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kCombineThreads / 64; ++v)
+        if (pm[v][1] > 0.0f) Mt = fmaxf(Mt, pm[v][0]);
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    float dt = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kCombineThreads / 64; ++v) {
+        const float wgt = pm[v][1] > 0.0f ? __builtin_amdgcn_exp2f(pm[v][0] - Mt) : 0.0f;
+        t0 += wgt * part[v][lane][0];
+        t1 += wgt * part[v][lane][1];
+        dt += wgt * pm[v][1];
+    }
+    combine_write<KVF8>(a, bh, lane, dt, t0, t1);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -877,8 +930,15 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const uint32_t heads = uint32_t(a.B * a.H), per_block = kCombineThreads / 64;
-    hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8>), dim3((heads + per_block - 1) / per_block),
-                       dim3(kCombineThreads), 0, stream, a);
+    const dim3 cgrid((heads + per_block - 1) / per_block), cblock(kCombineThreads);
+    if (a.splits <= 4)
+        hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8, 4>), cgrid, cblock, 0, stream, a);
+    else if (a.splits <= 8)
+        hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8, 8>), cgrid, cblock, 0, stream, a);
+    else if (a.splits <= 16)
+        hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8, 16>), cgrid, cblock, 0, stream, a);
+    else
+        hipLaunchKernelGGL((mla_attn_combine_wide_kernel<KVF8>), dim3(heads), cblock, 0, stream, a);
     return hipGetLastError();
 }
 

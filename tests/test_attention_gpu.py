@@ -145,6 +145,20 @@ def test_block_sizes(block_size):
     check(w, f"block_size={block_size}")
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True])
+@pytest.mark.parametrize("lengths", [(8192, 3000), (2048,), (1500, 40, 0)])
+def test_range_merge_group_sizes(lengths, kv_fp8):
+    """Few sequences split into many ranges: 64 ranges (four wavefronts
+    share a head's ranges and meet in LDS), 16 and 12 ranges (one wavefront
+    takes them in one group); short and empty sequences leave whole ranges
+    without keys."""
+    w = I.attn_custom(len(lengths), 16, lengths, kv_fp8=kv_fp8, name=f"ranges{len(lengths)}")
+    plan = M.attn_plan(M.AttnDims(w.batch, w.heads, w.num_blocks, w.block_size, w.max_blocks,
+                                  w.max_blocks * w.block_size), M.ATTN_KV_FP8 if kv_fp8 else 0)
+    assert plan.splits == {2: 64, 1: 16, 3: 12}[len(lengths)]
+    check(w, f"ranges lengths={lengths} kv_fp8={kv_fp8} splits={plan.splits}")
+
+
 def test_single_range_writes_output_directly():
     """Enough (sequence, head tile) pairs that each sequence is one range:
     the partial kernel normalises and writes bf16 itself (no combine)."""
