@@ -81,9 +81,8 @@ constexpr int kWaveTile = 2 * kTile * kVStride;       // bf16 elements per wavef
 // bf16 elements per LDS row of the query tile: 576 + 8 of padding keeps the
 // 16 rows one instruction reads on disjoint banks.
 constexpr int kQStride = kRow + 8;
-constexpr int kMergeDims = 256;                       // value dims merged per pass
 constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merge buffer too
-static_assert(kWaves * 16 * 64 * 16 <= kLdsBytes, "merge buffer");
+static_assert(kWaves * 24 * 64 * 16 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
 constexpr int kMinSplitSteps = 2;              // 64-key rounds per range, at least
@@ -280,15 +279,19 @@ __device__ __forceinline__ void lds_barrier() {
 // weights 2^(m_w - M) over the workgroup max M, then write the range's result:
 // bf16 output when the range is the whole sequence, else the unnormalised
 // output with its max and sum.  Threads 0..255 are the compute wavefronts;
-// all NT threads of the workgroup share the reduction.  Two passes of 256
-// value dims: wavefront w stores its 16 accumulator tiles lane-major
-// (tile j, lane l at 16 B * (64 (16 w + j) + l)), so every store and every
-// reducer load of an instruction covers 1 KB of consecutive LDS.  mb is LDS
-// scratch of at least 64 KB that no wavefront reads any more.
+// the others only pass the barriers.  One pass: compute wavefront w owns
+// value-dim tiles 8w .. 8w+7 (dims 128w .. 128w+127).  It stores the other
+// 24 of its 32 accumulator tiles to LDS, lane-major (tile slot k of wave v,
+// lane l at 16 B * (64 (24 v + k) + l), so every store and load instruction
+// covers 1 KB of consecutive LDS), and sums its own tiles from registers with
+// the three others' from LDS.  mb is LDS scratch of at least 96 KB that no
+// wavefront reads any more.
 template <bool KVF8, bool DIRECT, int NT>
 __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDimTiles], float m, float lsum,
                                             bool compute, int b, int split, int ht, float* mb,
                                             float (&mls)[2][kWaves][16]) {
+    constexpr int kOwn = kDimTiles / kWaves;                  // 8 tiles per wavefront
+    constexpr int kShared = kDimTiles - kOwn;                 // 24 tiles stored to LDS
     const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
     const int w = (threadIdx.x >> 6) & (kWaves - 1);
     if (compute && g == 0) {
@@ -301,49 +304,51 @@ __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDim
     for (int v = 0; v < kWaves; ++v)
         if (mls[1][v][c] > 0.0f) M = fmaxf(M, mls[0][v][c]);
     const float own = lsum > 0.0f ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-    // Every reducer item of a thread belongs to head c (items step by NT, a
-    // multiple of 64); its total weight and, with one range, 1 / sum.
     float Ltot = 0.0f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
         const float lv = mls[1][v][c];
         if (lv > 0.0f) Ltot += lv * __builtin_amdgcn_exp2f(mls[0][v][c] - M);
     }
+    f32x4* lm = reinterpret_cast<f32x4*>(mb);
+    if (compute) {
+#pragma unroll
+        for (int j = 0; j < kDimTiles; ++j) {
+            if (j / kOwn != w) {
+                const int k = j < kOwn * w ? j : j - kOwn;
+                lm[64 * (kShared * w + k) + lane] = o[j] * own;
+            }
+        }
+    }
+    lds_barrier();
+    if (!compute) return;
     const bool head_ok = ht * 16 + c < a.H;
     float fin = 1.0f;
     if constexpr (DIRECT) {
         fin = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
         if constexpr (KVF8) fin *= *a.kv_scale;
     }
-    const size_t row = (size_t)b * a.H + ht * 16 + c;       // (sequence, head) of this thread's items
+    const size_t row = (size_t)b * a.H + ht * 16 + c;       // (sequence, head) of this lane
     const size_t p = row * a.splits + split;
-    f32x4* lm = reinterpret_cast<f32x4*>(mb);
 #pragma unroll
-    for (int half = 0; half < kValue / kMergeDims; ++half) {
-        lds_barrier();   // LDS tiles (or the previous pass) no longer read
-        if (compute) {
+    for (int j = 0; j < kDimTiles; ++j) {
+        if (j / kOwn != w) continue;
+        f32x4 acc = o[j] * own;
 #pragma unroll
-            for (int j = 0; j < kMergeDims / 16; ++j)
-                lm[64 * (16 * w + j) + lane] = o[half * (kMergeDims / 16) + j] * own;
+        for (int v = 0; v < kWaves; ++v) {
+            if (v == w) continue;
+            const int k = j < kOwn * v ? j : j - kOwn;
+            acc += lm[64 * (kShared * v + k) + lane];
         }
-        lds_barrier();
-#pragma unroll
-        for (int it = 0; it < (16 * 64) / NT; ++it) {
-            const int item = threadIdx.x + NT * it;              // (tile j, lane): lane == this lane
-            const int j = item >> 6;
-            f32x4 acc = lm[64 * j + lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) acc += lm[64 * (16 * v + j) + lane];
-            if (head_ok) {
-                const int d0 = 16 * (half * (kMergeDims / 16) + j) + 4 * g;
-                if constexpr (DIRECT) {
-                    const f32x4 r = acc * fin;
-                    const bf16x2 lo = {(__bf16)r.x, (__bf16)r.y}, hi = {(__bf16)r.z, (__bf16)r.w};
-                    *reinterpret_cast<u32x2*>(a.out + row * kValue + d0) =
-                        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-                } else {
-                    *reinterpret_cast<f32x4*>(a.part_o + p * kValue + d0) = acc;
-                }
+        if (head_ok) {
+            const int d0 = 16 * j + 4 * g;
+            if constexpr (DIRECT) {
+                const f32x4 r = acc * fin;
+                const bf16x2 lo = {(__bf16)r.x, (__bf16)r.y}, hi = {(__bf16)r.z, (__bf16)r.w};
+                *reinterpret_cast<u32x2*>(a.out + row * kValue + d0) =
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            } else {
+                *reinterpret_cast<f32x4*>(a.part_o + p * kValue + d0) = acc;
             }
         }
     }
@@ -550,7 +555,7 @@ constexpr int kRingSlots = 3;
 constexpr int kTileBytes = kTile * kRow;                       // 9216 bytes of E4M3
 constexpr int kRingBytes = kWaves * kRingSlots * kTileBytes;   // 110592
 constexpr int kRingThreads = 2 * kThreads;
-static_assert(kWaves * 16 * 64 * 16 <= kRingBytes, "merge buffer inside the ring");
+static_assert(kWaves * 24 * 64 * 16 <= kRingBytes, "merge buffer inside the ring");
 
 __device__ __forceinline__ int lds_counter(const int* p) {
     return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
