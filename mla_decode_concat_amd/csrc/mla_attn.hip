@@ -16,12 +16,12 @@
 //  * scores on the matrix cores, transposed: S^T[key][head] = K Q^T with
 //    v_mfma_f32_16x16x32_bf16 over 18 steps of 32 of the 576 dimensions.
 //    Lane l loads 16 bytes of key c per instruction: bf16 dimensions
-//    32s + 8g .. +7 for step s, or E4M3 dimensions 64i + 16g .. +15, which
-//    feed steps 2i (first eight) and 2i + 1 (last eight).  The sum over the
-//    576 dimensions does not care how they are dealt to steps and K slots,
-//    so operand B is head c's query at the same dimensions, read from the
-//    workgroup's query tile in LDS.  The result leaves lane l with head c's
-//    scores for keys 4g .. 4g+3 of the tile.
+//    32s + 8g .. +7 for step s (the E4M3 kernel: dimensions 64i + 16g .. +15,
+//    which feed steps 2i (first eight) and 2i + 1 (last eight); the sum over
+//    the 576 dimensions does not care how they are dealt to steps and K
+//    slots).  Operand B is head c's query at the same dimensions, read from
+//    the workgroup's query tile in LDS.  The result leaves lane l with head
+//    c's scores for keys 4g .. 4g+3 of the tile.
 //  * each tile's value part (first 512 elements) goes, as bf16, to a
 //    wavefront-private LDS tile in the cache's row-major layout, and the
 //    tile's registers reload with the next pair's keys.
@@ -37,9 +37,10 @@
 //    of the four rows the group's lanes address (lane i: row i / 4,
 //    columns 4(i % 4) .. +3).
 //
-// E4M3 operands convert exactly to bf16 (3 mantissa bits, two values per
-// v_cvt_scalef32_pk_bf16_fp8 with scale 1); their scales are
-// applied in fp32 to the scores and to the result.  With one range per
+// E4M3 operands (queries in both kernels, keys and values in the ring
+// kernel) convert exactly to bf16 (3 mantissa bits, two values per
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1); their scales are applied in
+// fp32 to the scores and to the result.  With one range per
 // sequence the workgroup writes the bf16 output itself; otherwise it writes
 // (max, sum, unnormalised output) to the workspace and a second kernel merges
 // the ranges.
@@ -360,9 +361,10 @@ __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDim
     }
 }
 
-template <bool QF8, bool KVF8, bool DIRECT>
+template <bool QF8, bool DIRECT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_attn_partial_kernel(const Args a) {
+    constexpr bool KVF8 = false;   // bf16 cache (E4M3 caches go to mla_attn_ring_kernel)
     // Pairs of key tiles held in registers per wavefront.  Each tile of the
     // pair reloads (with the pair kPB ahead) as soon as its scores and value
     // rows are out of its registers.  More pairs in flight make the compiler
@@ -927,10 +929,10 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
         hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false>), grid, block, 0, stream, a);
     } else {
         if (!p.combine) {
-            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, true>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false>), grid, block, 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
