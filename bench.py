@@ -483,6 +483,30 @@ def cpu_baseline(w: I.Workload, host: dict, budget_s: float) -> dict:
                               "sample": f"{runs1} calls, {dt1 * 1e3:.1f} ms per call"}}
 
 
+def copy_reference(dev: str, moved_bytes: int, calls: int = 50) -> dict:
+    """The runtime's own device copy (torch copy_, a blit kernel) moving the
+    same number of bytes as one headline call (half read, half written), on
+    four rotating buffer pairs like the headline: a practical HBM ceiling for
+    a read+write stream on this GPU, measured beside the epilogue."""
+    n = (moved_bytes // 2) // 4096 * 4096
+    pairs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(n, dtype=torch.uint8, device=dev)) for _ in range(4)]
+    for i in range(8):
+        pairs[i % 4][1].copy_(pairs[i % 4][0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        pairs[i % 4][1].copy_(pairs[i % 4][0])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    del pairs
+    torch.cuda.empty_cache()
+    return {"what": "torch copy_ of the same bytes (runtime blit kernel), 4 rotating pairs",
+            "bytes_moved": 2 * n, "us_per_call": round(us, 3), "gbs": round(2 * n / us / 1e3, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,6 +622,8 @@ def main() -> int:
             del vsets
             torch.cuda.empty_cache()
 
+    ref_copy = copy_reference(dev, nbytes)
+    log(f"reference copy: {ref_copy}")
     decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
     attention = {} if args.no_attention else attention_timings(
         dev, args.steps, 0.0 if args.no_cpu_baseline else 3.0)
@@ -625,6 +651,7 @@ def main() -> int:
                    "grid_blocks": pl.grid_blocks, "block_threads": pl.block_threads,
                    "rows_per_wave": pl.rows_per_wave, "tail_steps": pl.tail_steps},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "reference_copy": ref_copy,
         "latency_us": latency,
         "variants_at_headline_shape": variants,
         "decode_step_slice_graph": decode_slice,
