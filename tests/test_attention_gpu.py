@@ -159,6 +159,27 @@ def test_range_merge_group_sizes(lengths, kv_fp8):
     check(w, f"ranges lengths={lengths} kv_fp8={kv_fp8} splits={plan.splits}")
 
 
+def _random_shape(case: int):
+    """A seeded random (batch, heads, lengths, block size, precisions) case:
+    lengths mix empty, sub-tile, page-crossing and multi-range sequences."""
+    r = np.random.default_rng(1000 + case)
+    batch = int(r.integers(1, 7))
+    heads = int(r.choice([1, 3, 16, 20, 33]))
+    block_size = int(r.choice([1, 7, 16, 64, 96]))
+    lengths = tuple(int(x) for x in r.choice([0, 1, 5, 16, 17, 63, 64, 65, 130, 257, 700, 1500], batch))
+    q_fp8, kv_fp8 = bool(r.integers(0, 2)), bool(r.integers(0, 2))
+    return batch, heads, lengths, block_size, q_fp8, kv_fp8
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_shapes(case):
+    batch, heads, lengths, block_size, q_fp8, kv_fp8 = _random_shape(case)
+    w = I.attn_custom(batch, heads, lengths, block_size=block_size, q_fp8=q_fp8, kv_fp8=kv_fp8,
+                      name=f"random{case}")
+    check(w, f"random case {case}: B={batch} H={heads} bs={block_size} L={lengths} "
+             f"q_fp8={q_fp8} kv_fp8={kv_fp8}", seed=50 + case)
+
+
 def test_single_range_writes_output_directly():
     """Enough (sequence, head tile) pairs that each sequence is one range:
     the partial kernel normalises and writes bf16 itself (no combine)."""
