@@ -577,6 +577,10 @@ def main() -> int:
 
     latency = {}
     if not args.no_latency:
+        # launch floor: the same graph replay of a kernel that writes 4 bytes
+        tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+        latency["graph_floor_one_element_fill"] = {"us_per_call_graph": round(time_graph_fn(lambda: tiny.fill_(1.0), calls=100), 3)}
+        log(f"graph floor (one-element fill): {latency['graph_floor_one_element_fill']}")
         for name in LATENCY:
             lw = I.WORKLOADS[name]
             lh = I.make_inputs(lw)
