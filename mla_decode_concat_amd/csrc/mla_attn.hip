@@ -172,10 +172,6 @@ struct KeyTile {
     static constexpr int step_dim(int s) { return FP8 ? 64 * (s >> 1) + 8 * (s & 1) : 32 * s; }
 };
 
-__device__ __forceinline__ float xor_lanes(float v, int mask) {
-    return __shfl_xor(v, mask, 64);
-}
-
 // Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane
 // row): v_permlane16_swap and v_permlane32_swap hand each lane its partner
 // row's value without going through LDS.
@@ -871,7 +867,7 @@ int check_dims(const mla_attn_dims* d, uint32_t flags) {
     return MLA_DQ_OK;
 }
 
-// Workgroups the key split aims for (two resident per CU); the environment
+// Workgroups the key split aims for (one resident per CU); the environment
 // variable MLA_ATTN_TARGET_WGS overrides it (read once per process).
 int64_t target_workgroups() {
     static const int64_t v = [] {
