@@ -235,32 +235,45 @@ struct PairRegs {
 // The workgroup's 16 query rows (heads 16 ht .. 16 ht + 15 of sequence b) as
 // bf16 in LDS, row stride kQStride; rows for heads past H are zero.  The NT
 // staging threads first issue all their loads (unconditionally, at clamped
-// rows) and only then write, so the loads share one memory latency.
+// rows) and only then write, so the loads share one memory latency; a
+// kernel may issue other loads between the two halves.
 template <bool QF8, int NT>
-__device__ __forceinline__ void stage_queries(const Args& a, int b, int ht, __bf16* qlds, int tid) {
-    constexpr int kChunks = 16 * (kRow / 8);   // 8-element chunks of the tile
-    constexpr int kIter = (kChunks + NT - 1) / NT;
-    const size_t q_row_bytes = (size_t)kRow * (QF8 ? 1 : 2);
+struct QueryStage {
+    static constexpr int kChunks = 16 * (kRow / 8);   // 8-element chunks of the tile
+    static constexpr int kIter = (kChunks + NT - 1) / NT;
     Chunk<QF8> v[kIter];
+
+    __device__ __forceinline__ void load(const Args& a, int b, int ht, int tid) {
+        const size_t q_row_bytes = (size_t)kRow * (QF8 ? 1 : 2);
 #pragma unroll
-    for (int k = 0; k < kIter; ++k) {
-        int idx = tid + NT * k;
-        idx = idx < kChunks ? idx : kChunks - 1;
-        const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
-        int hh = ht * 16 + hq;
-        hh = hh < a.H ? hh : a.H - 1;
-        v[k] = load_chunk<QF8>(a.q + ((size_t)b * a.H + hh) * q_row_bytes, 8 * ch);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < kIter; ++k) {
-        const int idx = tid + NT * k;
-        if (idx < kChunks) {
+        for (int k = 0; k < kIter; ++k) {
+            int idx = tid + NT * k;
+            idx = idx < kChunks ? idx : kChunks - 1;
             const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
-            const bf16x8 x = ht * 16 + hq < a.H ? to_bf16<QF8>(v[k]) : bf16x8{};
-            *reinterpret_cast<bf16x8*>(qlds + hq * kQStride + 8 * ch) = x;
+            int hh = ht * 16 + hq;
+            hh = hh < a.H ? hh : a.H - 1;
+            v[k] = load_chunk<QF8>(a.q + ((size_t)b * a.H + hh) * q_row_bytes, 8 * ch);
         }
     }
+    __device__ __forceinline__ void store(const Args& a, int ht, __bf16* qlds, int tid) const {
+#pragma unroll
+        for (int k = 0; k < kIter; ++k) {
+            const int idx = tid + NT * k;
+            if (idx < kChunks) {
+                const int hq = idx / (kRow / 8), ch = idx % (kRow / 8);
+                const bf16x8 x = ht * 16 + hq < a.H ? to_bf16<QF8>(v[k]) : bf16x8{};
+                *reinterpret_cast<bf16x8*>(qlds + hq * kQStride + 8 * ch) = x;
+            }
+        }
+    }
+};
+
+template <bool QF8, int NT>
+__device__ __forceinline__ void stage_queries(const Args& a, int b, int ht, __bf16* qlds, int tid) {
+    QueryStage<QF8, NT> qs;
+    qs.load(a, b, ht, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    qs.store(a, ht, qlds, tid);
 }
 
 // Workgroup barrier for LDS traffic only: this wavefront's LDS operations are
@@ -386,42 +399,64 @@ mla_attn_partial_kernel(const Args a) {
     const int nt = k1 > first ? (k1 - first + kStepKeys - 1) / kStepKeys : 0;
     const int np = (nt + 1) / 2;
 
+    // The query loads go out first, then the first pair's block-table entries
+    // and keys.  Block-table entries are read at keys clamped to
+    // max_seq_len - 1 only, so they wait for nothing but the table (not for
+    // the sequence length).  Every tile of a pair goes through the value
+    // product, so every row read must be finite: a lane whose key lies past
+    // the range reads the tile's first key (lane 0's page), and a tile wholly
+    // past the range reads the range's first key.  Pairs from 1 on that lie
+    // past the range (requested only to keep the loads unconditional) repeat
+    // the range's last tile.
+    QueryStage<QF8, kThreads> qs;
+    qs.load(a, b, ht, threadIdx.x);
     const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
     const size_t row_bytes = (size_t)kRow * (KVF8 ? 1 : 2);
-    // Key c of tile t; past the range it is the range's last key (finite
-    // data of this sequence, given zero weight below).
     const int last = k1 > 0 ? k1 - 1 : 0;
-    auto tile_key = [&](int t) -> int {
-        const int key = first + kStepKeys * t + c;
-        return key < last ? key : last;
+    const int kmax = a.max_seq_len > 0 ? a.max_seq_len - 1 : 0;
+    auto tile_at = [&](int t) -> int { return t < 2 || t < nt ? t : (nt > 0 ? nt - 1 : 0); };
+    auto spec_key = [&](int t) -> int {
+        const int key = first + kStepKeys * tile_at(t) + c;
+        return key < kmax ? key : kmax;
     };
-    auto page_of = [&](int t) -> int { return bt[tile_key(t) / a.block_size]; };
+    auto page_of = [&](int t) -> int { return bt[spec_key(t) / a.block_size]; };
+    int page_first = 0;   // page of the range's first key (lane 0 of tile 0)
     auto row_of = [&](int t, int page) -> const uint8_t* {
+        const int raw = first + kStepKeys * tile_at(t) + c, raw0 = raw - c;
+        int key = raw < kmax ? raw : kmax;
+        if (raw > last) {
+            if (raw0 <= last) {
+                key = raw0;
+                page = __builtin_amdgcn_readlane(page, 0);
+            } else {
+                key = first < kmax ? first : kmax;
+                page = page_first;
+            }
+        }
         page = page < 0 ? 0 : (page >= a.num_blocks ? a.num_blocks - 1 : page);
-        return a.cache + ((size_t)page * a.block_size + tile_key(t) % a.block_size) * row_bytes;
+        return a.cache + ((size_t)page * a.block_size + key % a.block_size) * row_bytes;
     };
 
     PairRegs<KVF8> kc[kPB];
     int pg[kPB][2];
-    if (np > 0) {
 #pragma unroll
-        for (int j = 0; j < kPB; ++j) {
-            pg[j][0] = page_of(2 * j);
-            pg[j][1] = page_of(2 * j + 1);
-        }
+    for (int j = 0; j < kPB; ++j) {
+        pg[j][0] = page_of(2 * j);
+        pg[j][1] = page_of(2 * j + 1);
+    }
+    page_first = __builtin_amdgcn_readlane(pg[0][0], 0);
 #pragma unroll
-        for (int j = 0; j < kPB; ++j) {
+    for (int j = 0; j < kPB; ++j) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                load_tile<KVF8>(kc[j].t[h], row_of(2 * j + h, pg[j][h]), g);
-                pg[j][h] = page_of(2 * (j + kPB) + h);
-            }
+        for (int h = 0; h < 2; ++h) {
+            load_tile<KVF8>(kc[j].t[h], row_of(2 * j + h, pg[j][h]), g);
+            pg[j][h] = page_of(2 * (j + kPB) + h);
         }
     }
 
     // The tile's 16 query rows, as bf16, in LDS: operand B of the score
     // products is read from there.
-    stage_queries<QF8, kThreads>(a, b, ht, qlds, threadIdx.x);
+    qs.store(a, ht, qlds, threadIdx.x);
     __syncthreads();
     const __bf16* qrow = qlds + c * kQStride + KeyTile<KVF8>::lane_dim(g);
     float sc = a.score_scale;
