@@ -61,6 +61,8 @@ size_t mla_decode_attention_workspace_size(const mla_attn_dims* dims, uint32_t f
  *              16-B aligned.
  * block_table  int32 [B, max_blocks_per_seq]; entries used for j < seq_lens[b]
  *              must lie in [0, num_blocks) (the kernel clamps them into that range).
+ *              Entries past a sequence's length may be read and may hold anything;
+ *              neither they nor the cache rows they point to affect the output.
  * seq_lens     int32 [B]; values are clamped into [0, max_seq_len].
  * q_scale, kv_scale: fp32 scalars (device), required with the matching FP8 flag.
  * sm_scale     softmax scale applied to the raw dot products (host value).
