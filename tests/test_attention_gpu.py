@@ -263,6 +263,34 @@ def test_nan_in_unused_cache_slots_is_ignored(kv_fp8):
     assert_close(got, ref, bound(w, inp, ref), "nan-slots")
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_table_entries_past_the_length_are_ignored(kv_fp8):
+    """Block-table entries past each sequence's length hold garbage (negative
+    and huge page numbers) and every unused cache slot holds NaN: the
+    header allows the kernel to read them, but they may not reach the
+    output."""
+    w = I.attn_custom(5, 16, (70, 1, 129, 0, 900), kv_fp8=kv_fp8, name="table-garbage")
+    inp = I.make_attn_inputs(w)
+    cache = inp["cache"]
+    raw = cache.view(torch.uint8) if kv_fp8 else cache.view(torch.int16)
+    used = torch.zeros(w.num_blocks, w.block_size, dtype=torch.bool)
+    table = inp["block_table"].clone()
+    g = torch.Generator().manual_seed(11)
+    for b, L in enumerate(w.seq_lens):
+        j = torch.arange(L)
+        used[table[b, (j // w.block_size).long()].long(), j % w.block_size] = True
+        n_used = (L + w.block_size - 1) // w.block_size
+        tail = table.shape[1] - n_used
+        if tail > 0:
+            junk = torch.randint(-(2 ** 31), 2 ** 31 - 1, (tail,), generator=g, dtype=torch.int64)
+            table[b, n_used:] = junk.to(torch.int32)
+    raw[~used] = 0x7F if kv_fp8 else 0x7FC0
+    inp["block_table"] = table
+    got = run_gpu(w, inp, f"table-garbage kv_fp8={kv_fp8}")
+    ref = oracle_out(w, inp)
+    assert_close(got, ref, bound(w, inp, ref), "table-garbage")
+
+
 @pytest.mark.parametrize("q_fp8", [False, True])
 def test_every_e4m3_code_reaches_the_output_exactly(q_fp8):
     """With one key per sequence the softmax weight is exactly 1 and the
