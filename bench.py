@@ -388,7 +388,8 @@ def attention_timings(dev: str, steps: int, cpu_seconds: float = 0.0) -> dict:
     """Decode attention over the paged latent cache, per workload: device
     time per call (events around back-to-back calls on the launch stream),
     with enough independent cache copies rotated that their total exceeds
-    twice the 256 MB MALL (cold), and with one copy (warm)."""
+    twice the 256 MB MALL (cold), and with one copy (warm); also the cold
+    rotation captured in a HIP graph and replayed (no host launch gaps)."""
     out = {}
     for name, w in I.ATTN_WORKLOADS.items():
         host = I.make_attn_inputs(w)
@@ -399,6 +400,7 @@ def attention_timings(dev: str, steps: int, cpu_seconds: float = 0.0) -> dict:
         calls = max(20, steps // 4)
         cold = time_calls(sets, calls, 5)
         warm = time_calls(sets[:1], calls, 5)
+        graph_cold_us = time_graph(sets, calls=10 * len(sets), replays=10)
         nb = attn_algorithmic_bytes(w)
         pl = sets[0].prepared.plan
         out[name] = {
@@ -406,6 +408,7 @@ def attention_timings(dev: str, steps: int, cpu_seconds: float = 0.0) -> dict:
             "us_per_call": round(cold["event_ms_per_call"] * 1e3, 3),
             "gbs": round(nb / cold["event_ms_per_call"] / 1e6, 1),
             "pct_of_hbm_peak": round(100.0 * nb / cold["event_ms_per_call"] / 1e6 / HBM_PEAK_GBS, 2),
+            "us_per_call_graph": round(graph_cold_us, 3),
             "us_per_call_warm": round(warm["event_ms_per_call"] * 1e3, 3),
             "gbs_warm": round(nb / warm["event_ms_per_call"] / 1e6, 1),
             "splits": pl.splits, "keys_per_split": pl.keys_per_split,
