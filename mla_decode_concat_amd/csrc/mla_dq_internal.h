@@ -61,6 +61,17 @@
 #define MLA_DQ_LARGE_TAIL_LF 0
 #endif
 
+// Where tail lanes read the rope table: 1 = the workgroup first stages the
+// table rows of its tokens in LDS, 0 = each lane loads its own values from
+// the table.  Staging saves table loads and costs one barrier: it wins when
+// bandwidth-bound and loses on the latency-bound path (measured).
+#ifndef MLA_DQ_SMALL_TABLE_LDS
+#define MLA_DQ_SMALL_TABLE_LDS 0
+#endif
+#ifndef MLA_DQ_LARGE_TABLE_LDS
+#define MLA_DQ_LARGE_TABLE_LDS 1
+#endif
+
 namespace mla_dq {
 
 // A mapping: threads per workgroup, latent rows handled by each wavefront

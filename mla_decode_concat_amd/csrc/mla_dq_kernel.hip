@@ -20,7 +20,11 @@
 //    takes the tails of 8 rows per step.  NeoX pairs element i with i + 32,
 //    i.e. chunk j with chunk j ^ 4, which sits in lane (lane ^ 4): the
 //    partner's 8 values arrive by ds_swizzle, in registers.  Each tail lane
-//    loads the 8 cos and 8 sin values it needs from the caller's table row.
+//    takes the 8 cos and 8 sin values it needs from its token's table row:
+//    in the throughput mapping the workgroup first stages the table rows of
+//    its tokens in LDS (one 16-byte load per thread, then one barrier); in
+//    the latency mapping, where that barrier would lengthen the critical
+//    chain position -> table -> store, each lane loads its values itself.
 //
 // Workgroups [0, tail_blocks) do tails, the rest do latent parts; tails go
 // first because their dependency chain (position -> table row -> rotate) is
@@ -270,7 +274,7 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
 }
 
 // ---- positional tails: 8 rows' tails per wavefront step --------------------
-template <int BLOCK, int STEPS, bool STREAM, bool LF, bool VAR, bool ROPE, bool QF8, bool KVF8>
+template <int BLOCK, int STEPS, bool STREAM, bool LF, bool TLDS, bool VAR, bool ROPE, bool QF8, bool KVF8>
 __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
     // Variant modes are read only by the instances built for them; the
     // page's configuration (bf16, NeoX pairs, fp32 table) checks nothing.
@@ -285,7 +289,8 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
     // Lanes past the last row read row 0 (always valid) and store nothing,
     // so every load below is unconditional.  Activations and positions go
     // first, then the table rows (which need the positions); slots and
-    // scales are needed by the stores only.
+    // scales are needed by the stores only.  With TLDS the positions are
+    // read by the threads that stage the table rows, not by the tail lanes.
     uint32_t tok[STEPS], head[STEPS];
     bool live[STEPS];
     int64_t pos[STEPS], slot[STEPS];
@@ -314,20 +319,52 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
                                   : a.k_pe + t * a.k_pe_st;
         d[k] = load_in<STREAM, u32x4>(src + j * 8u);
         pos[k] = 0;
-        if constexpr (ROPE) pos[k] = a.positions[t];
+        if constexpr (ROPE && !TLDS) pos[k] = a.positions[t];
     }
     // Table values for this lane, widened to one per element: cos in c, sin
     // in s.  NeoX: elements 8j..8j+7 of a half use angles 8(j&3)..+7.
     // Interleaved: elements 8j..8j+7 are pairs 4j..4j+3.
     float c[ROPE ? STEPS : 1][8], s[ROPE ? STEPS : 1][8];
     if constexpr (ROPE) {
+        const uint32_t table_row_bytes = table_bf16 ? 128u : 256u;
+        // TLDS: the workgroup's rows [rlo, rhi) belong to tokens t_lo ..
+        // t_lo + ntok - 1.  Their table rows are copied to LDS, one 16-byte
+        // chunk per thread, and every tail lane then reads its values there.
+        // A token owns H + 1 >= 2 rows, so ntok <= rows / 2 + 1.
+        constexpr uint32_t kRowsPerWg = STEPS * kRowsPerStep;
+        constexpr uint32_t kMaxTokens = kRowsPerWg / 2 + 1;
+        const uint8_t* staged = nullptr;
+        uint32_t t_lo = 0;
+        if constexpr (TLDS) {
+            __shared__ __attribute__((aligned(16))) uint8_t table_lds[kMaxTokens * 256];
+            const uint32_t rlo = tile * kRowsPerWg;   // < total_rows: tile < tail_blocks
+            const uint32_t rhi = rlo + kRowsPerWg < a.total_rows ? rlo + kRowsPerWg : a.total_rows;
+            t_lo = fastdiv31(rlo, a.rows_per_token);
+            const uint32_t ntok = fastdiv31(rhi - 1u, a.rows_per_token) - t_lo + 1u;
+            const uint32_t shift = table_bf16 ? 3u : 4u;   // 16-byte chunks per row: 8 or 16
+            for (uint32_t i = threadIdx.x; i < (ntok << shift); i += BLOCK) {
+                const uint32_t k = i >> shift, q = i & ((1u << shift) - 1u);
+                int64_t p = a.positions[t_lo + k];
+                p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
+                *reinterpret_cast<u32x4*>(table_lds + 256u * k + 16u * q) = *reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const uint8_t*>(a.rope_cos_sin) + p * table_row_bytes + 16u * q);
+            }
+            __syncthreads();
+            staged = table_lds;
+        }
 #pragma unroll
         for (int k = 0; k < STEPS; ++k) {
-            int64_t p = pos[k];
-            p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
+            const uint8_t* row_base;
+            if constexpr (TLDS) {
+                row_base = staged + 256u * (live[k] ? tok[k] - t_lo : 0u);
+            } else {
+                int64_t p = pos[k];
+                p = p < 0 ? 0 : (p >= a.max_position ? a.max_position - 1 : p);
+                row_base = reinterpret_cast<const uint8_t*>(a.rope_cos_sin) + p * table_row_bytes;
+            }
             const uint32_t col = gptj ? 4u * j : 8u * (j & 3u);
             if (table_bf16) {
-                const uint16_t* trow = reinterpret_cast<const uint16_t*>(a.rope_cos_sin) + p * 64 + col;
+                const uint16_t* trow = reinterpret_cast<const uint16_t*>(row_base) + col;
                 if (gptj) {
                     const u32x2 cv = *reinterpret_cast<const u32x2*>(trow);
                     const u32x2 sv = *reinterpret_cast<const u32x2*>(trow + 32);
@@ -343,7 +380,7 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
                     unpack_bf16(*reinterpret_cast<const u32x4*>(trow + 32), s[k]);
                 }
             } else {
-                const float* trow = a.rope_cos_sin + p * 64 + col;
+                const float* trow = reinterpret_cast<const float*>(row_base) + col;
                 if (gptj) {
                     const f32x4 cv = *reinterpret_cast<const f32x4*>(trow);
                     const f32x4 sv = *reinterpret_cast<const f32x4*>(trow + 32);
@@ -427,9 +464,10 @@ mla_dq_epilogue_kernel(const KernelArgs a) {
     constexpr bool kSmall = BLOCK == kSmallMapping.block;
     constexpr bool LATENT_LF = kSmall ? MLA_DQ_SMALL_LATENT_LF : MLA_DQ_LARGE_LATENT_LF;
     constexpr bool TAIL_LF = kSmall ? MLA_DQ_SMALL_TAIL_LF : MLA_DQ_LARGE_TAIL_LF;
+    constexpr bool TABLE_LDS = kSmall ? MLA_DQ_SMALL_TABLE_LDS : MLA_DQ_LARGE_TABLE_LDS;
     const uint32_t b = blockIdx.x;
     if (b < a.tail_blocks) {
-        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, VAR, ROPE, QF8, KVF8>(a, b);
+        tail_rows<BLOCK, TAIL_STEPS, STREAM, TAIL_LF, TABLE_LDS, VAR, ROPE, QF8, KVF8>(a, b);
         return;
     }
     uint32_t tile = b - a.tail_blocks;
