@@ -260,15 +260,23 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
                                                       lane * 8u, 0, kAux);
             else
                 __builtin_amdgcn_raw_buffer_store_b128(d[k], dst, lane * 16u, 0, kAux);
-        } else {
-            const u32x2 f8 = e4m3_of_act(d[k], QF8 ? q_inv : kv_inv, fp16);
-            if constexpr (QF8) {
-                __builtin_amdgcn_raw_buffer_store_b64(f8, qdst, lane * 8u, 0, kAux);
-                __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst, lane * 16u, 0, kAux);
-            } else {
+        } else if constexpr (KVF8) {
+            // Query rows copied, cache row E4M3.  The row is wave-uniform, so
+            // a scalar branch spares the query rows (H of every H + 1) an
+            // E4M3 conversion they would not store (measured 1.5 % faster at
+            // 8192 tokens than converting every row).
+            if (is_q)
                 __builtin_amdgcn_raw_buffer_store_b128(d[k], qdst, lane * 16u, 0, kAux);
-                __builtin_amdgcn_raw_buffer_store_b64(f8, cdst, lane * 8u, 0, kAux);
-            }
+            else
+                __builtin_amdgcn_raw_buffer_store_b64(e4m3_of_act(d[k], kv_inv, fp16), cdst, lane * 8u,
+                                                      0, kAux);
+        } else {
+            // Query rows E4M3, cache row copied: the query rows convert
+            // anyway, and issuing both stores (one dropped) measured faster
+            // than branching.
+            const u32x2 f8 = e4m3_of_act(d[k], q_inv, fp16);
+            __builtin_amdgcn_raw_buffer_store_b64(f8, qdst, lane * 8u, 0, kAux);
+            __builtin_amdgcn_raw_buffer_store_b128(d[k], cdst, lane * 16u, 0, kAux);
         }
     }
 }
