@@ -192,6 +192,37 @@ def test_ragged_shapes_all_modes(T, H, fl):
     check_against_oracle(w, inp, q, cache, cache_init=init)
 
 
+@pytest.mark.parametrize("T,H", [(1, 1), (31, 1), (32, 1), (33, 1), (97, 1), (250, 2), (77, 3)])
+@pytest.mark.parametrize("fl", [f for f in FLAG_SETS if f[0]], ids=lambda f: "r%dq%dk%d" % f)
+def test_throughput_mapping_few_heads(T, H, fl):
+    """The throughput mapping stages the rope-table rows of the tokens each
+    workgroup covers in LDS.  With one head a workgroup's 64 tail rows span
+    33 tokens, the most the stage holds; ragged T leaves a partial last
+    workgroup.  Forced throughput mapping against the oracle, and equal to
+    the latency mapping, with a position table of distinct rows."""
+    rope, qf, kf = fl
+    w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=rope, q_fp8=qf, kv_fp8=kf,
+                 q_scale=0.04, kv_scale=0.3)
+    inp = I.make_inputs(w, seed=7 * T + H)
+    ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T, case=f"few heads large T={T} H={H} {fl}")
+    qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"few heads small T={T} H={H} {fl}")
+    assert np.array_equal(ql, qs) and np.array_equal(cl, cs)
+    check_against_oracle(w, inp, ql, cl)
+
+
+@pytest.mark.parametrize("dtype,style,table", [("fp16", "neox", "f32"), ("bf16", "gptj", "bf16"),
+                                               ("fp16", "gptj", "bf16"), ("bf16", "neox", "bf16")],
+                         ids=lambda v: str(v))
+def test_throughput_mapping_few_heads_variants(dtype, style, table):
+    """The LDS-staged table rows in the variant layouts (bf16 table rows are
+    half as long), one head, ragged T, forced throughput mapping."""
+    w = I.custom(95, 1, num_blocks=3, rope=True, q_fp8=False, kv_fp8=True, q_scale=0.04,
+                 kv_scale=0.3, dtype=dtype, rope_style=style, table_dtype=table)
+    inp = I.make_inputs(w, seed=95)
+    ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T, case=f"few heads variant {dtype}/{style}/{table}")
+    check_against_oracle(w, inp, ql, cl)
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.05, 2.0 ** -4, 3.7])
 def test_e4m3_exhaustive_all_bf16_inputs(scale):
     """Every bf16 bit pattern through the quantiser, in the latent part, the
