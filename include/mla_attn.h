@@ -68,7 +68,21 @@ size_t mla_decode_attention_workspace_size(const mla_attn_dims* dims, uint32_t f
  * sm_scale     softmax scale applied to the raw dot products (host value).
  * workspace    device memory of at least mla_decode_attention_workspace_size()
  *              bytes (may be NULL when that size is 0); contents are scratch.
- * All pointers are device pointers except dims (host).  Enqueued on stream.
+ * All pointers are device pointers except dims (host).  Enqueued on stream;
+ * the call returns after the launch, without waiting.  The caller owns every
+ * buffer.  out and the workspace must not overlap each other or any input.
+ *
+ * Returns 0, or (nothing launched; the checks read no device memory):
+ *   MLA_DQ_ERR_NULL   (-1) dims NULL, a required pointer NULL (a scale needed
+ *                          by its flag, the workspace when one is needed)
+ *   MLA_DQ_ERR_ALIGN  (-2) out, q, cache or workspace not 16-byte aligned,
+ *                          block_table, seq_lens or a scale not 4-byte aligned
+ *   MLA_DQ_ERR_DIM    (-3) a dimension out of range, or sm_scale not finite
+ *   MLA_DQ_ERR_FLAGS  (-4) an unknown flag bit
+ *   MLA_DQ_ERR_LAUNCH (-5) the HIP launch failed
+ *   MLA_DQ_ERR_ALIAS  (-6) out or the workspace overlaps another buffer
+ *   MLA_ATTN_ERR_WORKSPACE (-7) workspace_bytes below the size needed
+ * batch == 0 returns 0 with no launch.
  */
 int mla_decode_attention(void* out, const void* q, const void* cache, const int32_t* block_table,
                          const int32_t* seq_lens, const float* q_scale, const float* kv_scale,

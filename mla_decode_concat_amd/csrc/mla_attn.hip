@@ -949,6 +949,47 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
 
 bool aligned(const void* x, uintptr_t n) { return (reinterpret_cast<uintptr_t>(x) % n) == 0; }
 
+// Byte range [lo, lo + bytes) of one buffer; sizes saturate instead of wrapping.
+struct Span {
+    uintptr_t lo;
+    uint64_t bytes;
+};
+
+uint64_t mul_sat(uint64_t a, uint64_t b) {
+    uint64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? UINT64_MAX : r;
+}
+
+bool overlap(Span x, Span y) {
+    if (x.bytes == 0 || y.bytes == 0) return false;
+    const uint64_t xe = x.lo + x.bytes < x.lo ? UINT64_MAX : x.lo + x.bytes;
+    const uint64_t ye = y.lo + y.bytes < y.lo ? UINT64_MAX : y.lo + y.bytes;
+    return x.lo < ye && y.lo < xe;
+}
+
+// The output and the used part of the workspace are written while other
+// workgroups still read the inputs, so neither may overlap any other buffer.
+bool aliased(const void* out, const void* q, const void* cache, const int32_t* block_table,
+             const int32_t* seq_lens, const float* q_scale, const float* kv_scale, const void* workspace,
+             const mla_attn_dims* d, const mla_attn_plan& p, bool qf8, bool kvf8) {
+    auto at = [](const void* x) { return reinterpret_cast<uintptr_t>(x); };
+    const uint64_t bh = mul_sat(uint64_t(d->batch), uint64_t(d->num_heads));
+    const Span o{at(out), mul_sat(bh, kValue * 2)};
+    const Span ws{at(workspace), workspace ? uint64_t(p.workspace_bytes) : 0};
+    const Span in[] = {
+        {at(q), mul_sat(bh, qf8 ? kRow : 2 * kRow)},
+        {at(cache), mul_sat(mul_sat(uint64_t(d->num_blocks), uint64_t(d->block_size)), kvf8 ? kRow : 2 * kRow)},
+        {at(block_table), mul_sat(mul_sat(uint64_t(d->batch), uint64_t(d->max_blocks_per_seq)), 4)},
+        {at(seq_lens), mul_sat(uint64_t(d->batch), 4)},
+        {at(q_scale), qf8 ? 4u : 0u},
+        {at(kv_scale), kvf8 ? 4u : 0u},
+    };
+    if (overlap(o, ws)) return true;
+    for (const Span& s : in)
+        if (overlap(o, s) || overlap(ws, s)) return true;
+    return false;
+}
+
 template <bool QF8, bool KVF8>
 hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream) {
     const dim3 grid(uint32_t(p.workgroups)), block(uint32_t(p.block_threads));
@@ -1014,6 +1055,8 @@ int mla_decode_attention(void* out, const void* q, const void* cache, const int3
         (qf8 && !aligned(q_scale, 4)) || (kvf8 && !aligned(kv_scale, 4)))
         return MLA_DQ_ERR_ALIGN;
     if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return MLA_DQ_ERR_DIM;
+    if (aliased(out, q, cache, block_table, seq_lens, q_scale, kv_scale, workspace, dims, p, qf8, kvf8))
+        return MLA_DQ_ERR_ALIAS;
 
     Args a;
     a.out = static_cast<uint16_t*>(out);

@@ -171,6 +171,19 @@ def test_bad_softmax_scale(sm):
     assert _call(_ptrs(), 0, dims(), sm=sm) == B.ERR_DIM
 
 
+@pytest.mark.parametrize("moved,onto,off", [("out", "q", 16), ("q", "out", 4096), ("out", "cache", 0),
+                                            ("out", "bt", 32), ("out", "lens", 0), ("ws", "out", 16),
+                                            ("ws", "cache", 1 << 20), ("cache", "ws", 4096),
+                                            ("bt", "ws", 64), ("out", "ks", 0)])
+def test_output_or_workspace_overlapping_a_buffer(moved, onto, off):
+    """out and the workspace are written while other workgroups read the
+    inputs: any overlap with another buffer is refused before a launch."""
+    p = _ptrs()
+    p[moved] = p[onto] + off
+    assert _call(p, M.ATTN_KV_FP8, dims()) == B.ERR_ALIAS
+
+
+
 # ---- Python binding: argument checks that run before anything is launched ----
 
 def _cpu_args(B_=2, H=16, NB=4, BS=64, MB=2, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16):
