@@ -533,8 +533,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the epilogue has no cross-GPU step, and this "
-              "build runs and reports a single MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the epilogue exchanges nothing between GPUs, "
+              "so it runs and reports a single MI355X (use --gpus 1).", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
