@@ -417,8 +417,16 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < STEPS; ++k) slot[k] = a.slot_mapping[tok[k]];
-        if constexpr (QF8) q_inv = 1.0f / *a.q_scale;
-        if constexpr (KVF8) kv_inv = 1.0f / *a.kv_scale;
+        // The scales are used only by the stores, behind a branch.  The
+        // empty asm needs their values here, so their loads go out with the
+        // table loads instead of being sunk past the wait for the table (a
+        // third dependent memory round trip before the store).
+        float qs = 1.0f, ks = 1.0f;
+        if constexpr (QF8) qs = *a.q_scale;
+        if constexpr (KVF8) ks = *a.kv_scale;
+        asm volatile("" ::"s"(qs), "s"(ks));
+        if constexpr (QF8) q_inv = 1.0f / qs;
+        if constexpr (KVF8) kv_inv = 1.0f / ks;
     }
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
