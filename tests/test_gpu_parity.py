@@ -395,6 +395,37 @@ def test_variants_match_oracle(dtype, style, table, qf, kf, T, H):
     check_against_oracle(w, inp, qs, cs)
 
 
+def _random_case(i: int):
+    """Seeded random shape and mode: tokens, heads, block size, precision of
+    each output, activation type, rotation style and table type, slot
+    recipe, and which mapping is forced (if any)."""
+    rng = np.random.default_rng(1000 + i)
+    H = int(rng.choice([1, 2, 3, 5, 7, 8, 15, 16, 17, 31, 64, 128]))
+    T = int(rng.integers(1, max(2, min(3000, 60000 // (H + 1)))))
+    bs = int(rng.choice([1, 16, 64, 128]))
+    rope, qf, kf = bool(rng.integers(2)), bool(rng.integers(2)), bool(rng.integers(2))
+    dtype = "fp16" if rng.integers(4) == 0 else "bf16"
+    style = "gptj" if rope and rng.integers(3) == 0 else "neox"
+    table = "bf16" if rope and rng.integers(3) == 0 else "f32"
+    nb = (T + bs - 1) // bs + int(rng.integers(0, 3))
+    force = [0, M.FORCE_SMALL_T, M.FORCE_LARGE_T, M.FORCE_LARGE_T | M.FORCE_STREAM][int(rng.integers(4))]
+    w = I.custom(T, H, num_blocks=nb, block_size=bs, rope=rope, q_fp8=qf, kv_fp8=kf,
+                 q_scale=float(rng.choice([0.05, 0.3, 1.0])), kv_scale=float(rng.choice([0.05, 2.0])),
+                 dtype=dtype, rope_style=style, table_dtype=table,
+                 max_position=int(rng.choice([1, 77, 4096])))
+    return w, force, int(rng.integers(1 << 30))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_seeded_random_shapes_and_modes(i):
+    """Random shapes, heads, block sizes, flag and variant combinations and
+    launch overrides, each against the oracle."""
+    w, force, seed = _random_case(i)
+    inp = I.make_inputs(w, seed=seed)
+    q, cache = run_gpu(w, inp, force, case=f"random case {i} (seed {seed})")
+    check_against_oracle(w, inp, q, cache)
+
+
 @pytest.mark.parametrize("T,H", [(1, 16), (65, 16)])
 def test_fp16_copy_path(T, H):
     w = I.custom(T, H, dtype="fp16")
