@@ -16,7 +16,7 @@
  * and FP8 off, q equals cat(ql_nope, q_pe) and the cache rows at the slots
  * equal cat(kv_c, k_pe); the cache starts as zeros and every other byte stays.
  *
- * Readings where the page is silent (all stated again in the design notes):
+ * Readings where the page is silent:
  *  - rotation is the NeoX half-split form (element i pairs with element
  *    i+32) unless the interleaved GPT-J pairing (2i with 2i+1) is asked for;
  *    the rope table row for position p holds cos[0:32] then sin[0:32]
