@@ -252,3 +252,51 @@ def attn_custom(batch: int, heads: int, seq_lens, block_size: int = 64, q_fp8: b
         seq_lens = (seq_lens,) * batch
     return AttnWorkload(name, batch, heads, tuple(int(x) for x in seq_lens), block_size, q_fp8,
                         kv_fp8, **kw)
+
+
+def make_inputs_on_device(w: Workload, device: str, seed: int = DEFAULT_SEED,
+                          chunk: int = 1 << 27) -> dict:
+    """The same recipe as make_inputs, drawn on the device by torch's device
+    generator (for sizes whose host copy would be impractical; the values
+    differ from make_inputs' for the same seed).  Activations are N(0,1)
+    fp32 rounded to the activation type, drawn ``chunk`` elements at a time;
+    slots are a prefix of a random permutation of all cache slots; positions
+    follow the workload's recipe.  The cache starts as zeros."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    T, H = w.tokens, w.heads
+
+    def randn_act(*shape):
+        out = torch.empty(*shape, dtype=w.torch_dtype, device=device)
+        for part in out.view(-1).split(chunk):
+            part.copy_(torch.randn(part.numel(), generator=g, dtype=torch.float32, device=device))
+        return out
+
+    ql_nope = randn_act(T, H, NOPE)
+    q_pe = randn_act(T, H, PE)
+    kv_c = randn_act(T, NOPE)
+    k_pe = randn_act(T, PE)
+    S = w.num_slots
+    if w.slots != "randperm" or T > S:
+        raise ValueError("device inputs take a prefix of a slot permutation")
+    slots = torch.randperm(S, generator=g, dtype=torch.int64, device=device)[:T].contiguous()
+    if w.positions == "none":
+        positions = None
+    elif w.positions == "arange":
+        positions = torch.arange(T, dtype=torch.int64, device=device)
+    elif w.positions.startswith("uniform:"):
+        hi = int(w.positions.split(":")[1])
+        positions = torch.randint(0, hi, (T,), generator=g, dtype=torch.int64, device=device)
+    else:
+        raise ValueError(w.positions)
+    kv_dtype = torch.float8_e4m3fn if w.kv_fp8 else w.torch_dtype
+    cache = torch.zeros(w.num_blocks, w.block_size, ROW, dtype=kv_dtype, device=device)
+    table = None
+    if w.rope:
+        table = shared_rope_table(w.max_position)
+        if w.table_dtype == "bf16":
+            table = table.to(torch.bfloat16)
+        table = table.to(device)
+    return dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
+                slot_mapping=slots, positions=positions, rope_cos_sin=table,
+                q_scale=torch.tensor([w.q_scale], dtype=torch.float32, device=device) if w.q_fp8 else None,
+                kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32, device=device) if w.kv_fp8 else None)

@@ -18,6 +18,7 @@ import torch
 
 import mla_decode_concat_amd as M
 from mla_decode_concat_amd import inputs as I
+import oracle
 from tests._util import bits, oracle_run
 
 pytestmark = pytest.mark.gpu
@@ -528,3 +529,52 @@ def test_binding_rejects_wrong_dtypes():
     with pytest.raises(ValueError):
         M.mla_decode_q_concat_kv_insert(q16, dev["ql_nope"].float(), dev["q_pe"], dev["kv_c"],
                                         dev["k_pe"], dev["cache"], dev["slot_mapping"])
+
+
+def test_maximum_token_count_sampled():
+    """The largest token count the C ABI accepts at 16 heads: row indices and
+    the T * (H + 1) * 72 chunk count sit just below 2^31 (one token more is
+    refused).  Full-size call (about 52 GB of device buffers), then both ends
+    and a random sample of tokens against the oracle token by token, every
+    sampled cache row, and the untouched cache rows still zero."""
+    H = 16
+    T = (2 ** 31 - 1) // (72 * (H + 1))
+    w = I.custom(T, H, rope=True, q_fp8=True, kv_fp8=True)
+    flags = flags_of(w)
+    d = M.Dims(num_tokens=T, num_heads=H, num_blocks=w.num_blocks, block_size=w.block_size,
+               max_position=w.max_position, ql_nope_stride_t=H * 512, ql_nope_stride_h=512,
+               q_pe_stride_t=H * 64, q_pe_stride_h=64, kv_c_stride_t=512, k_pe_stride_t=64)
+    assert M.plan(d, flags).total_rows == T * (H + 1)
+    d.num_tokens = T + 1
+    with pytest.raises(M.MlaDqError):
+        M.plan(d, flags)
+    if torch.cuda.mem_get_info()[0] < 64 * (1 << 30):
+        pytest.skip("needs about 60 GB of free device memory")
+    announce(f"maximum size T={T} H={H}: drawing inputs on the device")
+    dev = I.make_inputs_on_device(w, DEV, seed=29)
+    q = torch.empty(T, H, I.ROW, dtype=torch.float8_e4m3fn, device=DEV)
+    announce(f"maximum size T={T} H={H}: kernel")
+    M.mla_decode_q_concat_kv_insert(q, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"],
+                                    dev["cache"], dev["slot_mapping"], dev["positions"],
+                                    dev["rope_cos_sin"], dev["q_scale"], dev["kv_scale"], flags)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(31)
+    idx = torch.cat([torch.arange(64), torch.arange(T - 64, T), torch.randperm(T, generator=gen)[:2048]])
+    idx = torch.unique(idx)
+    n = idx.numel()
+    di = idx.to(DEV)
+    slots = dev["slot_mapping"][di]
+    want_q = np.zeros((n, H, I.ROW), dtype=np.uint8)
+    want_rows = np.zeros((n, 1, I.ROW), dtype=np.uint8)
+    oracle.insert(want_q, bits(dev["ql_nope"][di]), bits(dev["q_pe"][di]), bits(dev["kv_c"][di]),
+                  bits(dev["k_pe"][di]), want_rows, np.arange(n, dtype=np.int64),
+                  dev["positions"][di].cpu().numpy(), dev["rope_cos_sin"].cpu().numpy(),
+                  w.q_scale, w.kv_scale, True, True, True)
+    assert_same(bits(q[di]), want_q, "q_out (sampled tokens)")
+    rows = dev["cache"].view(-1, I.ROW)
+    assert_same(bits(rows[slots]), want_rows.reshape(n, I.ROW), "cache rows (sampled tokens)")
+    written = torch.zeros(rows.shape[0], dtype=torch.bool, device=DEV)
+    written[dev["slot_mapping"]] = True
+    assert int(rows[~written].view(torch.uint8).count_nonzero()) == 0
+    del dev, q, rows, written
+    torch.cuda.empty_cache()
