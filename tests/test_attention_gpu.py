@@ -159,6 +159,19 @@ def test_range_merge_group_sizes(lengths, kv_fp8):
     check(w, f"ranges lengths={lengths} kv_fp8={kv_fp8} splits={plan.splits}")
 
 
+@pytest.mark.parametrize("lengths,kv_fp8", [((1 << 18,), True), ((1 << 18, 3), False)])
+def test_long_sequence_many_ranges(lengths, kv_fp8):
+    """A sequence of 2^18 cached tokens (4096 pages; 151 or 302 MB of cache):
+    256 ranges of 1024 keys, merged by the wide combine kernel in groups of
+    16 per wavefront; and, with a bf16 cache, beside it a 3-token sequence
+    whose ranges are all but one empty (128 ranges of 2048 keys)."""
+    w = I.attn_custom(len(lengths), 16, lengths, kv_fp8=kv_fp8, name="long")
+    plan = M.attn_plan(M.AttnDims(w.batch, w.heads, w.num_blocks, w.block_size, w.max_blocks,
+                                  w.max_blocks * w.block_size), M.ATTN_KV_FP8 if kv_fp8 else 0)
+    assert (plan.splits, plan.keys_per_split) == (256 // len(lengths), 1024 * len(lengths))
+    check(w, f"long lengths={lengths} kv_fp8={kv_fp8} splits={plan.splits}", seed=77)
+
+
 def _random_shape(case: int):
     """A seeded random (batch, heads, lengths, block size, precisions) case:
     lengths mix empty, sub-tile, page-crossing and multi-range sequences."""
