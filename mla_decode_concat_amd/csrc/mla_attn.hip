@@ -105,6 +105,8 @@ struct Args {
     float score_scale;   // sm_scale * log2(e)
     int32_t B, H, num_blocks, block_size, max_blocks, max_seq_len;
     int32_t splits, keys_per_split, head_tiles, xcd_remap;
+    int32_t grid;        // workgroups of the range kernel (read with the other
+                         // arguments, not from the dispatch's implicit ones)
 };
 
 // Eight E4M3 codes -> eight bf16, two per v_cvt_scalef32_pk_bf16_fp8 with
@@ -211,7 +213,7 @@ __device__ __forceinline__ bf16x4 read_tr(const __bf16* p) {
 __device__ __forceinline__ void decode_wg(const Args& a, int& b, int& split, int& ht) {
     int x = blockIdx.x;
     if (a.xcd_remap) {
-        const int n = gridDim.x;             // a multiple of 8 when remapping
+        const int n = a.grid;                // a multiple of 8 when remapping
         x = (x % 8) * (n / 8) + x / 8;
     }
     ht = x % a.head_tiles;
@@ -780,11 +782,14 @@ constexpr int kCombineThreads = 256;
 
 // Ranges [s_begin, s_end) of one (sequence, head) into one wavefront's
 // running (max M, weight sum den, weighted output acc over dims 8l .. 8l+7).
-template <int G>
+template <bool KVF8, int G>
 __device__ __forceinline__ void combine_ranges(const Args& a, size_t p0, int s_begin, int s_end, int lane,
-                                               float& M, float& den, f32x4& acc0, f32x4& acc1) {
+                                               float& M, float& den, f32x4& acc0, f32x4& acc1, float& kvs) {
     const float* po = a.part_o + p0 * kValue + 8 * lane;
-    for (int s0 = s_begin; s0 < s_end; s0 += G) {
+    // s_end >= 1 and s_begin < s_end in both callers; a do-while has no
+    // entry test, so the argument loads are not split by a wait for splits.
+    int s0 = s_begin;
+    do {
         f32x4 v[2 * G];
         float ms[G], ls[G];
 #pragma unroll
@@ -794,6 +799,16 @@ __device__ __forceinline__ void combine_ranges(const Args& a, size_t p0, int s_b
             v[2 * u + 1] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kValue + 4);
             ms[u] = a.part_m[p0 + s];
             ls[u] = s0 + u < s_end ? a.part_l[p0 + s] : 0.0f;
+        }
+        if constexpr (KVF8) {
+            // The scale is needed by the final store only.  Its load goes out
+            // behind the first group's loads; the empty asm needs its value
+            // here, so it is not deferred until after they return (a further
+            // memory round trip before the store).
+            if (s0 == s_begin) {
+                kvs = *a.kv_scale;
+                asm volatile("" ::"s"(kvs));
+            }
         }
         float Mn = M;
 #pragma unroll
@@ -813,13 +828,15 @@ __device__ __forceinline__ void combine_ranges(const Args& a, size_t p0, int s_b
             acc1 += wgt * v[2 * u + 1];
             den += wgt * ls[u];
         }
-    }
+        s0 += G;
+    } while (s0 < s_end);
 }
 
 template <bool KVF8>
-__device__ __forceinline__ void combine_write(const Args& a, int bh, int lane, float den, f32x4 acc0, f32x4 acc1) {
+__device__ __forceinline__ void combine_write(const Args& a, int bh, int lane, float den, f32x4 acc0, f32x4 acc1,
+                                              float kvs) {
     float f = den > 0.0f ? 1.0f / den : 0.0f;
-    if constexpr (KVF8) f *= *a.kv_scale;
+    if constexpr (KVF8) f *= kvs;
     uint16_t r[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -837,11 +854,15 @@ template <bool KVF8, int G>
 __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);   // b * H + h
-    if (bh >= a.B * a.H) return;
-    float M = -INFINITY, den = 0.0f;
+    // No early exit: a wavefront past the last head merges the last head
+    // again and stores nothing, so the argument loads and the first partial
+    // loads do not wait on a bounds test.
+    const int nbh = a.B * a.H;                 // >= 1 whenever this kernel runs
+    const int bhc = bh < nbh ? bh : nbh - 1;
+    float M = -INFINITY, den = 0.0f, kvs = 1.0f;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    combine_ranges<G>(a, (size_t)bh * a.splits, 0, a.splits, lane, M, den, acc0, acc1);
-    combine_write<KVF8>(a, bh, lane, den, acc0, acc1);
+    combine_ranges<KVF8, G>(a, (size_t)bhc * a.splits, 0, a.splits, lane, M, den, acc0, acc1, kvs);
+    if (bh < nbh) combine_write<KVF8>(a, bh, lane, den, acc0, acc1, kvs);
 }
 
 // More ranges: one workgroup per (sequence, head); its four wavefronts take
@@ -855,12 +876,12 @@ __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_wide_kernel(
     const int per = (a.splits + 3) / 4;
     const int sb = w * per < a.splits ? w * per : a.splits;
     const int se = sb + per < a.splits ? sb + per : a.splits;
-    float M = -INFINITY, den = 0.0f;
+    float M = -INFINITY, den = 0.0f, kvs = 1.0f;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     if (per <= 8)
-        combine_ranges<8>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1);
+        combine_ranges<KVF8, 8>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1, kvs);
     else
-        combine_ranges<16>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1);
+        combine_ranges<KVF8, 16>(a, (size_t)bh * a.splits, sb, se, lane, M, den, acc0, acc1, kvs);
     part[w][lane][0] = acc0;
     part[w][lane][1] = acc1;
     if (lane == 0) {
@@ -882,7 +903,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_wide_kernel(
         t1 += wgt * part[v][lane][1];
         dt += wgt * pm[v][1];
     }
-    combine_write<KVF8>(a, bh, lane, dt, t0, t1);
+    combine_write<KVF8>(a, bh, lane, dt, t0, t1, kvs);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -1081,6 +1102,7 @@ int mla_decode_attention(void* out, const void* q, const void* cache, const int3
     a.keys_per_split = p.keys_per_split;
     a.head_tiles = p.head_tiles;
     a.xcd_remap = p.xcd_remap;
+    a.grid = int32_t(p.workgroups);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (qf8)
