@@ -215,6 +215,9 @@ ATTN_WORKLOADS = {
     "attn_b64_l4096_h16_bf16": AttnWorkload("attn_b64_l4096_h16_bf16", 64, 16, (4096,) * 64),
     "attn_b1_l1024_h16_kvfp8": AttnWorkload("attn_b1_l1024_h16_kvfp8", 1, 16, (1024,),
                                             q_fp8=False, kv_fp8=True),
+    # one (sequence, head tile) per CU: no key split, no merge pass
+    "attn_b256_l4096_h16_kvfp8": AttnWorkload("attn_b256_l4096_h16_kvfp8", 256, 16, (4096,) * 256,
+                                              q_fp8=False, kv_fp8=True),
 }
 
 
