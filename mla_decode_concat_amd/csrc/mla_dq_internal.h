@@ -25,9 +25,13 @@
 #ifndef MLA_DQ_LARGE_TAIL_STEPS
 #define MLA_DQ_LARGE_TAIL_STEPS 2
 #endif
-// Small-T mapping while T * (H + 1) <= this many rows.
+// Small-T mapping while T * (H + 1) <= this many rows: the most rows whose
+// 64-thread latent and tail workgroups (rows + rows / 8) still fit in one
+// round of 16 workgroups on each of the 256 CUs.  Measured on MI355X, the
+// latency mapping wins up to here and the throughput mapping beyond, for
+// 16 to 128 heads.
 #ifndef MLA_DQ_SMALL_ROWS_MAX_DEFAULT
-#define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 2304
+#define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 3640
 #endif
 // Streaming (non-temporal) loads and stores once a call moves at least this
 // many bytes: above the 256 MB Infinity Cache nothing survives to the next

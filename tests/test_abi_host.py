@@ -205,7 +205,10 @@ def _bytes(T, H, flags):
 
 
 def test_plan_threshold_and_coverage():
-    for T in (1, 2, 63, 64, 65, 135, 136, 256, 8192):
+    pl = M.plan(_dims(T=1, H=16), 0)
+    rows = pl.small_rows_max           # the latency mapping's largest launch: one round of
+    assert rows + (rows + 7) // 8 <= 16 * 256 < rows + 1 + (rows + 8) // 8   # 64-thread groups
+    for T in (1, 2, 63, 64, 65, 135, 136, 214, 215, 256, 8192):
         for H in (1, 16, 128):
             for flags in (0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8 | M.KV_FP8,
                           M.ROPE | M.ROPE_GPTJ | M.TABLE_BF16 | M.FP16):
