@@ -86,7 +86,7 @@ constexpr int kLdsBytes = kWaves * kWaveTile * 2;     // 135168: covers the merg
 static_assert(kWaves * 24 * 64 * 16 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
-constexpr int kMinSplitSteps = 2;              // 64-key rounds per range, at least
+constexpr int kMinSplitSteps = 1;              // 64-key rounds per range, at least
 // The running max moves only when a pair of tiles exceeds it by more than
 // this (log2 units).
 constexpr float kRebase = 8.0f;
@@ -947,9 +947,9 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
     const int64_t target = target_workgroups();
     int64_t splits = base > 0 ? (target + base - 1) / base : 1;
     if (splits < 1) splits = 1;
-    // at least two 64-key rounds per range: a range's fixed cost (first loads,
-    // merge of its four wavefronts, its partial results) then stays small
-    // against its keys
+    // at least one 64-key round per range (one tile per compute wavefront):
+    // with few sequences, more and shorter ranges measured faster than
+    // fewer, longer ones now that the merge takes many ranges per round trip
     const int64_t most = (steps + kMinSplitSteps - 1) / kMinSplitSteps;
     if (splits > most) splits = most;
     if (splits > kMaxSplits) splits = kMaxSplits;

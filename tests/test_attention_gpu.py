@@ -162,17 +162,19 @@ def test_block_sizes(block_size):
 
 
 @pytest.mark.parametrize("kv_fp8", [False, True])
-@pytest.mark.parametrize("lengths", [(8192, 3000), (2048,), (1500, 40, 0)])
-def test_range_merge_group_sizes(lengths, kv_fp8):
-    """Few sequences split into many ranges: 64 ranges (four wavefronts
-    share a head's ranges and meet in LDS), 16 and 12 ranges (one wavefront
-    takes them in one group); short and empty sequences leave whole ranges
-    without keys."""
+@pytest.mark.parametrize("lengths,splits", [((8192, 3000), 128), ((4096, 3000), 64), ((1024,), 16),
+                                            ((768, 40, 0), 12), ((700,) * 40, 6)],
+                         ids=["128", "64", "16", "12", "6"])
+def test_range_merge_group_sizes(lengths, splits, kv_fp8):
+    """Few sequences split into many ranges: 128 and 64 ranges (four
+    wavefronts share a head's ranges and meet in LDS), 16 and 12 ranges (one
+    wavefront takes them in one group of 16), 6 ranges (a group of 8); short
+    and empty sequences leave whole ranges without keys."""
     w = I.attn_custom(len(lengths), 16, lengths, kv_fp8=kv_fp8, name=f"ranges{len(lengths)}")
     plan = M.attn_plan(M.AttnDims(w.batch, w.heads, w.num_blocks, w.block_size, w.max_blocks,
                                   w.max_blocks * w.block_size), M.ATTN_KV_FP8 if kv_fp8 else 0)
-    assert plan.splits == {2: 64, 1: 16, 3: 12}[len(lengths)]
-    check(w, f"ranges lengths={lengths} kv_fp8={kv_fp8} splits={plan.splits}")
+    assert plan.splits == splits
+    check(w, f"ranges lengths={lengths[:3]} kv_fp8={kv_fp8} splits={plan.splits}")
 
 
 @pytest.mark.parametrize("lengths,kv_fp8", [((1 << 18,), True), ((1 << 18, 3), False)])
