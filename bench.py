@@ -653,7 +653,7 @@ def main() -> int:
                    "cache": f"[{w.num_blocks},{w.block_size},576] {'e4m3' if w.kv_fp8 else 'bf16'}",
                    "q_out": "e4m3" if w.q_fp8 else "bf16", "rope": w.rope,
                    "buffer_sets": args.buffer_sets,
-                   "mapping": "small_t" if pl.mapping == 0 else "large_t",
+                   "mapping": {0: "small_t", 1: "large_t", 2: "mid_t"}[pl.mapping],
                    "streaming": bool(pl.streaming),
                    "grid_blocks": pl.grid_blocks, "block_threads": pl.block_threads,
                    "rows_per_wave": pl.rows_per_wave, "tail_steps": pl.tail_steps},

@@ -63,17 +63,20 @@ extern "C" {
 #define MLA_DQ_TABLE_BF16 (1u << 5) /* rope_cos_sin holds bf16 instead of
                                        fp32; needs ROPE                    */
 /* Launch overrides for tests and sweeps; they never change the results.
- * By default the library picks the latency mapping (one latent row per
- * wavefront in 64-thread workgroups) while T * (H + 1) is small and the
- * throughput mapping (256-thread workgroups, tails batched) above a measured
- * row threshold; the page's launcher makes the same token-count-dependent
- * choice ("implementation breakdown" items 1 and 3).  Independently, loads
- * and stores stream past the caches (non-temporal) once one call moves more
- * bytes than the Infinity Cache can keep. */
-#define MLA_DQ_FORCE_SMALL_T (1u << 8)  /* latency mapping                 */
+ * By default the library picks, by the row count T * (H + 1), one of three
+ * mappings at measured row thresholds: the latency mapping (one latent row
+ * per wavefront, 64-thread workgroups) for the fewest rows, the same in
+ * 128-thread workgroups next, and the throughput mapping (256-thread
+ * workgroups, tails batched, rope table staged in LDS) above; the page's
+ * launcher makes the same token-count-dependent choice ("implementation
+ * breakdown" items 1 and 3).  Independently, loads and stores stream past
+ * the caches (non-temporal) once one call moves more bytes than the
+ * Infinity Cache can keep.  At most one mapping override may be set. */
+#define MLA_DQ_FORCE_SMALL_T (1u << 8)  /* latency mapping, 64 threads     */
 #define MLA_DQ_FORCE_LARGE_T (1u << 9)  /* throughput mapping              */
 #define MLA_DQ_FORCE_STREAM  (1u << 10) /* non-temporal loads and stores   */
 #define MLA_DQ_FORCE_CACHED  (1u << 11) /* default cache policy            */
+#define MLA_DQ_FORCE_MID_T   (1u << 12) /* latency mapping, 128 threads    */
 
 /* ---- return codes ------------------------------------------------------ */
 #define MLA_DQ_OK          0
@@ -150,19 +153,22 @@ const char* mla_dq_strerror(int code);
  * lane of one wavefront) and its 64-wide positional tail (8 chunks: 8 lanes,
  * so 8 rows' tails per wavefront). */
 typedef struct mla_dq_launch_plan {
-    int32_t mapping;          /* 0 = small-T (latency), 1 = large-T (throughput) */
+    int32_t mapping;          /* 0 = small-T (latency, 64 threads),
+                                 1 = large-T (throughput),
+                                 2 = mid-T (latency, 128 threads)              */
     int32_t streaming;        /* 1 = non-temporal loads and stores               */
     int32_t block_threads;    /* threads per workgroup (a multiple of 64)        */
     int32_t rows_per_wave;    /* latent rows per wavefront                       */
     int32_t tail_steps;       /* steps of 8 tails per wavefront                  */
     int32_t reserved;
-    int64_t small_rows_max;   /* row threshold in force                          */
+    int64_t small_rows_max;   /* row threshold of the small-T mapping in force   */
     int64_t stream_bytes_min; /* byte threshold in force                         */
     int64_t bytes;            /* bytes the call reads and writes                 */
     int64_t tail_blocks;      /* workgroups doing positional tails (first)       */
     int64_t latent_blocks;    /* workgroups doing latent parts (after them)      */
     int64_t grid_blocks;      /* tail_blocks + latent_blocks                     */
     int64_t total_rows;       /* T * (H + 1)                                     */
+    int64_t mid_rows_max;     /* row threshold of the mid-T mapping in force     */
 } mla_dq_launch_plan;
 
 /* Returns MLA_DQ_OK and fills *plan, or a negative code for bad dims/flags.

@@ -27,6 +27,7 @@ FORCE_SMALL_T = 1 << 8
 FORCE_LARGE_T = 1 << 9
 FORCE_STREAM = 1 << 10
 FORCE_CACHED = 1 << 11
+FORCE_MID_T = 1 << 12
 
 OK = 0
 ERR_NULL = -1
@@ -53,7 +54,7 @@ class LaunchPlan(ctypes.Structure):
                 ("small_rows_max", ctypes.c_int64), ("stream_bytes_min", ctypes.c_int64),
                 ("bytes", ctypes.c_int64), ("tail_blocks", ctypes.c_int64),
                 ("latent_blocks", ctypes.c_int64), ("grid_blocks", ctypes.c_int64),
-                ("total_rows", ctypes.c_int64)]
+                ("total_rows", ctypes.c_int64), ("mid_rows_max", ctypes.c_int64)]
 
 
 class MlaDqError(RuntimeError):

@@ -46,6 +46,11 @@ int64_t small_rows_max() {
     return v;
 }
 
+int64_t mid_rows_max() {
+    static const int64_t v = env_int64("MLA_DQ_MID_ROWS_MAX", kDefaultMidRowsMax);
+    return v;
+}
+
 int64_t stream_bytes_min() {
     static const int64_t v = env_int64("MLA_DQ_STREAM_BYTES_MIN", kDefaultStreamBytesMin);
     return v;
@@ -69,11 +74,13 @@ int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
     if (d == nullptr) return MLA_DQ_ERR_NULL;
     const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FP16 |
                            MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16 | MLA_DQ_FORCE_SMALL_T |
-                           MLA_DQ_FORCE_LARGE_T | MLA_DQ_FORCE_STREAM | MLA_DQ_FORCE_CACHED;
+                           MLA_DQ_FORCE_LARGE_T | MLA_DQ_FORCE_STREAM | MLA_DQ_FORCE_CACHED |
+                           MLA_DQ_FORCE_MID_T;
     if (flags & ~known) return MLA_DQ_ERR_FLAGS;
     if ((flags & (MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16)) && !(flags & MLA_DQ_ROPE))
         return MLA_DQ_ERR_FLAGS;
-    if ((flags & MLA_DQ_FORCE_SMALL_T) && (flags & MLA_DQ_FORCE_LARGE_T)) return MLA_DQ_ERR_FLAGS;
+    const uint32_t forced_mappings = flags & (MLA_DQ_FORCE_SMALL_T | MLA_DQ_FORCE_MID_T | MLA_DQ_FORCE_LARGE_T);
+    if (forced_mappings & (forced_mappings - 1)) return MLA_DQ_ERR_FLAGS;   // more than one
     if ((flags & MLA_DQ_FORCE_STREAM) && (flags & MLA_DQ_FORCE_CACHED)) return MLA_DQ_ERR_FLAGS;
     const int64_t T = d->num_tokens, H = d->num_heads;
     if (T < 0 || H < 1 || d->num_blocks < 1 || d->block_size < 1) return MLA_DQ_ERR_DIM;
@@ -107,15 +114,16 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     if (rc < 0) return rc;
     const int64_t T = d->num_tokens, H = d->num_heads;
     const int64_t rows = T * (H + 1);
-    const int64_t rows_thr = small_rows_max(), bytes_thr = stream_bytes_min();
+    const int64_t rows_thr = small_rows_max(), mid_thr = mid_rows_max(), bytes_thr = stream_bytes_min();
     const int64_t bytes = call_bytes(d, flags);
-    int mapping = rows <= rows_thr ? 0 : 1;
+    int mapping = rows <= rows_thr ? 0 : (rows <= mid_thr ? 2 : 1);
     if (flags & MLA_DQ_FORCE_SMALL_T) mapping = 0;
+    if (flags & MLA_DQ_FORCE_MID_T) mapping = 2;
     if (flags & MLA_DQ_FORCE_LARGE_T) mapping = 1;
     int streaming = bytes >= bytes_thr ? 1 : 0;
     if (flags & MLA_DQ_FORCE_STREAM) streaming = 1;
     if (flags & MLA_DQ_FORCE_CACHED) streaming = 0;
-    const Mapping& m = mapping == 0 ? kSmallMapping : kLargeMapping;
+    const Mapping& m = mapping == 0 ? kSmallMapping : (mapping == 2 ? kMidMapping : kLargeMapping);
     const int64_t latent_per_block = int64_t(m.block / 64) * m.rows_per_wave;
     const int64_t tails_per_block = int64_t(m.block / 8) * m.tail_steps;
     int64_t tail_blocks = (rows + tails_per_block - 1) / tails_per_block;
@@ -137,6 +145,7 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     out->latent_blocks = (rows + latent_per_block - 1) / latent_per_block;
     out->grid_blocks = out->tail_blocks + out->latent_blocks;
     out->total_rows = rows;
+    out->mid_rows_max = mid_thr;
     return MLA_DQ_OK;
 }
 

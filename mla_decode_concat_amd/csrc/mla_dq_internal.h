@@ -16,6 +16,9 @@
 #ifndef MLA_DQ_SMALL_BLOCK
 #define MLA_DQ_SMALL_BLOCK 64
 #endif
+#ifndef MLA_DQ_MID_BLOCK
+#define MLA_DQ_MID_BLOCK 128
+#endif
 #ifndef MLA_DQ_LARGE_BLOCK
 #define MLA_DQ_LARGE_BLOCK 256
 #endif
@@ -25,13 +28,16 @@
 #ifndef MLA_DQ_LARGE_TAIL_STEPS
 #define MLA_DQ_LARGE_TAIL_STEPS 2
 #endif
-// Small-T mapping while T * (H + 1) <= this many rows: the most rows whose
-// 64-thread latent and tail workgroups (rows + rows / 8) still fit in one
-// round of 16 workgroups on each of the 256 CUs.  Measured on MI355X, the
-// latency mapping wins up to here and the throughput mapping beyond, for
-// 16 to 128 heads.
+// Small-T mapping while T * (H + 1) <= the first threshold, mid-T mapping
+// (the same latency settings in 128-thread workgroups) up to the second,
+// throughput mapping above.  Measured on MI355X for 16 to 128 heads: the
+// 64-thread workgroups win up to about 900 rows, the 128-thread ones up to
+// about 5000 to 6000.
 #ifndef MLA_DQ_SMALL_ROWS_MAX_DEFAULT
-#define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 3640
+#define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 896
+#endif
+#ifndef MLA_DQ_MID_ROWS_MAX_DEFAULT
+#define MLA_DQ_MID_ROWS_MAX_DEFAULT 5120
 #endif
 // Streaming (non-temporal) loads and stores once a call moves at least this
 // many bytes: above the 256 MB Infinity Cache nothing survives to the next
@@ -87,11 +93,19 @@ struct Mapping {
     int tail_steps;
 };
 constexpr Mapping kSmallMapping{MLA_DQ_SMALL_BLOCK, 1, 1};
+constexpr Mapping kMidMapping{MLA_DQ_MID_BLOCK, 1, 1};
 constexpr Mapping kLargeMapping{MLA_DQ_LARGE_BLOCK, MLA_DQ_LARGE_ROWS_PER_WAVE,
                                 MLA_DQ_LARGE_TAIL_STEPS};
+// The kernel tells the latency mappings from the throughput mapping by the
+// workgroup size.
+static_assert(kSmallMapping.block != kLargeMapping.block && kMidMapping.block != kLargeMapping.block &&
+                  kSmallMapping.block != kMidMapping.block,
+              "the three mappings need distinct workgroup sizes");
 // Thresholds (overridable with the environment variables
-// MLA_DQ_SMALL_ROWS_MAX and MLA_DQ_STREAM_BYTES_MIN, read once).
+// MLA_DQ_SMALL_ROWS_MAX, MLA_DQ_MID_ROWS_MAX and MLA_DQ_STREAM_BYTES_MIN,
+// read once).
 constexpr int64_t kDefaultSmallRowsMax = MLA_DQ_SMALL_ROWS_MAX_DEFAULT;
+constexpr int64_t kDefaultMidRowsMax = MLA_DQ_MID_ROWS_MAX_DEFAULT;
 constexpr int64_t kDefaultStreamBytesMin = MLA_DQ_STREAM_BYTES_MIN_DEFAULT;
 
 constexpr int64_t kRowChunks = 72;   // 576 elements / 8 per 16-byte chunk

@@ -30,13 +30,15 @@
 // first because their dependency chain (position -> table row -> rotate) is
 // the longer one.
 //
-// Two mappings.  Small token counts are latency-bound, so every wavefront
-// takes one latent row (and 8 tails) and all loads are in flight at once
-// across as many CUs as possible.  Large token counts are bandwidth-bound,
-// so each wavefront takes several latent rows, issuing all their loads
-// before its first store.  The page's kernel makes the same token-count-
-// dependent choice with whole warps (implementation breakdown item 1); the
-// threshold here is set by measurement on MI355X.
+// Three mappings, chosen by the row count.  Small and mid token counts are
+// latency-bound: every wavefront takes one latent row (and 8 tails), all
+// loads are in flight at once, and the activations go out first; the small
+// mapping uses one-wavefront workgroups, the mid mapping two-wavefront ones.
+// Large token counts are bandwidth-bound: 256-thread workgroups batch two
+// steps of tails per wavefront and stage the rope table rows in LDS.  The
+// page's kernel makes the same token-count-dependent choice with whole warps
+// (implementation breakdown item 1); the thresholds here are set by
+// measurement on MI355X.
 //
 // Loads that do not depend on the upstream projection (slot, position,
 // scale) are issued before the activations, as the page's kernel reorders
@@ -475,9 +477,10 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
 template <int BLOCK, int RPW, int TAIL_STEPS, bool STREAM, bool VAR, bool ROPE, bool QF8, bool KVF8>
 __global__ void __launch_bounds__(BLOCK)
 mla_dq_epilogue_kernel(const KernelArgs a) {
-    // The latency mapping issues the activation loads before anything the
-    // stores alone need; the throughput mapping reads slots and scales first.
-    constexpr bool kSmall = BLOCK == kSmallMapping.block;
+    // The latency mappings (small-T and mid-T workgroup sizes) issue the
+    // activation loads before anything the stores alone need; the throughput
+    // mapping reads slots and scales first.
+    constexpr bool kSmall = BLOCK != kLargeMapping.block;
     constexpr bool LATENT_LF = kSmall ? MLA_DQ_SMALL_LATENT_LF : MLA_DQ_LARGE_LATENT_LF;
     constexpr bool TAIL_LF = kSmall ? MLA_DQ_SMALL_TAIL_LF : MLA_DQ_LARGE_TAIL_LF;
     constexpr bool TABLE_LDS = kSmall ? MLA_DQ_SMALL_TABLE_LDS : MLA_DQ_LARGE_TABLE_LDS;
@@ -524,6 +527,9 @@ static hipError_t launch_mapping(const KernelArgs& a, const mla_dq_launch_plan& 
     if (plan.mapping == 0)
         return launch_flags<kSmallMapping.block, kSmallMapping.rows_per_wave,
                             kSmallMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
+    if (plan.mapping == 2)
+        return launch_flags<kMidMapping.block, kMidMapping.rows_per_wave,
+                            kMidMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
     return launch_flags<kLargeMapping.block, kLargeMapping.rows_per_wave,
                         kLargeMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
 }

@@ -59,10 +59,24 @@ def test_flag_and_code_values_match_header():
     assert val("MLA_DQ_TABLE_BF16") == M.TABLE_BF16
     assert val("MLA_DQ_FORCE_STREAM") == M.FORCE_STREAM
     assert val("MLA_DQ_FORCE_CACHED") == M.FORCE_CACHED
+    assert val("MLA_DQ_FORCE_MID_T") == M.FORCE_MID_T
     for name, v in (("MLA_DQ_ERR_NULL", B.ERR_NULL), ("MLA_DQ_ERR_ALIGN", B.ERR_ALIGN),
                     ("MLA_DQ_ERR_DIM", B.ERR_DIM), ("MLA_DQ_ERR_FLAGS", B.ERR_FLAGS),
                     ("MLA_DQ_ERR_LAUNCH", B.ERR_LAUNCH), ("MLA_DQ_ERR_ALIAS", B.ERR_ALIAS)):
         assert int(re.search(rf"#define {name}\s+(-?\d+)", text).group(1)) == v
+
+
+def test_plan_and_dims_structs_match_header_layout():
+    """The ctypes mirrors of mla_dq_launch_plan and mla_dq_dims list the
+    header's fields in the header's order and types."""
+    import ctypes
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct mla_dq_launch_plan \{(.*?)\} mla_dq_launch_plan;", text, re.S).group(1)
+    fields = re.findall(r"(int32_t|int64_t)\s+(\w+);", body)
+    want = [(n, ctypes.c_int32 if t == "int32_t" else ctypes.c_int64) for t, n in fields]
+    assert [(n, t) for n, t in B.LaunchPlan._fields_] == want
+    body = re.search(r"typedef struct mla_dq_dims \{(.*?)\} mla_dq_dims;", text, re.S).group(1)
+    assert [n for n, _ in B.Dims._fields_] == re.findall(r"int64_t\s+(\w+);", body)
 
 
 def test_strerror_every_code():
@@ -105,7 +119,9 @@ def test_null_dims():
     assert _call(_ptrs(), 0, None) == B.ERR_NULL
 
 
-@pytest.mark.parametrize("flags", [1 << 6, 1 << 12, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+@pytest.mark.parametrize("flags", [1 << 6, 1 << 13, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+                                   M.FORCE_SMALL_T | M.FORCE_MID_T, M.FORCE_MID_T | M.FORCE_LARGE_T,
+                                   M.FORCE_SMALL_T | M.FORCE_MID_T | M.FORCE_LARGE_T,
                                    M.FORCE_STREAM | M.FORCE_CACHED, M.ROPE_GPTJ, M.TABLE_BF16,
                                    M.ROPE_GPTJ | M.TABLE_BF16 | M.FP16])
 def test_bad_flags(flags):
@@ -206,16 +222,17 @@ def _bytes(T, H, flags):
 
 def test_plan_threshold_and_coverage():
     pl = M.plan(_dims(T=1, H=16), 0)
-    rows = pl.small_rows_max           # the latency mapping's largest launch: one round of
-    assert rows + (rows + 7) // 8 <= 16 * 256 < rows + 1 + (rows + 8) // 8   # 64-thread groups
-    for T in (1, 2, 63, 64, 65, 135, 136, 214, 215, 256, 8192):
+    assert 0 < pl.small_rows_max <= pl.mid_rows_max
+    for T in (1, 2, 52, 53, 63, 64, 65, 135, 136, 214, 215, 256, 301, 302, 8192):
         for H in (1, 16, 128):
             for flags in (0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8 | M.KV_FP8,
                           M.ROPE | M.ROPE_GPTJ | M.TABLE_BF16 | M.FP16):
                 pl = M.plan(_dims(T=T, H=H), flags)
                 rows = T * (H + 1)
                 assert pl.total_rows == rows
-                assert pl.mapping == (0 if rows <= pl.small_rows_max else 1)
+                want = 0 if rows <= pl.small_rows_max else (2 if rows <= pl.mid_rows_max else 1)
+                assert pl.mapping == want
+                assert pl.block_threads == {0: 64, 2: 128, 1: 256}[pl.mapping]
                 assert pl.bytes == _bytes(T, H, flags)
                 assert pl.streaming == (1 if pl.bytes >= pl.stream_bytes_min else 0)
                 assert pl.block_threads % 64 == 0
@@ -227,6 +244,8 @@ def test_plan_threshold_and_coverage():
                 assert pl.grid_blocks == pl.tail_blocks + pl.latent_blocks
     assert M.plan(_dims(T=1), M.FORCE_LARGE_T).mapping == 1
     assert M.plan(_dims(T=10 ** 5), M.FORCE_SMALL_T).mapping == 0
+    assert M.plan(_dims(T=1), M.FORCE_MID_T).mapping == 2
+    assert M.plan(_dims(T=10 ** 5), M.FORCE_MID_T).mapping == 2
     assert M.plan(_dims(T=1), M.FORCE_STREAM).streaming == 1
     assert M.plan(_dims(T=10 ** 5, H=128), M.FORCE_CACHED).streaming == 0
     assert M.plan(_dims(T=0), 0).grid_blocks == 0
@@ -234,12 +253,13 @@ def test_plan_threshold_and_coverage():
 
 def test_plan_defaults_match_measured_choice():
     """The 8192-token workload streams on the throughput mapping; the
-    1/64/65-token workloads use the latency mapping with the default policy."""
+    1-token workload uses the 64-thread latency mapping and the 64/65-token
+    workloads the 128-thread one, with the default cache policy."""
     big = M.plan(_dims(T=8192, H=16, NB=4096), M.ROPE | M.KV_FP8)
     assert (big.mapping, big.streaming) == (1, 1)
-    for T in (1, 64, 65):
+    for T, mapping in ((1, 0), (64, 2), (65, 2)):
         p = M.plan(_dims(T=T, H=16), M.ROPE | M.Q_FP8 | M.KV_FP8)
-        assert (p.mapping, p.streaming) == (0, 0)
+        assert (p.mapping, p.streaming) == (mapping, 0)
 
 
 def test_plan_rejects_bad_input():
@@ -252,11 +272,12 @@ def test_plan_rejects_bad_input():
 def test_threshold_env_override_in_fresh_process():
     code = ("import mla_decode_concat_amd as M; from mla_decode_concat_amd import _binding as B;"
             "d=B.Dims(); d.num_tokens=1000; d.num_heads=16; d.num_blocks=1; d.block_size=64;"
-            "p=M.plan(d,0); print(p.small_rows_max, p.mapping, p.stream_bytes_min, p.streaming)")
-    env = dict(os.environ, MLA_DQ_SMALL_ROWS_MAX="17000", MLA_DQ_STREAM_BYTES_MIN="1000",
-               PYTHONPATH=ROOT)
+            "p=M.plan(d,0); print(p.small_rows_max, p.mapping, p.stream_bytes_min, p.streaming,"
+            " p.mid_rows_max); d.num_tokens=1500; print(M.plan(d,0).mapping)")
+    env = dict(os.environ, MLA_DQ_SMALL_ROWS_MAX="17000", MLA_DQ_MID_ROWS_MAX="30000",
+               MLA_DQ_STREAM_BYTES_MIN="1000", PYTHONPATH=ROOT)
     out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
-    assert out.stdout.split() == ["17000", "0", "1000", "1"]
+    assert out.stdout.split() == ["17000", "0", "1000", "1", "30000", "2"]
 
 
 # ---- fast division used by the kernel's index decode --------------------------

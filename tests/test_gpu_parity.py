@@ -133,13 +133,14 @@ def test_workload_matches_oracle(name):
 
 
 LAUNCHES = [M.FORCE_SMALL_T | M.FORCE_CACHED, M.FORCE_SMALL_T | M.FORCE_STREAM,
+            M.FORCE_MID_T | M.FORCE_CACHED, M.FORCE_MID_T | M.FORCE_STREAM,
             M.FORCE_LARGE_T | M.FORCE_CACHED, M.FORCE_LARGE_T | M.FORCE_STREAM]
 
 
 @pytest.mark.parametrize("name", ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8",
                                   "t256_h128_rope_qfp8"])
 def test_forced_launches_agree(name):
-    """Both mappings and both cache policies give identical bytes on
+    """All three mappings and both cache policies give identical bytes on
     identical inputs (the page's split path is bitwise identical to the
     unsplit one)."""
     w = I.WORKLOADS[name]
@@ -207,7 +208,9 @@ def test_throughput_mapping_few_heads(T, H, fl):
     inp = I.make_inputs(w, seed=7 * T + H)
     ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T, case=f"few heads large T={T} H={H} {fl}")
     qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"few heads small T={T} H={H} {fl}")
+    qm, cm = run_gpu(w, inp, M.FORCE_MID_T, case=f"few heads mid T={T} H={H} {fl}")
     assert np.array_equal(ql, qs) and np.array_equal(cl, cs)
+    assert np.array_equal(qm, qs) and np.array_equal(cm, cs)
     check_against_oracle(w, inp, ql, cl)
 
 
@@ -386,13 +389,15 @@ VARIANTS = [("fp16", "neox", "f32"), ("bf16", "gptj", "f32"), ("bf16", "neox", "
 @pytest.mark.parametrize("T,H", [(37, 5), (300, 16)])
 def test_variants_match_oracle(dtype, style, table, qf, kf, T, H):
     """fp16 activations, interleaved rotation and a bf16 table, in every FP8
-    mode, on both mappings (forced) and against the oracle."""
+    mode, on all three mappings (forced) and against the oracle."""
     w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=True, q_fp8=qf, kv_fp8=kf,
                  q_scale=0.04, kv_scale=0.3, dtype=dtype, rope_style=style, table_dtype=table)
     inp = I.make_inputs(w, seed=T + H)
     qs, cs = run_gpu(w, inp, M.FORCE_SMALL_T, case=f"variant {dtype}/{style}/{table} small")
     ql, cl = run_gpu(w, inp, M.FORCE_LARGE_T | M.FORCE_STREAM, case=f"variant {dtype}/{style}/{table} large")
+    qm, cm = run_gpu(w, inp, M.FORCE_MID_T, case=f"variant {dtype}/{style}/{table} mid")
     assert np.array_equal(qs, ql) and np.array_equal(cs, cl)
+    assert np.array_equal(qs, qm) and np.array_equal(cs, cm)
     check_against_oracle(w, inp, qs, cs)
 
 
@@ -409,7 +414,8 @@ def _random_case(i: int):
     style = "gptj" if rope and rng.integers(3) == 0 else "neox"
     table = "bf16" if rope and rng.integers(3) == 0 else "f32"
     nb = (T + bs - 1) // bs + int(rng.integers(0, 3))
-    force = [0, M.FORCE_SMALL_T, M.FORCE_LARGE_T, M.FORCE_LARGE_T | M.FORCE_STREAM][int(rng.integers(4))]
+    force = [0, M.FORCE_SMALL_T, M.FORCE_MID_T, M.FORCE_LARGE_T,
+             M.FORCE_LARGE_T | M.FORCE_STREAM][int(rng.integers(5))]
     w = I.custom(T, H, num_blocks=nb, block_size=bs, rope=rope, q_fp8=qf, kv_fp8=kf,
                  q_scale=float(rng.choice([0.05, 0.3, 1.0])), kv_scale=float(rng.choice([0.05, 2.0])),
                  dtype=dtype, rope_style=style, table_dtype=table,
