@@ -489,14 +489,19 @@ def test_page_call_with_variants():
     assert_same(bits(dev["cache"].cpu()), want_cache, "cache", True)
 
 
-def test_decode_slice_views_in_a_graph():
+@pytest.mark.parametrize("T,H", [(64, 16), (8, 128)])
+@pytest.mark.parametrize("force", ["plan", "small", "mid", "large"])
+def test_decode_slice_views_in_a_graph(T, H, force):
     """The epilogue reads its inputs as strided views of upstream GEMM outputs
     (q_pe inside [T,H,192], ql_nope as the transposed [H,T,512] product,
     kv_c/k_pe inside one [T,576] row), captured with the producers in a HIP
-    graph; every replay equals the oracle on the materialised inputs."""
-    announce("decode slice in a graph")
+    graph, under the plan's mapping and each forced one; every replay equals
+    the oracle on the materialised inputs."""
+    announce(f"decode slice in a graph T={T} H={H} mapping={force}")
     import bench
-    ds = bench.DecodeSlice(64, 16, DEV)
+    ds = bench.DecodeSlice(T, H, DEV)
+    ds.flags |= {"plan": 0, "small": M.FORCE_SMALL_T, "mid": M.FORCE_MID_T,
+                 "large": M.FORCE_LARGE_T}[force]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -504,8 +509,8 @@ def test_decode_slice_views_in_a_graph():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     ql_nope, q_pe, kv_c, k_pe = ds.producers()
-    assert ql_nope.stride() == (512, 64 * 512, 1) and q_pe.stride() == (16 * 192, 192, 1)
-    w = I.custom(64, 16, num_blocks=1, rope=True, q_fp8=True, kv_fp8=True)
+    assert ql_nope.stride() == (512, T * 512, 1) and q_pe.stride() == (H * 192, 192, 1)
+    w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
     inp = I.make_inputs(w)
     inp.update(ql_nope=ql_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(),
                kv_c=kv_c.cpu().contiguous(), k_pe=k_pe.cpu().contiguous())
