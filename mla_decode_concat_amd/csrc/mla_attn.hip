@@ -779,6 +779,11 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
 // rescales what is already summed when a later group raises it (ranges
 // without keys weigh zero).
 constexpr int kCombineThreads = 256;
+// The merge of up to 16 ranges runs one wavefront per workgroup: with few
+// sequences its handful of wavefronts then spread over as many CUs (measured
+// 0.4-0.6 us faster per call at 1 x 1024 and 8 x 512 keys than four per
+// workgroup, and the same at 64 sequences).
+constexpr int kNarrowThreads = 64;
 
 // Ranges [s_begin, s_end) of one (sequence, head) into one wavefront's
 // running (max M, weight sum den, weighted output acc over dims 8l .. 8l+7).
@@ -849,11 +854,11 @@ __device__ __forceinline__ void combine_write(const Args& a, int bh, int lane, f
     *reinterpret_cast<u32x4*>(a.out + (size_t)bh * kValue + 8 * lane) = packed;
 }
 
-// Up to sixteen ranges: one wavefront per (sequence, head), four per workgroup.
+// Up to sixteen ranges: one wavefront per (sequence, head) and per workgroup.
 template <bool KVF8, int G>
-__global__ void __launch_bounds__(kCombineThreads) mla_attn_combine_kernel(const Args a) {
+__global__ void __launch_bounds__(kNarrowThreads) mla_attn_combine_kernel(const Args a) {
     const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);   // b * H + h
+    const int bh = blockIdx.x * (kNarrowThreads / 64) + (threadIdx.x >> 6);   // b * H + h
     // No early exit: a wavefront past the last head merges the last head
     // again and stores nothing, so the argument loads and the first partial
     // loads do not wait on a bounds test.
@@ -1029,8 +1034,8 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const uint32_t heads = uint32_t(a.B * a.H), per_block = kCombineThreads / 64;
-    const dim3 cgrid((heads + per_block - 1) / per_block), cblock(kCombineThreads);
+    const uint32_t heads = uint32_t(a.B * a.H), per_block = kNarrowThreads / 64;
+    const dim3 cgrid((heads + per_block - 1) / per_block), cblock(kNarrowThreads), wblock(kCombineThreads);
     if (a.splits <= 4)
         hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8, 4>), cgrid, cblock, 0, stream, a);
     else if (a.splits <= 8)
@@ -1038,7 +1043,7 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     else if (a.splits <= 16)
         hipLaunchKernelGGL((mla_attn_combine_kernel<KVF8, 16>), cgrid, cblock, 0, stream, a);
     else
-        hipLaunchKernelGGL((mla_attn_combine_wide_kernel<KVF8>), dim3(heads), cblock, 0, stream, a);
+        hipLaunchKernelGGL((mla_attn_combine_wide_kernel<KVF8>), dim3(heads), wblock, 0, stream, a);
     return hipGetLastError();
 }
 
