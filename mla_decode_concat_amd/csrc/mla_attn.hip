@@ -87,6 +87,14 @@ static_assert(kWaves * 24 * 64 * 16 <= kLdsBytes, "merge buffer");
 constexpr int kTargetWorkgroupsDefault = 256;  // one resident workgroup per CU
 constexpr int kMaxSplits = 1024;               // key ranges per sequence, at most
 constexpr int kMinSplitSteps = 1;              // 64-key rounds per range, at least
+// Partial outputs of at least this many bytes per call are stored
+// non-temporally (measured, µs per call with cold caches: E4M3 64 x 4096 keys
+// 39.3 -> 36.9-37.5, 32 x 2048 keys 19.1-19.4 -> 17.8-18.1; bf16 64 x 4096
+// 64.7 -> 64.1).  With fewer the merge kernel's reads of them slow down more
+// than the stores gain (1 x 1024 keys 10.5 -> 11.0).  A kernel instance per
+// choice: with a run-time branch the compiler merges the two stores and drops
+// the non-temporal hint.
+constexpr int64_t kStreamPartialBytes = 4ll << 20;
 // The running max moves only when a pair of tiles exceeds it by more than
 // this (log2 units).
 constexpr float kRebase = 8.0f;
@@ -298,7 +306,7 @@ __device__ __forceinline__ void lds_barrier() {
 // covers 1 KB of consecutive LDS), and sums its own tiles from registers with
 // the three others' from LDS.  mb is LDS scratch of at least 96 KB that no
 // wavefront reads any more.
-template <bool KVF8, bool DIRECT, int NT>
+template <bool KVF8, bool DIRECT, bool STREAMP, int NT>
 __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDimTiles], float m, float lsum,
                                             bool compute, int b, int split, int ht, float* mb,
                                             float (&mls)[2][kWaves][16]) {
@@ -360,7 +368,11 @@ __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDim
                 *reinterpret_cast<u32x2*>(a.out + row * kValue + d0) =
                     u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
             } else {
-                *reinterpret_cast<f32x4*>(a.part_o + p * kValue + d0) = acc;
+                f32x4* dst = reinterpret_cast<f32x4*>(a.part_o + p * kValue + d0);
+                if constexpr (STREAMP)
+                    __builtin_nontemporal_store(acc, dst);
+                else
+                    *dst = acc;
             }
         }
     }
@@ -372,7 +384,7 @@ __device__ __forceinline__ void merge_waves(const Args& a, const f32x4 (&o)[kDim
     }
 }
 
-template <bool QF8, bool DIRECT>
+template <bool QF8, bool DIRECT, bool STREAMP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_attn_partial_kernel(const Args a) {
     constexpr bool KVF8 = false;   // bf16 cache (E4M3 caches go to mla_attn_ring_kernel)
@@ -554,7 +566,8 @@ mla_attn_partial_kernel(const Args a) {
             if (p0 + j < np) process(j, p0 + j);
     }
 
-    merge_waves<KVF8, DIRECT, kThreads>(a, o, m, lsum, true, b, split, ht, reinterpret_cast<float*>(smem), mls);
+    merge_waves<KVF8, DIRECT, STREAMP, kThreads>(a, o, m, lsum, true, b, split, ht, reinterpret_cast<float*>(smem),
+                                                 mls);
 }
 
 // ---- E4M3 cache: loader and compute wavefronts over an LDS ring -------------
@@ -609,7 +622,7 @@ __device__ __forceinline__ bf16x4 e4m3x4_to_bf16(uint32_t word) {
     return bf16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-template <bool QF8, bool DIRECT>
+template <bool QF8, bool DIRECT, bool STREAMP>
 __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
     __shared__ __attribute__((aligned(16))) __bf16 qlds[16 * kQStride];
@@ -769,7 +782,8 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
         }
     }
 
-    merge_waves<true, DIRECT, kRingThreads>(a, o, m, lsum, !loader, b, split, ht, reinterpret_cast<float*>(ring), mls);
+    merge_waves<true, DIRECT, STREAMP, kRingThreads>(a, o, m, lsum, !loader, b, split, ht,
+                                                     reinterpret_cast<float*>(ring), mls);
 }
 
 // Merge the key ranges of one (sequence, head).  A wavefront's lane l owns
@@ -1019,18 +1033,25 @@ bool aliased(const void* out, const void* q, const void* cache, const int32_t* b
 template <bool QF8, bool KVF8>
 hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream) {
     const dim3 grid(uint32_t(p.workgroups)), block(uint32_t(p.block_threads));
+    const bool streamp = int64_t(a.B) * a.H * a.splits * kValue * 4 >= kStreamPartialBytes;
     if constexpr (KVF8) {
         if (!p.combine) {
-            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, true, false>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false>), grid, block, 0, stream, a);
+        if (streamp)
+            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, false>), grid, block, 0, stream, a);
     } else {
         if (!p.combine) {
-            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, true, false>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false>), grid, block, 0, stream, a);
+        if (streamp)
+            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, false, false>), grid, block, 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
