@@ -85,7 +85,9 @@ extern "C" {
 #define MLA_DQ_ERR_DIM    -3 /* a dimension or stride is out of range             */
 #define MLA_DQ_ERR_FLAGS  -4 /* unknown flag bit, or contradictory FORCE bits    */
 #define MLA_DQ_ERR_LAUNCH -5 /* the HIP launch reported an error                  */
-#define MLA_DQ_ERR_ALIAS  -6 /* q_out overlaps an input or the cache              */
+#define MLA_DQ_ERR_ALIAS  -6 /* q_out or the cache overlaps an input that the
+                                flags use (activations, slots, positions, rope
+                                table, scales), or q_out overlaps the cache    */
 
 /* Shapes and input strides.  Strides are in elements (bf16) and let the
  * inputs be views of larger buffers, as the page's neighbouring GEMM change
@@ -146,6 +148,12 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
 
 /* Human-readable text for a return code; never NULL, static storage. */
 const char* mla_dq_strerror(int code);
+
+/* Hexadecimal digest of the source files (kernel sources and these headers)
+ * the library was compiled from, fixed at build time; a loader compares it
+ * with the sources it ships beside, so that a library built from other
+ * sources is refused.  Never NULL, static storage. */
+const char* mla_dq_source_digest(void);
 
 /* The launch the library would make for these dims and flags: host-only, no
  * GPU needed, no device memory touched.  The kernel splits every 576-wide

@@ -37,7 +37,8 @@ ERR_FLAGS = -4
 ERR_LAUNCH = -5
 ERR_ALIAS = -6
 
-EXPORTED_SYMBOLS = ("mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan")
+EXPORTED_SYMBOLS = ("mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan",
+                    "mla_dq_source_digest")
 
 
 class Dims(ctypes.Structure):
@@ -71,8 +72,31 @@ def library_path() -> str:
     return _build.LIB
 
 
+class StaleLibraryError(RuntimeError):
+    """The library on disk was compiled from other sources than those beside it."""
+
+
+def library_digest(lib: ctypes.CDLL) -> str:
+    lib.mla_dq_source_digest.argtypes = []
+    lib.mla_dq_source_digest.restype = ctypes.c_char_p
+    return lib.mla_dq_source_digest().decode()
+
+
+def check_digest(lib: ctypes.CDLL, want: str | None = None) -> None:
+    """Raise StaleLibraryError unless the library was built from the sources
+    now in the package (or from sources with digest ``want``)."""
+    want = _build.source_digest() if want is None else want
+    got = library_digest(lib)
+    if got != want:
+        raise StaleLibraryError(
+            f"{_build.LIB} was built from sources with digest {got}, but the sources beside it "
+            f"have digest {want}: rebuild it (python -m mla_decode_concat_amd.build)")
+
+
 def load() -> ctypes.CDLL:
-    """Load libmla_dq.so (building it first only if it does not exist)."""
+    """Load libmla_dq.so, building it first only if it does not exist.  A
+    library built from other sources than the ones beside it is refused
+    (StaleLibraryError), never used."""
     global _lib
     with _lock:
         if _lib is not None:
@@ -80,6 +104,7 @@ def load() -> ctypes.CDLL:
         if not os.path.exists(_build.LIB):
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
+        check_digest(lib)
         vp, i64p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         lib.mla_decode_q_concat_kv_insert.argtypes = [
             vp, vp, vp, vp, vp, vp, i64p, i64p, f32p, f32p, f32p, ctypes.c_uint32,

@@ -30,7 +30,13 @@ Extent extent3(const void* p, int64_t T, int64_t H, int64_t st, int64_t sh, int6
     return Extent{b, b + uintptr_t(last) * uintptr_t(elem_bytes)};
 }
 
-bool overlap(Extent x, Extent y) { return x.lo < y.hi && y.lo < x.hi; }
+Extent span(const void* p, int64_t bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Extent{b, b + uintptr_t(bytes)};
+}
+
+// An empty extent (lo == hi) overlaps nothing.
+bool overlap(Extent x, Extent y) { return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi; }
 
 int64_t env_int64(const char* name, int64_t fallback) {
     const char* s = getenv(name);
@@ -172,13 +178,20 @@ int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_
                    reinterpret_cast<uintptr_t>(q_out) + uintptr_t(T * H * 576 * (qf8 ? 1 : 2))};
     const Extent c{reinterpret_cast<uintptr_t>(cache),
                    reinterpret_cast<uintptr_t>(cache) + uintptr_t(slots * 576 * (kvf8 ? 1 : 2))};
+    // Every input the flags make the kernel read: some workgroups may read
+    // one after others have stored rows, so no output may overlap any of them.
+    const Extent none{0, 0};
+    const int64_t table_row = (flags & MLA_DQ_TABLE_BF16) ? 128 : 256;
     const Extent in[] = {
         extent3(ql_nope, T, H, d->ql_nope_stride_t, d->ql_nope_stride_h, 512, 2),
         extent3(q_pe, T, H, d->q_pe_stride_t, d->q_pe_stride_h, 64, 2),
         extent3(kv_c, T, 1, d->kv_c_stride_t, 0, 512, 2),
         extent3(k_pe, T, 1, d->k_pe_stride_t, 0, 64, 2),
-        Extent{reinterpret_cast<uintptr_t>(slot_mapping),
-               reinterpret_cast<uintptr_t>(slot_mapping) + uintptr_t(T * 8)},
+        span(slot_mapping, T * 8),
+        rope ? span(positions, T * 8) : none,
+        rope ? span(rope_cos_sin, d->max_position * table_row) : none,
+        qf8 ? span(q_scale, 4) : none,
+        kvf8 ? span(kv_scale, 4) : none,
     };
     if (overlap(q, c)) return MLA_DQ_ERR_ALIAS;
     for (const Extent& e : in)
@@ -239,6 +252,12 @@ int mla_dq_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* pla
     return mla_dq::plan(dims, flags, plan);
 }
 
+#ifndef MLA_DQ_SOURCE_DIGEST
+#define MLA_DQ_SOURCE_DIGEST "unknown"
+#endif
+
+const char* mla_dq_source_digest(void) { return MLA_DQ_SOURCE_DIGEST; }
+
 const char* mla_dq_strerror(int code) {
     switch (code) {
         case MLA_DQ_OK: return "success";
@@ -247,7 +266,7 @@ const char* mla_dq_strerror(int code) {
         case MLA_DQ_ERR_DIM: return "dimension or stride out of range";
         case MLA_DQ_ERR_FLAGS: return "unknown flag bit or contradictory launch overrides";
         case MLA_DQ_ERR_LAUNCH: return "HIP kernel launch failed";
-        case MLA_DQ_ERR_ALIAS: return "q_out overlaps an input or the cache, or the cache overlaps an input";
+        case MLA_DQ_ERR_ALIAS: return "q_out or the cache overlaps an input, or q_out overlaps the cache";
         case MLA_ATTN_ERR_WORKSPACE: return "workspace smaller than mla_decode_attention_workspace_size()";
         default: return "unknown mla_dq error code";
     }

@@ -50,26 +50,27 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 def mla_decode_attention(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
                          seq_lens: np.ndarray, sm_scale: float, q_scale: float | None = None,
-                         kv_scale: float | None = None, fp16: bool = False) -> np.ndarray:
+                         kv_scale: float | None = None, with_abs: bool = False):
     """Reference attention in float64.
 
-    q            [B, H, 576] bf16/fp16 bit patterns (uint16) or E4M3 codes (uint8)
-    cache        [num_blocks, bs, 576] bit patterns (uint16) or E4M3 codes (uint8)
+    q            [B, H, 576] bf16 bit patterns (uint16) or E4M3 codes (uint8)
+    cache        [num_blocks, bs, 576] bf16 bit patterns (uint16) or E4M3 codes (uint8)
     block_table  [B, max_blocks] int, seq_lens [B] int
     q_scale / kv_scale: per-tensor scales of E4M3 operands
-    Returns [B, H, 512] float64.
+    Returns out [B, H, 512] float64; with ``with_abs`` also the same weighted
+    sum over the absolute values, sum_j softmax(s)_j * |row_j[0:512]|, which
+    scales the rounding error of any evaluation of the weighted sum.
     """
     def decode(x, scale):
         if x.dtype == np.uint8:
             return e4m3_decode(x) * float(scale)
-        if fp16:
-            return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
         return bf16_decode(x)
 
     B, H = q.shape[0], q.shape[1]
     bs = cache.shape[1]
     qd = decode(q, q_scale)
     out = np.zeros((B, H, NOPE), dtype=np.float64)
+    mag = np.zeros((B, H, NOPE), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
         if L == 0:
@@ -82,4 +83,6 @@ def mla_decode_attention(q: np.ndarray, cache: np.ndarray, block_table: np.ndarr
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         out[b] = p @ rows[:, :NOPE]
-    return out
+        if with_abs:
+            mag[b] = p @ np.abs(rows[:, :NOPE])
+    return (out, mag) if with_abs else out

@@ -28,7 +28,8 @@ def _declared_functions(header=HEADER):
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert set(names) == {"mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan"}
+    assert set(names) == {"mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan",
+                          "mla_dq_source_digest"}
     lib = ctypes.CDLL(B.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -208,6 +209,52 @@ def test_cache_overlapping_input_is_rejected():
     p = _ptrs()
     p["cache"] = p["kv_c"] + 16
     assert _call(p, 0, _dims()) == B.ERR_ALIAS
+
+
+@pytest.mark.parametrize("name,flags", [("pos", M.ROPE), ("cs", M.ROPE),
+                                        ("cs", M.ROPE | M.TABLE_BF16), ("qs", M.Q_FP8),
+                                        ("ks", M.KV_FP8)])
+@pytest.mark.parametrize("out", ["q_out", "cache"])
+def test_output_overlapping_flagged_input_is_rejected(name, flags, out):
+    """Positions, the rope table and the scales count as inputs when the flags
+    make the kernel read them: an output over any of them is refused."""
+    d = _dims(maxpos=16)
+    p = _ptrs()
+    # the last byte the kernel would read of that input
+    last = {"pos": 4 * 8, "cs": 16 * (128 if flags & M.TABLE_BF16 else 256), "qs": 4, "ks": 4}[name] - 1
+    p[out] = (p[name] + last) // 16 * 16 - (16 if out == "q_out" else 0)
+    assert _call(p, flags, d) == B.ERR_ALIAS
+
+
+def test_loaded_library_matches_its_sources():
+    """The library on disk carries the digest of the sources beside it."""
+    from mla_decode_concat_amd import build as BLD
+    lib = ctypes.CDLL(B.library_path())
+    assert B.library_digest(lib) == BLD.source_digest()
+    B.check_digest(lib)
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    """A one-byte change in any source changes the digest, and a library
+    whose digest differs from the sources' is refused by load()."""
+    import shutil
+    from mla_decode_concat_amd import build as BLD
+    pkg = tmp_path / "mla_decode_concat_amd"
+    shutil.copytree(os.path.join(ROOT, "mla_decode_concat_amd", "csrc"), pkg / "csrc")
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    assert BLD.source_digest(str(pkg), str(tmp_path)) == BLD.source_digest()
+    for f in BLD.source_files(str(pkg), str(tmp_path)):
+        data = open(f, "rb").read()
+        open(f, "wb").write(data + b" ")
+        assert BLD.source_digest(str(pkg), str(tmp_path)) != BLD.source_digest(), f
+        open(f, "wb").write(data)
+    lib = ctypes.CDLL(B.library_path())
+    with pytest.raises(B.StaleLibraryError):
+        B.check_digest(lib, want="0" * 32)
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(BLD, "source_digest", lambda *a, **k: "f" * 32)
+    with pytest.raises(B.StaleLibraryError):
+        B.load()
 
 
 # ---- launch plan -------------------------------------------------------------

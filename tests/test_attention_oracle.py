@@ -119,3 +119,44 @@ def test_empty_sequence_gives_zeros():
     inp = I.make_attn_inputs(w)
     out = _run(w, inp)
     assert np.all(out[0] == 0) and np.any(out[1] != 0)
+
+
+def _run_abs(w, inp):
+    return A.mla_decode_attention(bits(inp["q"]), bits(inp["cache"]), inp["block_table"].numpy(),
+                                  inp["seq_lens"].numpy(), w.sm_scale,
+                                  w.q_scale if w.q_fp8 else None, w.kv_scale if w.kv_fp8 else None,
+                                  with_abs=True)
+
+
+def test_weighted_abs_single_key_and_zero_query():
+    """sum_j p_j |v_j|: one key gives |v| exactly; a zero query (uniform
+    weights) gives the mean of |v| over the sequence."""
+    w = I.attn_custom(2, 16, 1, kv_fp8=True)
+    inp = I.make_attn_inputs(w)
+    out, mag = _run_abs(w, inp)
+    assert np.array_equal(out, _run(w, inp))
+    for b in range(2):
+        assert np.array_equal(mag[b], np.abs(np.repeat(_rows(w, inp, b)[:, :512], 16, axis=0)))
+    w = I.attn_custom(2, 4, (9, 150), block_size=16)
+    inp = I.make_attn_inputs(w, seed=9)
+    inp["q"].zero_()
+    _, mag = _run_abs(w, inp)
+    for b in range(2):
+        want = np.abs(_rows(w, inp, b)[:, :512]).mean(axis=0)
+        assert np.allclose(mag[b], want[None, :], rtol=1e-12, atol=0)
+
+
+def test_weighted_abs_bounds_and_equality_for_nonnegative_values():
+    """|out| <= sum_j p_j |v_j| <= max_j |v_j| (triangle inequality, weights
+    summing to 1); with every value non-negative the two sums coincide."""
+    w = I.attn_custom(3, 16, (1, 70, 600), kv_fp8=True)
+    inp = I.make_attn_inputs(w, seed=10)
+    out, mag = _run_abs(w, inp)
+    assert np.all(np.abs(out) <= mag * (1 + 1e-12))
+    for b in range(3):
+        assert np.all(mag[b] <= np.abs(_rows(w, inp, b)[:, :512]).max(axis=0)[None, :] * (1 + 1e-12))
+    assert np.any(np.abs(out) < 0.5 * mag)       # signs cancel in the plain sum
+    raw = inp["cache"].view(torch.uint8)
+    raw &= 0x7F                                  # clear every sign bit
+    out, mag = _run_abs(w, inp)
+    assert np.allclose(out, mag, rtol=1e-12, atol=0)

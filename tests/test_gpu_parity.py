@@ -281,28 +281,104 @@ def test_strided_input_views():
     check_against_oracle(w, inp, q, cache)
 
 
-def test_out_of_range_slots_and_positions():
-    w = I.custom(6, 4, num_blocks=1, rope=True, kv_fp8=True, max_position=16)
-    inp = I.make_inputs(w, seed=4)
-    inp["slot_mapping"] = torch.tensor([-1, 64, 3, 1 << 40, -7, 63], dtype=torch.int64)
-    inp["positions"] = torch.tensor([-5, 16, 1000, 3, 15, 0], dtype=torch.int64)
-    init = np.full((1, 64, 576), 0x5A, dtype=np.uint8)
-    q, cache = run_gpu(w, inp, cache_init=init, case="out-of-range slots/positions")
+SLOT_JUNK = (-1, -7, -(1 << 40), -(1 << 63))
+POS_JUNK = (-5, -1, -(1 << 63), (1 << 63) - 1)
+
+
+def _out_of_range(inp: dict, w: I.Workload, seed: int, frac: float = 0.25):
+    """Replace a seeded fraction of the slots by padding or out-of-range
+    values (-1, -7, the slot count and past it, +-2^40, int64 extremes) and,
+    with rotation, of the positions by values outside [0, max_position)."""
+    rng = np.random.default_rng(seed)
+    S, T = w.num_slots, w.tokens
+    junk = np.array(SLOT_JUNK + (S, S + 5, 1 << 40, (1 << 63) - 1), dtype=np.int64)
+    slots = inp["slot_mapping"].numpy().copy()
+    pick = rng.random(T) < frac
+    slots[pick] = rng.choice(junk, int(pick.sum()))
+    inp["slot_mapping"] = torch.from_numpy(slots)
+    if w.rope:
+        pjunk = np.array(POS_JUNK + (w.max_position, w.max_position + 3, 1 << 40), dtype=np.int64)
+        pos = inp["positions"].numpy().copy()
+        pick = rng.random(T) < frac
+        pos[pick] = rng.choice(pjunk, int(pick.sum()))
+        inp["positions"] = torch.from_numpy(pos)
+    return inp
+
+
+def _background(w: I.Workload, seed: int) -> np.ndarray:
+    """A random cache background (finite bf16 values, or any E4M3 byte)."""
+    rng = np.random.default_rng(seed)
+    init = rng.integers(0, 256, size=(w.num_blocks, w.block_size, 576 * (1 if w.kv_fp8 else 2)),
+                        dtype=np.uint8)
+    if w.kv_fp8:
+        return init
+    return init.view(np.uint16) & np.uint16(0x3FFF)
+
+
+# (T, H, max_position): one tail step; a throughput workgroup whose staged
+# table rows include clamped positions (1-3 heads, ragged T >= 97); the mid
+# and throughput mappings at 16 heads
+EDGE_SHAPES = [(6, 4, 16), (97, 1, 16), (130, 2, 77), (200, 3, 4096), (333, 16, 64)]
+
+
+@pytest.mark.parametrize("launch", LAUNCHES, ids=lambda f: f"{f:#x}")
+@pytest.mark.parametrize("T,H,maxpos", EDGE_SHAPES, ids=lambda v: str(v))
+@pytest.mark.parametrize("kf", [False, True], ids=["kv", "KV8"])
+def test_out_of_range_slots_and_positions(T, H, maxpos, kf, launch):
+    """Padding (-1) and out-of-range slots skip the cache row and nothing
+    else; out-of-range positions are clamped into the table.  Under every
+    mapping and cache policy, on a random cache background."""
+    w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=True, q_fp8=True, kv_fp8=kf,
+                 max_position=maxpos, q_scale=0.04, kv_scale=0.3)
+    inp = _out_of_range(I.make_inputs(w, seed=4 + T), w, seed=T * 7 + H)
+    init = _background(w, seed=T)
+    q, cache = run_gpu(w, inp, launch, cache_init=init, case=f"out-of-range T={T} H={H}")
     check_against_oracle(w, inp, q, cache, cache_init=init)
 
 
-def test_duplicate_slots_leave_one_candidate():
-    w = I.custom(3, 2, num_blocks=1)
-    inp = I.make_inputs(w, seed=2)
-    inp["slot_mapping"] = torch.tensor([5, 5, 9], dtype=torch.int64)
-    q, cache = run_gpu(w, inp, case="duplicate slots")
-    rows = cache.reshape(-1, 576)
-    # each 8-element chunk of the shared row comes from one of the two tokens
-    cands = [bits(torch.cat([inp["kv_c"][t], inp["k_pe"][t]])).reshape(72, 8) for t in (0, 1)]
-    got = rows[5].reshape(72, 8)
-    for c in range(72):
-        assert any(np.array_equal(got[c], cand[c]) for cand in cands), c
-    assert np.array_equal(rows[9], bits(torch.cat([inp["kv_c"][2], inp["k_pe"][2]])))
+@pytest.mark.parametrize("launch", LAUNCHES, ids=lambda f: f"{f:#x}")
+def test_out_of_range_slots_without_rotation(launch):
+    """The copy path (no positions read) with padding and out-of-range
+    slots, under every mapping and cache policy."""
+    w = I.custom(150, 2, num_blocks=4, q_scale=0.04, kv_scale=0.3)
+    inp = _out_of_range(I.make_inputs(w, seed=8), w, seed=9, frac=0.5)
+    init = _background(w, seed=10)
+    q, cache = run_gpu(w, inp, launch, cache_init=init, case="out-of-range slots, copy path")
+    check_against_oracle(w, inp, q, cache, cache_init=init)
+
+
+@pytest.mark.parametrize("launch", LAUNCHES, ids=lambda f: f"{f:#x}")
+@pytest.mark.parametrize("T,H", [(3, 2), (120, 3)])
+def test_duplicate_slots_leave_one_candidate(T, H, launch):
+    """Tokens that share a slot: every 8-element chunk of that row comes from
+    one of them (the header's contract); rows of unique slots are exact."""
+    w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=True, kv_fp8=True, kv_scale=0.3)
+    inp = I.make_inputs(w, seed=2 + T)
+    slots = inp["slot_mapping"].numpy().copy()
+    groups = [[0, 1]] if T == 3 else [[0, 1, 2], [5, 60], [33, 119, 64, 90]]
+    for g in groups:
+        slots[g] = slots[g[0]]
+    inp["slot_mapping"] = torch.from_numpy(slots)
+    q, cache = run_gpu(w, inp, launch, case=f"duplicate slots T={T}")
+    want_q, want_cache = oracle_run(w, inp)
+    assert_same(q, want_q, "q_out")
+    rows, want_rows = cache.reshape(-1, 576), want_cache.reshape(-1, 576)
+    shared = {int(slots[g[0]]): g for g in groups}
+    keep = np.ones(rows.shape[0], dtype=bool)
+    keep[list(shared)] = False
+    assert_same(rows[keep], want_rows[keep], "cache rows of unique slots and untouched rows")
+    w1 = I.custom(1, H, num_blocks=1, rope=True, kv_fp8=True, kv_scale=0.3)
+    for s_, g in shared.items():
+        cands = []
+        for t in g:       # the row token t alone would write
+            sub = dict(inp, slot_mapping=torch.tensor([0], dtype=torch.int64),
+                       cache=torch.zeros(1, 64, 576, dtype=torch.float8_e4m3fn))
+            for k in ("ql_nope", "q_pe", "kv_c", "k_pe", "positions"):
+                sub[k] = inp[k][t:t + 1].clone()
+            cands.append(oracle_run(w1, sub)[1].reshape(-1, 576)[0].reshape(72, 8))
+        got = rows[s_].reshape(72, 8)
+        for c in range(72):
+            assert any(np.array_equal(got[c], cand[c]) for cand in cands), (s_, c)
 
 
 def test_zero_tokens_launches_nothing():
@@ -420,16 +496,20 @@ def _random_case(i: int):
                  q_scale=float(rng.choice([0.05, 0.3, 1.0])), kv_scale=float(rng.choice([0.05, 2.0])),
                  dtype=dtype, rope_style=style, table_dtype=table,
                  max_position=int(rng.choice([1, 77, 4096])))
-    return w, force, int(rng.integers(1 << 30))
+    junk = float(rng.choice([0.0, 0.0, 0.1, 0.5]))     # share of out-of-range slots/positions
+    return w, force, int(rng.integers(1 << 30)), junk
 
 
 @pytest.mark.parametrize("i", range(24))
 def test_seeded_random_shapes_and_modes(i):
     """Random shapes, heads, block sizes, flag and variant combinations and
-    launch overrides, each against the oracle."""
-    w, force, seed = _random_case(i)
+    launch overrides, some cases with padding or out-of-range slots and
+    positions, each against the oracle."""
+    w, force, seed, junk = _random_case(i)
     inp = I.make_inputs(w, seed=seed)
-    q, cache = run_gpu(w, inp, force, case=f"random case {i} (seed {seed})")
+    if junk:
+        inp = _out_of_range(inp, w, seed=seed + 1, frac=junk)
+    q, cache = run_gpu(w, inp, force, case=f"random case {i} (seed {seed}, junk {junk})")
     check_against_oracle(w, inp, q, cache)
 
 

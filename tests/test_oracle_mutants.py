@@ -48,6 +48,8 @@ MUTANTS = [
     ("scatter_by_token", "write_row(cache + (size_t)s * kv_row_bytes", "write_row(cache + (size_t)t * kv_row_bytes"),
     ("slot_zero_skipped", "if (s < 0 || s >= num_slots) continue;", "if (s <= 0 || s >= num_slots) continue;"),
     ("q_rows_transposed", "int64_t r = t * H + h;", "int64_t r = h * T + t;"),
+    ("rope_f64_sign", "y[i0] = a * c - b * s;", "y[i0] = a * c + b * s;"),
+    ("rope_f64_dropped_term", "y[i1] = b * c + a * s;", "y[i1] = b * c;"),
 ]
 
 CHECKS = [
@@ -69,6 +71,7 @@ CHECKS = [
     lambda: P.test_oracle_matches_library_composition_all_modes((True, False, False)),
     lambda: P.test_oracle_matches_library_composition_all_modes((True, True, False)),
     P.test_out_of_range_slots_leave_cache_untouched,
+    lambda: P.test_rope_f64_is_the_complex_product_with_the_table_row(True),
 ]
 
 
@@ -131,6 +134,10 @@ ATT_MUTANTS = [
     ("e4m3_bias", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     ("scale_ignored", "return e4m3_decode(x) * float(scale)", "return e4m3_decode(x)"),
     ("last_key_dropped", "j = np.arange(L)", "j = np.arange(max(L - 1, 1))"),
+    ("abs_of_sum_not_sum_of_abs", "mag[b] = p @ np.abs(rows[:, :NOPE])",
+     "mag[b] = np.abs(p @ rows[:, :NOPE])"),
+    ("abs_weights_unnormalised", "mag[b] = p @ np.abs(rows[:, :NOPE])",
+     "mag[b] = np.exp(s) @ np.abs(rows[:, :NOPE])"),
 ]
 ATT_CHECKS = [
     AP.test_e4m3_decode_every_code_vs_torch,
@@ -140,6 +147,8 @@ ATT_CHECKS = [
     lambda: AP.test_matches_library_sdpa(False, False),
     lambda: AP.test_matches_library_sdpa(True, True),
     AP.test_zero_query_averages_values,
+    AP.test_weighted_abs_single_key_and_zero_query,
+    AP.test_weighted_abs_bounds_and_equality_for_nonnegative_values,
 ]
 
 

@@ -330,6 +330,47 @@ def test_rope_f32_within_rounding_bound_of_f64():
         assert np.all(np.abs(y32 - y64) <= bound)
 
 
+@pytest.mark.parametrize("gptj", [False, True])
+def test_rope_f64_is_the_complex_product_with_the_table_row(gptj):
+    """The float64 twin (used by the rounding-bound pins) pairs the elements
+    as the fp32 rotation does: as complex numbers (x_a + j x_b) times
+    (cos + j sin) of the same table row, computed by numpy's complex product,
+    with (a, b) = (i, i+32) or (2i, 2i+1)."""
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(12)
+    for trial in range(100):
+        p = int(rng.integers(0, 4096))
+        x = _f32(_x_bits(1500 + trial, scale=3.0)).astype(np.float64)
+        c, s = table[p, :32].astype(np.float64), table[p, 32:].astype(np.float64)
+        a, b = (x[0::2], x[1::2]) if gptj else (x[:32], x[32:])
+        z = (a + 1j * b) * (c + 1j * s)
+        want = np.empty(64)
+        if gptj:
+            want[0::2], want[1::2] = z.real, z.imag
+        else:
+            want[:32], want[32:] = z.real, z.imag
+        got = oracle.rope_f64(x.astype(np.float32), table[p, :32], table[p, 32:], gptj=gptj)
+        mag = np.repeat(np.abs(a) + np.abs(b), 2) if gptj else np.concatenate([np.abs(a) + np.abs(b)] * 2)
+        assert np.all(np.abs(got - want) <= 4 * 2.0 ** -53 * mag + 1e-300)
+
+
+def test_gptj_rope_f32_within_rounding_bound_of_f64():
+    table = I.rope_table(4096).numpy()
+    rng = np.random.default_rng(13)
+    u = 2.0 ** -24
+    for trial in range(200):
+        p = int(rng.integers(0, 4096))
+        x = _f32(_x_bits(1700 + trial, scale=5.0))
+        y32 = oracle.rope_f32(x, table[p, :32], table[p, 32:], gptj=True).astype(np.float64)
+        y64 = oracle.rope_f64(x, table[p, :32], table[p, 32:], gptj=True)
+        a, b = x[0::2].astype(np.float64), x[1::2].astype(np.float64)
+        c, s = table[p, :32].astype(np.float64), table[p, 32:].astype(np.float64)
+        t = np.empty(64)
+        t[0::2] = np.abs(a * c) + np.abs(b * s)
+        t[1::2] = np.abs(b * c) + np.abs(a * s)
+        assert np.all(np.abs(y32 - y64) <= t * (2 * u + u * u) + 1e-45)
+
+
 def test_rope_matches_library_rotate_half_fp32():
     """Eager torch fp32: x*cos + rotate_half(x)*sin, each op rounded."""
     table = I.rope_table(4096)
