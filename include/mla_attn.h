@@ -89,6 +89,37 @@ int mla_decode_attention(void* out, const void* q, const void* cache, const int3
                          float sm_scale, void* workspace, size_t workspace_bytes, uint32_t flags,
                          const mla_attn_dims* dims, void* stream);
 
+/*
+ * The same attention for callers that cannot allocate device memory or pass
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, checks and results are those of
+ * mla_decode_attention without the workspace.  When the split needs one, the
+ * partial results go to a scratch buffer of MLA_ATTN_SCRATCH_BYTES that the
+ * library keeps in device memory, one per GPU, from the library's load on
+ * that GPU until the process ends.  Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library call.
+ *
+ * MLA_ATTN_SCRATCH_BYTES covers every split of the default plan (at most 510
+ * workgroups of 16 heads, 16 776 960 bytes); a plan that needs more (only
+ * with MLA_ATTN_TARGET_WGS raised) returns MLA_ATTN_ERR_SCRATCH and launches
+ * nothing.  All calls on one GPU share its buffer, which keeps the last
+ * call's contents; each call writes every part of it that it reads, so it
+ * needs no clearing.  Calls that may overlap on one GPU (on streams without
+ * an order between them, or from threads that do not serialise them) race
+ * on the buffer: order them.  The buffer used is the one of the GPU that runs
+ * stream (the current device for a NULL stream).  Returns the codes of
+ * mla_decode_attention except MLA_ATTN_ERR_WORKSPACE, plus:
+ *   MLA_ATTN_ERR_SCRATCH (-8) the split needs more than MLA_ATTN_SCRATCH_BYTES
+ *   MLA_DQ_ERR_LAUNCH    (-5) also when the buffer's address cannot be found
+ */
+#define MLA_ATTN_SCRATCH_BYTES (16u << 20)
+#define MLA_ATTN_ERR_SCRATCH -8   /* the split needs more than MLA_ATTN_SCRATCH_BYTES */
+
+int mla_decode_attention_noalloc(void* out, const void* q, const void* cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const float* q_scale, const float* kv_scale, float sm_scale,
+                                 uint32_t flags, const mla_attn_dims* dims, void* stream);
+
 /* The split of the keys the library would use (host-only, no GPU). */
 typedef struct mla_attn_plan {
     int32_t splits;             /* key ranges per sequence                          */

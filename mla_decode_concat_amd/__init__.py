@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     MlaDqError, Dims, LaunchPlan, fused_mla_decode_q_concat_kv_cache_insert,
     mla_decode_q_concat_kv_insert, PreparedInsert, plan, strerror, load,
     ATTN_Q_FP8, ATTN_KV_FP8, AttnDims, AttnPlan, PreparedAttention, attn_plan,
-    attn_workspace_size, mla_decode_attention,
+    attn_workspace_size, mla_decode_attention, mla_decode_attention_noalloc,
 )

@@ -317,9 +317,11 @@ def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch
 ATTN_Q_FP8 = 1 << 0
 ATTN_KV_FP8 = 1 << 1
 ERR_WORKSPACE = -7
+ERR_SCRATCH = -8
+SCRATCH_BYTES = 16 << 20     # MLA_ATTN_SCRATCH_BYTES: the no-alloc entry point's buffer
 
 ATTN_EXPORTED_SYMBOLS = ("mla_decode_attention", "mla_decode_attention_workspace_size",
-                         "mla_decode_attention_plan")
+                         "mla_decode_attention_plan", "mla_decode_attention_noalloc")
 
 
 class AttnDims(ctypes.Structure):
@@ -343,6 +345,9 @@ def _attn_lib() -> ctypes.CDLL:
             vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_uint32,
             ctypes.POINTER(AttnDims), vp]
         lib.mla_decode_attention.restype = ctypes.c_int
+        lib.mla_decode_attention_noalloc.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_uint32, ctypes.POINTER(AttnDims), vp]
+        lib.mla_decode_attention_noalloc.restype = ctypes.c_int
         lib.mla_decode_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDims),
                                                             ctypes.c_uint32]
         lib.mla_decode_attention_workspace_size.restype = ctypes.c_size_t
@@ -464,4 +469,30 @@ def mla_decode_attention(q: torch.Tensor, cache: torch.Tensor, block_table: torc
         out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
     PreparedAttention(out, q, cache, block_table, seq_lens, sm_scale, q_scale, kv_scale,
                       max_seq_len)()
+    return out
+
+
+def mla_decode_attention_noalloc(out: torch.Tensor, q: torch.Tensor, cache: torch.Tensor,
+                                 block_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                                 q_scale: torch.Tensor | None = None,
+                                 kv_scale: torch.Tensor | None = None,
+                                 max_seq_len: int | None = None, stream=None) -> torch.Tensor:
+    """Decode attention into the caller's ``out`` through the entry point that
+    allocates nothing (include/mla_attn.h): split ranges use the library's
+    per-GPU scratch buffer, so calls on one GPU must be ordered.  Raises
+    MlaDqError (code ERR_SCRATCH) if the split needs more than SCRATCH_BYTES."""
+    _attn_validate(out, q, cache, block_table, seq_lens, q_scale, kv_scale)
+    d = _attn_dims(q, cache, block_table, max_seq_len)
+    args = (_ptr(out), _ptr(q), _ptr(cache), _ptr(block_table), _ptr(seq_lens), _ptr(q_scale),
+            _ptr(kv_scale), ctypes.c_float(float(sm_scale)), ctypes.c_uint32(_attn_flags(q, cache)),
+            ctypes.byref(d))
+    fn = _attn_lib().mla_decode_attention_noalloc
+    index = out.device.index
+    if index == torch.cuda.current_device():
+        rc = fn(*args, _raw_stream(index, stream))
+    else:
+        with torch.cuda.device(index):
+            rc = fn(*args, _raw_stream(index, stream))
+    if rc != OK:
+        raise MlaDqError(rc, strerror(rc))
     return out

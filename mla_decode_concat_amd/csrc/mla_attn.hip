@@ -52,6 +52,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "mla_attn.h"
 #include "mla_dq.h"
 
@@ -1068,6 +1070,99 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     return hipGetLastError();
 }
 
+// Scratch of mla_decode_attention_noalloc: the partial results of split key
+// ranges for callers that cannot allocate or pass a workspace.  Every GPU
+// the library runs on holds its own copy from the module's load until the
+// process ends.  In host code this name is only a stand-in for the device
+// symbol: kernels get the per-device address from scratch_address().
+static __device__ __align__(256) uint8_t scratch[MLA_ATTN_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the GPU that runs `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current.  NULL if the lookup fails.
+void* scratch_address(hipStream_t stream) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    static std::mutex lock;
+    static void* addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> guard(lock);
+    if (addr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+int attention(void* out, const void* q, const void* cache, const int32_t* block_table, const int32_t* seq_lens,
+              const float* q_scale, const float* kv_scale, float sm_scale, void* workspace,
+              size_t workspace_bytes, uint32_t flags, const mla_attn_dims* dims, hipStream_t stream,
+              bool use_scratch) {
+    mla_attn_plan p;
+    int rc = make_plan(dims, flags, &p);
+    if (rc != MLA_DQ_OK) return rc;
+    if (dims->batch == 0) return MLA_DQ_OK;
+    if (use_scratch && p.workspace_bytes > int64_t(MLA_ATTN_SCRATCH_BYTES)) return MLA_ATTN_ERR_SCRATCH;
+    const bool qf8 = flags & MLA_ATTN_Q_FP8, kvf8 = flags & MLA_ATTN_KV_FP8;
+    if (!out || !q || !cache || !block_table || !seq_lens) return MLA_DQ_ERR_NULL;
+    if ((qf8 && !q_scale) || (kvf8 && !kv_scale)) return MLA_DQ_ERR_NULL;
+    if (!use_scratch) {
+        if (p.workspace_bytes > 0 && !workspace) return MLA_DQ_ERR_NULL;
+        if (workspace_bytes < size_t(p.workspace_bytes)) return MLA_ATTN_ERR_WORKSPACE;
+    }
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(cache, 16) || !aligned(block_table, 4) ||
+        !aligned(seq_lens, 4) || (workspace && !aligned(workspace, 16)) ||
+        (qf8 && !aligned(q_scale, 4)) || (kvf8 && !aligned(kv_scale, 4)))
+        return MLA_DQ_ERR_ALIGN;
+    if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return MLA_DQ_ERR_DIM;
+    if (use_scratch) {
+        // the library's own buffer, only where the split needs one
+        workspace = p.workspace_bytes > 0 ? scratch_address(stream) : nullptr;
+        if (p.workspace_bytes > 0 && workspace == nullptr) return MLA_DQ_ERR_LAUNCH;
+    }
+    if (aliased(out, q, cache, block_table, seq_lens, q_scale, kv_scale, workspace, dims, p, qf8, kvf8))
+        return MLA_DQ_ERR_ALIAS;
+
+    Args a;
+    a.out = static_cast<uint16_t*>(out);
+    a.q = static_cast<const uint8_t*>(q);
+    a.cache = static_cast<const uint8_t*>(cache);
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.q_scale = q_scale;
+    a.kv_scale = kv_scale;
+    const int64_t parts = dims->batch * dims->num_heads * int64_t(p.splits);
+    a.part_o = p.workspace_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.part_m = a.part_o ? a.part_o + parts * kValue : nullptr;
+    a.part_l = a.part_m ? a.part_m + parts : nullptr;
+    a.score_scale = sm_scale * 1.4426950408889634f;
+    a.B = int32_t(dims->batch);
+    a.H = int32_t(dims->num_heads);
+    a.num_blocks = int32_t(dims->num_blocks);
+    a.block_size = int32_t(dims->block_size);
+    a.max_blocks = int32_t(dims->max_blocks_per_seq);
+    a.max_seq_len = int32_t(dims->max_seq_len);
+    a.splits = p.splits;
+    a.keys_per_split = p.keys_per_split;
+    a.head_tiles = p.head_tiles;
+    a.xcd_remap = p.xcd_remap;
+    a.grid = int32_t(p.workgroups);
+    hipError_t e;
+    if (qf8)
+        e = kvf8 ? launch_pair<true, true>(a, p, stream) : launch_pair<true, false>(a, p, stream);
+    else
+        e = kvf8 ? launch_pair<false, true>(a, p, stream) : launch_pair<false, false>(a, p, stream);
+    return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
+}
+
 }  // namespace mla_attn
 
 extern "C" {
@@ -1087,55 +1182,15 @@ int mla_decode_attention(void* out, const void* q, const void* cache, const int3
                          const int32_t* seq_lens, const float* q_scale, const float* kv_scale,
                          float sm_scale, void* workspace, size_t workspace_bytes, uint32_t flags,
                          const mla_attn_dims* dims, void* stream) {
-    using namespace mla_attn;
-    mla_attn_plan p;
-    int rc = make_plan(dims, flags, &p);
-    if (rc != MLA_DQ_OK) return rc;
-    if (dims->batch == 0) return MLA_DQ_OK;
-    const bool qf8 = flags & MLA_ATTN_Q_FP8, kvf8 = flags & MLA_ATTN_KV_FP8;
-    if (!out || !q || !cache || !block_table || !seq_lens) return MLA_DQ_ERR_NULL;
-    if ((qf8 && !q_scale) || (kvf8 && !kv_scale)) return MLA_DQ_ERR_NULL;
-    if (p.workspace_bytes > 0 && !workspace) return MLA_DQ_ERR_NULL;
-    if (workspace_bytes < size_t(p.workspace_bytes)) return MLA_ATTN_ERR_WORKSPACE;
-    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(cache, 16) || !aligned(block_table, 4) ||
-        !aligned(seq_lens, 4) || (workspace && !aligned(workspace, 16)) ||
-        (qf8 && !aligned(q_scale, 4)) || (kvf8 && !aligned(kv_scale, 4)))
-        return MLA_DQ_ERR_ALIGN;
-    if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return MLA_DQ_ERR_DIM;
-    if (aliased(out, q, cache, block_table, seq_lens, q_scale, kv_scale, workspace, dims, p, qf8, kvf8))
-        return MLA_DQ_ERR_ALIAS;
+    return mla_attn::attention(out, q, cache, block_table, seq_lens, q_scale, kv_scale, sm_scale, workspace,
+                               workspace_bytes, flags, dims, static_cast<hipStream_t>(stream), false);
+}
 
-    Args a;
-    a.out = static_cast<uint16_t*>(out);
-    a.q = static_cast<const uint8_t*>(q);
-    a.cache = static_cast<const uint8_t*>(cache);
-    a.block_table = block_table;
-    a.seq_lens = seq_lens;
-    a.q_scale = q_scale;
-    a.kv_scale = kv_scale;
-    const int64_t parts = dims->batch * dims->num_heads * int64_t(p.splits);
-    a.part_o = static_cast<float*>(workspace);
-    a.part_m = a.part_o ? a.part_o + parts * kValue : nullptr;
-    a.part_l = a.part_m ? a.part_m + parts : nullptr;
-    a.score_scale = sm_scale * 1.4426950408889634f;
-    a.B = int32_t(dims->batch);
-    a.H = int32_t(dims->num_heads);
-    a.num_blocks = int32_t(dims->num_blocks);
-    a.block_size = int32_t(dims->block_size);
-    a.max_blocks = int32_t(dims->max_blocks_per_seq);
-    a.max_seq_len = int32_t(dims->max_seq_len);
-    a.splits = p.splits;
-    a.keys_per_split = p.keys_per_split;
-    a.head_tiles = p.head_tiles;
-    a.xcd_remap = p.xcd_remap;
-    a.grid = int32_t(p.workgroups);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (qf8)
-        e = kvf8 ? launch_pair<true, true>(a, p, s) : launch_pair<true, false>(a, p, s);
-    else
-        e = kvf8 ? launch_pair<false, true>(a, p, s) : launch_pair<false, false>(a, p, s);
-    return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
+int mla_decode_attention_noalloc(void* out, const void* q, const void* cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const float* q_scale, const float* kv_scale,
+                                 float sm_scale, uint32_t flags, const mla_attn_dims* dims, void* stream) {
+    return mla_attn::attention(out, q, cache, block_table, seq_lens, q_scale, kv_scale, sm_scale, nullptr, 0,
+                               flags, dims, static_cast<hipStream_t>(stream), true);
 }
 
 }  // extern "C"

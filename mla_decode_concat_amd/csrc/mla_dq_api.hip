@@ -268,6 +268,8 @@ const char* mla_dq_strerror(int code) {
         case MLA_DQ_ERR_LAUNCH: return "HIP kernel launch failed";
         case MLA_DQ_ERR_ALIAS: return "q_out or the cache overlaps an input, or q_out overlaps the cache";
         case MLA_ATTN_ERR_WORKSPACE: return "workspace smaller than mla_decode_attention_workspace_size()";
+        case MLA_ATTN_ERR_SCRATCH:
+            return "the key split needs more than the library's scratch buffer (MLA_ATTN_SCRATCH_BYTES)";
         default: return "unknown mla_dq error code";
     }
 }

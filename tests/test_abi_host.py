@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 def test_library_exports_every_attention_function():
     names = _declared_functions(ATTN_HEADER)
     assert set(names) == {"mla_decode_attention", "mla_decode_attention_workspace_size",
-                          "mla_decode_attention_plan"}
+                          "mla_decode_attention_plan", "mla_decode_attention_noalloc"}
     lib = ctypes.CDLL(B.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -82,7 +82,7 @@ def test_plan_and_dims_structs_match_header_layout():
 
 def test_strerror_every_code():
     seen = set()
-    for c in (0, -1, -2, -3, -4, -5, -6, -7):
+    for c in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = M.strerror(c)
         assert s and s not in seen
         seen.add(s)

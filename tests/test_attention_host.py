@@ -24,6 +24,38 @@ def test_flag_and_code_values_match_header():
     assert re.search(r"#define MLA_ATTN_KV_FP8\s+\(1u << 1\)", text) and M.ATTN_KV_FP8 == 2
     assert int(re.search(r"#define MLA_ATTN_ERR_WORKSPACE\s+(-?\d+)", text).group(1)) == \
         B.ERR_WORKSPACE
+    assert int(re.search(r"#define MLA_ATTN_ERR_SCRATCH\s+(-?\d+)", text).group(1)) == B.ERR_SCRATCH
+    assert re.search(r"#define MLA_ATTN_SCRATCH_BYTES\s+\(16u << 20\)", text) and B.SCRATCH_BYTES == 16 << 20
+
+
+def test_default_plans_fit_the_scratch_buffer():
+    """Every split the default plan makes fits the allocation-free entry
+    point's buffer: at most 510 workgroups of 16 heads need records, the
+    largest being 255 (sequence, head tile) pairs split in two."""
+    worst = 0
+    for B_ in list(range(1, 300)) + [511, 1024]:
+        for H in (1, 15, 16, 17, 31, 32, 48, 64, 128):
+            for L in (64, 65, 1000, 4096, 1 << 16, 1 << 20):
+                MB = (L + 63) // 64
+                ws = M.attn_workspace_size(dims(B_, H, NB=MB, MB=MB, L=L), M.ATTN_KV_FP8)
+                worst = max(worst, ws)
+    assert 0 < worst <= B.SCRATCH_BYTES
+    assert worst == 255 * 16 * 2 * (512 + 2) * 4
+
+
+def test_noalloc_refuses_a_split_beyond_the_scratch_in_fresh_process():
+    """With the workgroup target raised the split can need more than the
+    buffer: the call returns MLA_ATTN_ERR_SCRATCH before touching the GPU."""
+    code = ("import ctypes, mla_decode_concat_amd as M; from mla_decode_concat_amd import _binding as B;"
+            "d=M.AttnDims(); d.batch=64; d.num_heads=128; d.num_blocks=4096; d.block_size=64;"
+            "d.max_blocks_per_seq=64; d.max_seq_len=4096; lib=B._attn_lib();"
+            "p=[(1<<36)+i*(1<<32) for i in range(7)];"
+            "print(M.attn_plan(d,2).workspace_bytes, lib.mla_decode_attention_noalloc(*p, ctypes.c_float(0.07),"
+            " ctypes.c_uint32(2), ctypes.byref(d), None))")
+    env = dict(os.environ, MLA_ATTN_TARGET_WGS="8192", PYTHONPATH=ROOT)
+    out = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True, check=True)
+    need, rc = out.stdout.split()
+    assert int(need) > B.SCRATCH_BYTES and int(rc) == B.ERR_SCRATCH
 
 
 def test_plan_struct_matches_header_layout():
