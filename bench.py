@@ -21,6 +21,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -171,12 +172,19 @@ def time_host(fn, calls: int = 2000) -> float:
 
 
 class DecodeSlice:
-    """One GPU's share (H heads) of the MLA q path around the epilogue, with
-    random weights: the q_b projection GEMM [T,1536] x [1536, H*192] and the
-    per-head W_UK product [H,T,128] x [H,128,512] produce ql_nope and q_pe;
-    kv_c and k_pe are the two parts of one [T,576] kv_a projection output.
-    The epilogue reads ql_nope, q_pe, kv_c and k_pe as strided views of those
-    outputs (no copies), or, for comparison, from contiguous copies."""
+    """One GPU's share (H heads) of the MLA path around the epilogue, with
+    random weights.  The fused-A projection [T,7168] x [7168, 1536+576] gives
+    q_a and kv_a.  q_a goes through its RMSNorm, the q_b projection
+    [T,1536] x [1536, H*192] and the per-head W_UK product [H,T,128] x
+    [H,128,512], which give ql_nope and q_pe; the first 512 elements of kv_a
+    go through their RMSNorm (kv_c), the last 64 are k_pe.  The epilogue reads
+    ql_nope, q_pe and k_pe as strided views of those outputs (no copies), or,
+    for comparison, from contiguous copies.
+
+    With ``fork`` the epilogue runs as two launches: the cache rows (which
+    need only kv_c and k_pe) on a second stream right after the kv norm,
+    beside the q_b and W_UK products, and the query rows after W_UK; the
+    main stream then waits for both."""
 
     def __init__(self, T: int, H: int, dev: str, seed: int = 3):
         g = torch.Generator(device="cpu").manual_seed(seed)
@@ -184,10 +192,12 @@ class DecodeSlice:
         def rnd(*shape, scale=1.0):
             return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16).to(dev)
         self.T, self.H = T, H
-        self.x = rnd(T, 1536)
+        self.hidden = rnd(T, 7168)
+        self.w_a = rnd(7168, 1536 + 576, scale=7168 ** -0.5)
         self.w_qb = rnd(1536, H * 192, scale=1536 ** -0.5)
         self.w_uk = rnd(H, 128, 512, scale=128 ** -0.5)
-        self.kv_a = rnd(T, 576)
+        self.g_q = rnd(1536, scale=0.1) + 1.0
+        self.g_kv = rnd(512, scale=0.1) + 1.0
         w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
         host = I.make_inputs(w)
         self.cache = host["cache"].to(dev)
@@ -198,22 +208,50 @@ class DecodeSlice:
         self.kv_scale = host["kv_scale"].to(dev)
         self.q_out = torch.empty(T, H, 576, dtype=torch.float8_e4m3fn, device=dev)
         self.flags = M.ROPE | M.Q_FP8 | M.KV_FP8
+        self.side = torch.cuda.Stream(device=dev)          # default priority
+
+    def _kv(self, qkv):
+        kv_c = torch.nn.functional.rms_norm(qkv[:, 1536:2048], (512,), self.g_kv, 1e-6)
+        return kv_c, qkv[:, 2048:]
+
+    def _q(self, qkv):
+        q_a = torch.nn.functional.rms_norm(qkv[:, :1536], (1536,), self.g_q, 1e-6)
+        q = (q_a @ self.w_qb).view(self.T, self.H, 192)
+        ql = torch.bmm(q[..., :128].transpose(0, 1).contiguous(), self.w_uk)   # [H, T, 512]
+        return ql.transpose(0, 1), q[..., 128:]
 
     def producers(self):
-        q = (self.x @ self.w_qb).view(self.T, self.H, 192)
-        ql = torch.bmm(q[..., :128].transpose(0, 1).contiguous(), self.w_uk)   # [H, T, 512]
-        return ql.transpose(0, 1), q[..., 128:], self.kv_a[:, :512], self.kv_a[:, 512:]
+        qkv = self.hidden @ self.w_a
+        kv_c, k_pe = self._kv(qkv)
+        ql_nope, q_pe = self._q(qkv)
+        return ql_nope, q_pe, kv_c, k_pe
 
-    def step(self, epilogue: bool = True, copies: bool = False):
+    def _epilogue(self, ql_nope, q_pe, kv_c, k_pe, extra: int = 0):
+        M.mla_decode_q_concat_kv_insert(self.q_out, ql_nope, q_pe, kv_c, k_pe, self.cache,
+                                        self.slots, self.positions, self.table, self.q_scale,
+                                        self.kv_scale, self.flags | extra)
+
+    def step(self, epilogue: bool = True, copies: bool = False, fork: bool = False):
+        if fork:
+            main = torch.cuda.current_stream()
+            qkv = self.hidden @ self.w_a
+            kv_c, k_pe = self._kv(qkv)
+            self.side.wait_stream(main)           # the side branch needs kv_c and k_pe only
+            ql_nope, q_pe = self._q(qkv)
+            with torch.cuda.stream(self.side):
+                self._epilogue(ql_nope, q_pe, kv_c, k_pe, M.CACHE_ROWS_ONLY)
+            kv_c.record_stream(self.side)
+            k_pe.record_stream(self.side)
+            self._epilogue(ql_nope, q_pe, kv_c, k_pe, M.Q_ROWS_ONLY)
+            main.wait_stream(self.side)
+            return
         ql_nope, q_pe, kv_c, k_pe = self.producers()
         if not epilogue:
             return
         if copies:
             ql_nope, q_pe = ql_nope.contiguous(), q_pe.contiguous()
             kv_c, k_pe = kv_c.contiguous(), k_pe.contiguous()
-        M.mla_decode_q_concat_kv_insert(self.q_out, ql_nope, q_pe, kv_c, k_pe, self.cache,
-                                        self.slots, self.positions, self.table, self.q_scale,
-                                        self.kv_scale, self.flags)
+        self._epilogue(ql_nope, q_pe, kv_c, k_pe)
 
 
 class DecodeStep(DecodeSlice):
@@ -242,9 +280,10 @@ class DecodeStep(DecodeSlice):
                                         self.seq_lens, w.sm_scale, self.q_scale, self.kv_scale,
                                         max_seq_len=L)
 
-    def step(self, epilogue: bool = True, copies: bool = False, attention: bool = True):
-        super().step(epilogue, copies)
-        if epilogue and attention:
+    def step(self, epilogue: bool = True, copies: bool = False, attention: bool = True,
+             fork: bool = False):
+        super().step(epilogue, copies, fork)
+        if (epilogue or fork) and attention:
             self.attn()
 
 
@@ -271,30 +310,61 @@ def time_graph_fn(fn, calls: int = 20, replays: int = 20) -> float:
     return e0.elapsed_time(e1) * 1e3 / (calls * replays)
 
 
+def _alternating_medians(fns: dict, calls: int, rounds: int = 3) -> dict:
+    """Graph-replayed µs per call of each fn, the variants measured in turn
+    `rounds` times (so that clock and thermal drift hit all alike); the
+    median of the rounds per variant."""
+    runs = {k: [] for k in fns}
+    for _ in range(rounds):
+        for k, fn in fns.items():
+            runs[k].append(time_graph_fn(fn, calls=calls))
+    return {k: float(np.median(v)) for k, v in runs.items()}
+
+
 def decode_slice_timings(dev: str) -> dict:
     """Graph-replayed µs per decode-step slice: producers alone, producers +
-    epilogue on strided views, producers + copies + epilogue; and the whole
-    step with the decode attention over 4096 cached tokens per sequence."""
+    epilogue on strided views, producers + copies + epilogue, and the
+    epilogue forked (cache rows on a second stream beside the q_b and W_UK
+    products, query rows after them); and the whole step with the decode
+    attention over 4096 cached tokens per sequence, unforked and forked."""
     out = {}
-    for T in (1, 64):
+    for T in (1, 64, 128):
         ds = DecodeSlice(T, 16, dev)
-        base = time_graph_fn(lambda: ds.step(epilogue=False))
-        strided = time_graph_fn(lambda: ds.step())
-        copies = time_graph_fn(lambda: ds.step(copies=True))
-        out[f"t{T}_h16"] = {"producers_us": round(base, 3), "with_epilogue_us": round(strided, 3),
-                            "with_copies_and_epilogue_us": round(copies, 3),
-                            "epilogue_increment_us": round(strided - base, 3),
-                            "copies_avoided_us": round(copies - strided, 3)}
+
+        def forced(f):
+            def run():
+                saved = ds.flags
+                ds.flags |= f
+                ds.step()
+                ds.flags = saved
+            return run
+        r = _alternating_medians({"base": lambda: ds.step(epilogue=False),
+                                  "strided": lambda: ds.step(),
+                                  "small": forced(M.FORCE_SMALL_T),
+                                  "mid": forced(M.FORCE_MID_T),
+                                  "copies": lambda: ds.step(copies=True),
+                                  "forked": lambda: ds.step(fork=True)}, calls=20)
+        out[f"t{T}_h16"] = {"producers_us": round(r["base"], 3),
+                            "with_epilogue_us": round(r["strided"], 3),
+                            "with_copies_and_epilogue_us": round(r["copies"], 3),
+                            "with_forked_epilogue_us": round(r["forked"], 3),
+                            "epilogue_increment_us": round(r["strided"] - r["base"], 3),
+                            "epilogue_increment_small_t_us": round(r["small"] - r["base"], 3),
+                            "epilogue_increment_mid_t_us": round(r["mid"] - r["base"], 3),
+                            "forked_epilogue_increment_us": round(r["forked"] - r["base"], 3),
+                            "copies_avoided_us": round(r["copies"] - r["strided"], 3)}
         log(f"decode slice T={T}: {out[f't{T}_h16']}")
     for B in (1, 64):
         st = DecodeStep(B, 16, 4096, dev)
-        base = time_graph_fn(lambda: st.step(epilogue=False), calls=10)
-        epi = time_graph_fn(lambda: st.step(attention=False), calls=10)
-        full = time_graph_fn(lambda: st.step(), calls=10)
+        r = _alternating_medians({"base": lambda: st.step(epilogue=False),
+                                  "epi": lambda: st.step(attention=False),
+                                  "full": lambda: st.step(),
+                                  "forked": lambda: st.step(fork=True)}, calls=10)
         out[f"b{B}_h16_l4096_with_attention"] = {
-            "producers_us": round(base, 3), "with_epilogue_us": round(epi, 3),
-            "with_epilogue_and_attention_us": round(full, 3),
-            "attention_increment_us": round(full - epi, 3)}
+            "producers_us": round(r["base"], 3), "with_epilogue_us": round(r["epi"], 3),
+            "with_epilogue_and_attention_us": round(r["full"], 3),
+            "forked_with_attention_us": round(r["forked"], 3),
+            "attention_increment_us": round(r["full"] - r["epi"], 3)}
         log(f"decode step B={B} L=4096: {out[f'b{B}_h16_l4096_with_attention']}")
         del st
     return out
@@ -510,6 +580,124 @@ def copy_reference(dev: str, moved_bytes: int, calls: int = 50) -> dict:
             "bytes_moved": 2 * n, "us_per_call": round(us, 3), "gbs": round(2 * n / us / 1e3, 1)}
 
 
+# (name, tokens or sequences, cached tokens (None: the slice without the
+# attention), forked, extra epilogue flags, epilogue alone on the slice's views)
+STEP_TRACE_CASES = [
+    ("slice_t64_h16", 64, None, False, 0, False),
+    ("slice_t64_h16_mid_t", 64, None, False, M.FORCE_MID_T, False),
+    ("slice_t64_h16_epilogue_alone", 64, None, False, 0, True),
+    ("slice_t64_h16_forked", 64, None, True, 0, False),
+    ("step_b64_h16_l4096", 64, 4096, False, 0, False),
+    ("step_b64_h16_l4096_forked", 64, 4096, True, 0, False),
+    ("step_b1_h16_l4096", 1, 4096, False, 0, False),
+    ("step_b1_h16_l4096_forked", 1, 4096, True, 0, False),
+]
+
+
+def step_trace(dev: str, replays: int) -> None:
+    """For a kernel trace of one decode step: each case captures ONE step in
+    a HIP graph (or only its epilogue, on views the producers wrote once)
+    and replays it `replays` times, draining the GPU and idling 200 µs
+    between replays, so that in the trace every replay is a group of kernels
+    set apart by idle time (see trace_summary)."""
+    for name, T, L, fork, extra, alone in STEP_TRACE_CASES:
+        obj = DecodeSlice(T, 16, dev) if L is None else DecodeStep(T, 16, L, dev)
+        obj.flags |= extra
+        if alone:
+            views = obj.producers()
+            fn = lambda: obj._epilogue(*views)           # noqa: E731
+        else:
+            fn = lambda: obj.step(fork=fork)              # noqa: E731
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(replays):
+            g.replay()
+            torch.cuda.synchronize()
+            time.sleep(200e-6)
+        log(f"step trace {name}: {replays} replays")
+        del g, obj, fn
+        torch.cuda.empty_cache()
+
+
+def _short_kernel_name(name: str) -> str:
+    if name.startswith("Cijk_") or "gemm" in name.lower():
+        return "GEMM (hipBLASLt)"
+    for key in ("mla_dq_epilogue_kernel", "mla_attn_ring_kernel", "mla_attn_partial_kernel",
+                "mla_attn_combine_wide_kernel", "mla_attn_combine_kernel"):
+        if key in name:
+            return key
+    if "rms_norm" in name.lower() or "rmsnorm" in name.lower() or "layer_norm" in name.lower():
+        return "RMSNorm (torch)"
+    if "elementwise" in name or "copy" in name.lower():
+        return "elementwise (torch)"
+    return name[:40]
+
+
+def trace_summary(csv_path: str, idle_us: float = 100.0) -> str:
+    """Median timeline of the replayed steps in a rocprofv3 kernel trace.
+
+    Kernels are split into replays at idle gaps longer than ``idle_us``;
+    replays with the same kernel sequence (name and grid) form one case.
+    For each case and kernel: median start and end relative to the replay's
+    first kernel start, median duration, and the median gap from the latest
+    end of the kernels before it (negative: it overlaps one of them)."""
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         _short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]),
+                         int(r["Workgroup_Size_X"])))
+    rows.sort()
+    groups, cur = [], []
+    for r in rows:
+        if cur and r[0] - max(x[1] for x in cur) > idle_us * 1e3:
+            groups.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        groups.append(cur)
+    cases = {}
+    for g in groups:
+        sig = tuple((x[2], x[3] // x[4]) for x in g)
+        cases.setdefault(sig, []).append(g)
+    # cases in the order they first ran; named after --step-trace's cases
+    # when the trace holds exactly those
+    kept = sorted(((sig, gs) for sig, gs in cases.items()
+                   if len(gs) >= 5 and any(k[0] == "mla_dq_epilogue_kernel" for k in sig)),
+                  key=lambda kv: float(np.median([g[0][0] for g in kv[1]])))
+    names = [c[0] for c in STEP_TRACE_CASES] if len(kept) == len(STEP_TRACE_CASES) else [""] * len(kept)
+    lines = []
+    for (sig, gs), name in zip(kept, names):
+        title = f"{name}: " if name else ""
+        lines.append(f"\n### {title}{len(gs)} replays of {len(sig)} kernels\n")
+        lines.append("Median µs from the first kernel's start:\n")
+        lines.append("| # | Kernel | Workgroups | Start | End | Duration | Gap from previous end |")
+        lines.append("|---|---|---|---|---|---|---|")
+        total = []
+        for k, (nm, wgs) in enumerate(sig):
+            st = [(g[k][0] - g[0][0]) / 1e3 for g in gs]
+            en = [(g[k][1] - g[0][0]) / 1e3 for g in gs]
+            du = [(g[k][1] - g[k][0]) / 1e3 for g in gs]
+            gap = [(g[k][0] - max(x[1] for x in g[:k])) / 1e3 for g in gs] if k else [0.0]
+            lines.append(f"| {k} | {nm} | {wgs} | {np.median(st):.2f} | {np.median(en):.2f} | "
+                         f"{np.median(du):.2f} | {np.median(gap):.2f} |" if k else
+                         f"| {k} | {nm} | {wgs} | {np.median(st):.2f} | {np.median(en):.2f} | "
+                         f"{np.median(du):.2f} | — |")
+        total = [(max(x[1] for x in g) - g[0][0]) / 1e3 for g in gs]
+        busy = [sum(x[1] - x[0] for x in g) / 1e3 for g in gs]
+        lines.append(f"\nFirst start to last end: median {np.median(total):.2f} µs; sum of kernel "
+                     f"durations {np.median(busy):.2f} µs.")
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,12 +714,21 @@ def main() -> int:
                     help="time only the decode-attention workloads (prints their JSON)")
     ap.add_argument("--only-decode-slice", action="store_true",
                     help="time only the decode-step slices in HIP graphs (prints their JSON)")
+    ap.add_argument("--step-trace", type=int, default=0, metavar="REPLAYS",
+                    help="replay one captured decode step per case REPLAYS times, apart "
+                         "(for a rocprofv3 kernel trace; see --trace-summary)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print the per-replay kernel timeline of a rocprofv3 kernel trace "
+                         "(no GPU needed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of this many MiB (counter calibration)")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the epilogue exchanges nothing between GPUs, "
               "so it runs and reports a single MI355X (use --gpus 1).", file=sys.stderr)
@@ -542,6 +739,9 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
 
+    if args.step_trace:
+        step_trace(dev, args.step_trace)
+        return 0
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -65,8 +65,9 @@ extern "C" {
 /* Launch overrides for tests and sweeps; they never change the results.
  * By default the library picks, by the row count T * (H + 1), one of three
  * mappings at measured row thresholds: the latency mapping (one latent row
- * per wavefront, 64-thread workgroups) for the fewest rows, the same in
- * 128-thread workgroups next, and the throughput mapping (256-thread
+ * per wavefront, 64-thread workgroups) for the fewest rows (up to 896, or
+ * up to 2560 with at most 32 heads), the same in 128-thread workgroups
+ * next (up to 5120), and the throughput mapping (256-thread
  * workgroups, tails batched, rope table staged in LDS) above; the page's
  * launcher makes the same token-count-dependent choice ("implementation
  * breakdown" items 1 and 3).  Independently, loads and stores stream past
@@ -77,6 +78,18 @@ extern "C" {
 #define MLA_DQ_FORCE_STREAM  (1u << 10) /* non-temporal loads and stores   */
 #define MLA_DQ_FORCE_CACHED  (1u << 11) /* default cache policy            */
 #define MLA_DQ_FORCE_MID_T   (1u << 12) /* latency mapping, 128 threads    */
+/* Row subsets, for a caller that splits the epilogue around its
+ * dependencies.  The cache row of a token needs only kv_c and k_pe, which do
+ * not depend on the query projections; the page's kernel lets its cache-row
+ * warps skip the wait for the upstream GEMM for that reason
+ * ("implementation breakdown" item 2).  With MLA_DQ_Q_ROWS_ONLY the call
+ * writes only q_out; with MLA_DQ_CACHE_ROWS_ONLY only the cache rows.  One
+ * call of each, in either order or at the same time on two streams, leaves
+ * exactly the bytes of one call without them.  The arguments and checks are
+ * those of a full call (every pointer the flags require, even those the
+ * subset does not read).  At most one of the two. */
+#define MLA_DQ_Q_ROWS_ONLY     (1u << 13)
+#define MLA_DQ_CACHE_ROWS_ONLY (1u << 14)
 
 /* ---- return codes ------------------------------------------------------ */
 #define MLA_DQ_OK          0
@@ -169,13 +182,16 @@ typedef struct mla_dq_launch_plan {
     int32_t rows_per_wave;    /* latent rows per wavefront                       */
     int32_t tail_steps;       /* steps of 8 tails per wavefront                  */
     int32_t reserved;
-    int64_t small_rows_max;   /* row threshold of the small-T mapping in force   */
+    int64_t small_rows_max;   /* row threshold of the small-T mapping in force
+                                 for these heads                                  */
     int64_t stream_bytes_min; /* byte threshold in force                         */
     int64_t bytes;            /* bytes the call reads and writes                 */
     int64_t tail_blocks;      /* workgroups doing positional tails (first)       */
     int64_t latent_blocks;    /* workgroups doing latent parts (after them)      */
     int64_t grid_blocks;      /* tail_blocks + latent_blocks                     */
-    int64_t total_rows;       /* T * (H + 1)                                     */
+    int64_t total_rows;       /* rows of this launch: T * (H + 1), or T * H with
+                                 MLA_DQ_Q_ROWS_ONLY, or T with
+                                 MLA_DQ_CACHE_ROWS_ONLY                           */
     int64_t mid_rows_max;     /* row threshold of the mid-T mapping in force     */
 } mla_dq_launch_plan;
 

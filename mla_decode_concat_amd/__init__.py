@@ -7,7 +7,7 @@ binding.
 """
 from ._binding import (  # noqa: F401
     ROPE, Q_FP8, KV_FP8, FP16, ROPE_GPTJ, TABLE_BF16, FORCE_SMALL_T, FORCE_LARGE_T, FORCE_STREAM, FORCE_CACHED,
-    FORCE_MID_T,
+    FORCE_MID_T, Q_ROWS_ONLY, CACHE_ROWS_ONLY,
     MlaDqError, Dims, LaunchPlan, fused_mla_decode_q_concat_kv_cache_insert,
     mla_decode_q_concat_kv_insert, PreparedInsert, plan, strerror, load,
     ATTN_Q_FP8, ATTN_KV_FP8, AttnDims, AttnPlan, PreparedAttention, attn_plan,

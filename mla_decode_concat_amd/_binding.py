@@ -28,6 +28,8 @@ FORCE_LARGE_T = 1 << 9
 FORCE_STREAM = 1 << 10
 FORCE_CACHED = 1 << 11
 FORCE_MID_T = 1 << 12
+Q_ROWS_ONLY = 1 << 13
+CACHE_ROWS_ONLY = 1 << 14
 
 OK = 0
 ERR_NULL = -1

@@ -47,9 +47,11 @@ int64_t env_int64(const char* name, int64_t fallback) {
     return int64_t(n);
 }
 
-int64_t small_rows_max() {
-    static const int64_t v = env_int64("MLA_DQ_SMALL_ROWS_MAX", kDefaultSmallRowsMax);
-    return v;
+// The environment variable, when set, applies to every head count.
+int64_t small_rows_max(int64_t H) {
+    static const int64_t v = env_int64("MLA_DQ_SMALL_ROWS_MAX", -1);
+    if (v >= 0) return v;
+    return H <= kFewHeadsMax ? kDefaultSmallRowsMaxFewHeads : kDefaultSmallRowsMax;
 }
 
 int64_t mid_rows_max() {
@@ -65,13 +67,17 @@ int64_t stream_bytes_min() {
 // Bytes one call reads and writes: each 576-wide input row once (2-byte
 // elements), each output row once, plus slot, position and rope table row
 // per token.
+// per token.  A launch restricted to one kind of row counts only its rows
+// (and the slot only with the cache row).
 int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
     const int64_t T = d->num_tokens, H = d->num_heads;
     const bool rope = flags & MLA_DQ_ROPE;
+    const int64_t qh = (flags & MLA_DQ_CACHE_ROWS_ONLY) ? 0 : H;     // query rows per token
+    const int64_t kv = (flags & MLA_DQ_Q_ROWS_ONLY) ? 0 : 1;         // cache rows per token
     const int64_t table_row = (flags & MLA_DQ_TABLE_BF16) ? 128 : 256;
-    const int64_t read = T * (H * 1152 + 1152 + 8 + (rope ? 8 + table_row : 0));
-    const int64_t write = T * 576 * (H * ((flags & MLA_DQ_Q_FP8) ? 1 : 2) +
-                                     ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
+    const int64_t read = T * (qh * 1152 + kv * (1152 + 8) + (rope ? 8 + table_row : 0));
+    const int64_t write = T * 576 * (qh * ((flags & MLA_DQ_Q_FP8) ? 1 : 2) +
+                                     kv * ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
     return read + write;
 }
 
@@ -81,8 +87,9 @@ int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
     const uint32_t known = MLA_DQ_ROPE | MLA_DQ_Q_FP8 | MLA_DQ_KV_FP8 | MLA_DQ_FP16 |
                            MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16 | MLA_DQ_FORCE_SMALL_T |
                            MLA_DQ_FORCE_LARGE_T | MLA_DQ_FORCE_STREAM | MLA_DQ_FORCE_CACHED |
-                           MLA_DQ_FORCE_MID_T;
+                           MLA_DQ_FORCE_MID_T | MLA_DQ_Q_ROWS_ONLY | MLA_DQ_CACHE_ROWS_ONLY;
     if (flags & ~known) return MLA_DQ_ERR_FLAGS;
+    if ((flags & MLA_DQ_Q_ROWS_ONLY) && (flags & MLA_DQ_CACHE_ROWS_ONLY)) return MLA_DQ_ERR_FLAGS;
     if ((flags & (MLA_DQ_ROPE_GPTJ | MLA_DQ_TABLE_BF16)) && !(flags & MLA_DQ_ROPE))
         return MLA_DQ_ERR_FLAGS;
     const uint32_t forced_mappings = flags & (MLA_DQ_FORCE_SMALL_T | MLA_DQ_FORCE_MID_T | MLA_DQ_FORCE_LARGE_T);
@@ -114,13 +121,21 @@ int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
 
 }  // namespace
 
+// Rows per token of a launch: all H + 1, or only the H query rows, or only
+// the cache row.
+int64_t row_stride(int64_t H, uint32_t flags) {
+    if (flags & MLA_DQ_Q_ROWS_ONLY) return H;
+    if (flags & MLA_DQ_CACHE_ROWS_ONLY) return 1;
+    return H + 1;
+}
+
 int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     if (out == nullptr) return MLA_DQ_ERR_NULL;
     const int rc = check_flags_dims(flags, d);
     if (rc < 0) return rc;
     const int64_t T = d->num_tokens, H = d->num_heads;
-    const int64_t rows = T * (H + 1);
-    const int64_t rows_thr = small_rows_max(), mid_thr = mid_rows_max(), bytes_thr = stream_bytes_min();
+    const int64_t rows = T * row_stride(H, flags);
+    const int64_t rows_thr = small_rows_max(H), mid_thr = mid_rows_max(), bytes_thr = stream_bytes_min();
     const int64_t bytes = call_bytes(d, flags);
     int mapping = rows <= rows_thr ? 0 : (rows <= mid_thr ? 2 : 1);
     if (flags & MLA_DQ_FORCE_SMALL_T) mapping = 0;
@@ -237,7 +252,9 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
     a.k_pe_st = dims->k_pe_stride_t;
     a.num_slots = dims->num_blocks * dims->block_size;
     a.max_position = (flags & MLA_DQ_ROPE) ? dims->max_position : 1;
-    a.rows_per_token = make_fastdiv31(uint32_t(dims->num_heads + 1));
+    a.row_stride = uint32_t(mla_dq::row_stride(dims->num_heads, flags));
+    a.first_head = (flags & MLA_DQ_CACHE_ROWS_ONLY) ? uint32_t(dims->num_heads) : 0u;
+    a.rows_per_token = make_fastdiv31(a.row_stride);
     a.num_heads = uint32_t(dims->num_heads);
     a.total_rows = uint32_t(p.total_rows);
     a.tail_blocks = uint32_t(p.tail_blocks);

@@ -30,11 +30,19 @@
 #endif
 // Small-T mapping while T * (H + 1) <= the first threshold, mid-T mapping
 // (the same latency settings in 128-thread workgroups) up to the second,
-// throughput mapping above.  Measured on MI355X for 16 to 128 heads: the
-// 64-thread workgroups win up to about 900 rows, the 128-thread ones up to
+// throughput mapping above.  Measured on MI355X for 16 to 128 heads, with
+// the epilogue right after the per-head W_UK product of a decode step (its
+// place in a model): the 64-thread workgroups win up to about 900 rows, and
+// with at most 32 heads up to about 2600 rows; the 128-thread ones up to
 // about 5000 to 6000.
 #ifndef MLA_DQ_SMALL_ROWS_MAX_DEFAULT
 #define MLA_DQ_SMALL_ROWS_MAX_DEFAULT 896
+#endif
+#ifndef MLA_DQ_SMALL_ROWS_MAX_FEW_HEADS_DEFAULT
+#define MLA_DQ_SMALL_ROWS_MAX_FEW_HEADS_DEFAULT 2560
+#endif
+#ifndef MLA_DQ_FEW_HEADS_MAX
+#define MLA_DQ_FEW_HEADS_MAX 32
 #endif
 #ifndef MLA_DQ_MID_ROWS_MAX_DEFAULT
 #define MLA_DQ_MID_ROWS_MAX_DEFAULT 5120
@@ -105,6 +113,8 @@ static_assert(kSmallMapping.block != kLargeMapping.block && kMidMapping.block !=
 // MLA_DQ_SMALL_ROWS_MAX, MLA_DQ_MID_ROWS_MAX and MLA_DQ_STREAM_BYTES_MIN,
 // read once).
 constexpr int64_t kDefaultSmallRowsMax = MLA_DQ_SMALL_ROWS_MAX_DEFAULT;
+constexpr int64_t kDefaultSmallRowsMaxFewHeads = MLA_DQ_SMALL_ROWS_MAX_FEW_HEADS_DEFAULT;
+constexpr int64_t kFewHeadsMax = MLA_DQ_FEW_HEADS_MAX;
 constexpr int64_t kDefaultMidRowsMax = MLA_DQ_MID_ROWS_MAX_DEFAULT;
 constexpr int64_t kDefaultStreamBytesMin = MLA_DQ_STREAM_BYTES_MIN_DEFAULT;
 
@@ -125,9 +135,13 @@ struct KernelArgs {
     int64_t ql_nope_st, ql_nope_sh, q_pe_st, q_pe_sh, kv_c_st, k_pe_st;
     int64_t num_slots;
     int64_t max_position;
-    FastDiv31 rows_per_token;   // divides a row index by H + 1
+    FastDiv31 rows_per_token;   // divides a row index by row_stride
     uint32_t num_heads;
-    uint32_t total_rows;        // T * (H + 1)
+    uint32_t total_rows;        // T * row_stride
+    uint32_t row_stride;        // rows per token in this launch: H + 1, H (query rows
+                                // only) or 1 (cache rows only)
+    uint32_t first_head;        // row kind of a token's first row here: 0, or H
+                                // (cache rows only); kind H is the cache row
     uint32_t tail_blocks;       // workgroups [0, tail_blocks) do the tails
     uint32_t fp16;              // activations are fp16 (else bf16)
     uint32_t gptj;              // interleaved rotation pairs
@@ -140,6 +154,7 @@ int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_
              const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
              const float* kv_scale, uint32_t flags, const mla_dq_dims* dims);
 int plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* out);
+int64_t row_stride(int64_t H, uint32_t flags);
 
 #if defined(__HIPCC__)
 hipError_t launch(const KernelArgs& a, const mla_dq_launch_plan& plan, uint32_t flags,

@@ -6,7 +6,9 @@
 //
 // Work layout.  Every token owns H + 1 latent rows of 576 elements: its H
 // query rows, then its cache row (the page's kernel orders a token's work
-// items the same way: query slots first, then the cache slot).  A row is 72
+// items the same way: query slots first, then the cache slot).  A launch
+// restricted to the query rows or to the cache rows enumerates only those
+// (row_stride H or 1 rows per token).  A row is 72
 // chunks of 8 bf16 elements, one chunk being one 16-byte load: 64 chunks of
 // the 512-wide latent part and 8 chunks of the 64-wide positional tail.
 //
@@ -229,7 +231,7 @@ __device__ __forceinline__ void latent_rows(const KernelArgs& a, uint32_t tile) 
         live[k] = row < a.total_rows;
         const uint32_t r = live[k] ? row : 0u;
         tok[k] = fastdiv31(r, a.rows_per_token);
-        head[k] = r - tok[k] * (H + 1);
+        head[k] = r - tok[k] * a.row_stride + a.first_head;
         const uint16_t* sp = head[k] < H ? a.ql_nope + uint64_t(tok[k]) * a.ql_nope_st +
                                                uint64_t(head[k]) * a.ql_nope_sh
                                          : a.kv_c + uint64_t(tok[k]) * a.kv_c_st;
@@ -322,7 +324,7 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         live[k] = row < a.total_rows;
         const uint32_t r = live[k] ? row : 0u;
         tok[k] = fastdiv31(r, a.rows_per_token);
-        head[k] = r - tok[k] * (H + 1);
+        head[k] = r - tok[k] * a.row_stride + a.first_head;
         const uint64_t t = tok[k];
         const uint16_t* src = head[k] < H
                                   ? a.q_pe + t * a.q_pe_st + uint64_t(head[k]) * a.q_pe_sh
@@ -340,9 +342,10 @@ __device__ __forceinline__ void tail_rows(const KernelArgs& a, uint32_t tile) {
         // TLDS: the workgroup's rows [rlo, rhi) belong to tokens t_lo ..
         // t_lo + ntok - 1.  Their table rows are copied to LDS, one 16-byte
         // chunk per thread, and every tail lane then reads its values there.
-        // A token owns H + 1 >= 2 rows, so ntok <= rows / 2 + 1.
+        // A token owns at least one row of the launch (one, when only cache
+        // rows are written), so ntok <= rows.
         constexpr uint32_t kRowsPerWg = STEPS * kRowsPerStep;
-        constexpr uint32_t kMaxTokens = kRowsPerWg / 2 + 1;
+        constexpr uint32_t kMaxTokens = kRowsPerWg;
         const uint8_t* staged = nullptr;
         uint32_t t_lo = 0;
         if constexpr (TLDS) {

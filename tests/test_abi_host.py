@@ -61,6 +61,8 @@ def test_flag_and_code_values_match_header():
     assert val("MLA_DQ_FORCE_STREAM") == M.FORCE_STREAM
     assert val("MLA_DQ_FORCE_CACHED") == M.FORCE_CACHED
     assert val("MLA_DQ_FORCE_MID_T") == M.FORCE_MID_T
+    assert val("MLA_DQ_Q_ROWS_ONLY") == M.Q_ROWS_ONLY
+    assert val("MLA_DQ_CACHE_ROWS_ONLY") == M.CACHE_ROWS_ONLY
     for name, v in (("MLA_DQ_ERR_NULL", B.ERR_NULL), ("MLA_DQ_ERR_ALIGN", B.ERR_ALIGN),
                     ("MLA_DQ_ERR_DIM", B.ERR_DIM), ("MLA_DQ_ERR_FLAGS", B.ERR_FLAGS),
                     ("MLA_DQ_ERR_LAUNCH", B.ERR_LAUNCH), ("MLA_DQ_ERR_ALIAS", B.ERR_ALIAS)):
@@ -120,7 +122,8 @@ def test_null_dims():
     assert _call(_ptrs(), 0, None) == B.ERR_NULL
 
 
-@pytest.mark.parametrize("flags", [1 << 6, 1 << 13, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+@pytest.mark.parametrize("flags", [1 << 6, 1 << 15, 1 << 31, M.FORCE_SMALL_T | M.FORCE_LARGE_T,
+                                   M.Q_ROWS_ONLY | M.CACHE_ROWS_ONLY,
                                    M.FORCE_SMALL_T | M.FORCE_MID_T, M.FORCE_MID_T | M.FORCE_LARGE_T,
                                    M.FORCE_SMALL_T | M.FORCE_MID_T | M.FORCE_LARGE_T,
                                    M.FORCE_STREAM | M.FORCE_CACHED, M.ROPE_GPTJ, M.TABLE_BF16,
@@ -267,6 +270,28 @@ def _bytes(T, H, flags):
     return read + write
 
 
+@pytest.mark.parametrize("T,H", [(1, 16), (64, 16), (65, 1), (8192, 16), (256, 128)])
+@pytest.mark.parametrize("fl", [0, M.ROPE | M.Q_FP8, M.ROPE | M.KV_FP8 | M.TABLE_BF16])
+def test_plan_of_row_subsets(T, H, fl):
+    """A launch restricted to the query rows plans T * H rows, one restricted
+    to the cache rows T rows; the two move the bytes of a full launch plus
+    one more read of each token's position and table row."""
+    full = M.plan(_dims(T=T, H=H), fl)
+    q = M.plan(_dims(T=T, H=H), fl | M.Q_ROWS_ONLY)
+    c = M.plan(_dims(T=T, H=H), fl | M.CACHE_ROWS_ONLY)
+    assert (full.total_rows, q.total_rows, c.total_rows) == (T * (H + 1), T * H, T)
+    extra = T * (8 + (128 if fl & M.TABLE_BF16 else 256)) if fl & M.ROPE else 0
+    assert q.bytes + c.bytes == full.bytes + extra
+    for p in (q, c):
+        want = 0 if p.total_rows <= p.small_rows_max else (2 if p.total_rows <= p.mid_rows_max else 1)
+        assert p.mapping == want
+        tails = {0: 8, 2: 16, 1: 64}[p.mapping]
+        assert p.tail_blocks == (p.total_rows + tails - 1) // tails
+    d = _dims(T=T, H=H)
+    with pytest.raises(M.MlaDqError):
+        M.plan(d, fl | M.Q_ROWS_ONLY | M.CACHE_ROWS_ONLY)
+
+
 def test_plan_threshold_and_coverage():
     pl = M.plan(_dims(T=1, H=16), 0)
     assert 0 < pl.small_rows_max <= pl.mid_rows_max
@@ -299,14 +324,20 @@ def test_plan_threshold_and_coverage():
 
 
 def test_plan_defaults_match_measured_choice():
-    """The 8192-token workload streams on the throughput mapping; the
-    1-token workload uses the 64-thread latency mapping and the 64/65-token
-    workloads the 128-thread one, with the default cache policy."""
+    """The 8192-token workload streams on the throughput mapping; the 1, 64
+    and 65-token workloads at 16 heads use the 64-thread latency mapping
+    (measured fastest after the W_UK product of a decode step up to about
+    2600 rows with at most 32 heads), the 256-token full-head one the
+    throughput mapping; with 128 heads the 128-thread mapping takes over
+    above 896 rows.  All with the default cache policy below 192 MiB."""
     big = M.plan(_dims(T=8192, H=16, NB=4096), M.ROPE | M.KV_FP8)
     assert (big.mapping, big.streaming) == (1, 1)
-    for T, mapping in ((1, 0), (64, 2), (65, 2)):
-        p = M.plan(_dims(T=T, H=16), M.ROPE | M.Q_FP8 | M.KV_FP8)
-        assert (p.mapping, p.streaming) == (mapping, 0)
+    for T, H, mapping in ((1, 16, 0), (64, 16, 0), (65, 16, 0), (150, 16, 0), (151, 16, 2),
+                          (77, 32, 0), (78, 32, 2), (6, 128, 0), (7, 128, 2), (39, 128, 2),
+                          (40, 128, 1), (301, 16, 2), (302, 16, 1)):
+        p = M.plan(_dims(T=T, H=H), M.ROPE | M.Q_FP8 | M.KV_FP8)
+        assert (p.mapping, p.streaming) == (mapping, 0), (T, H)
+        assert p.small_rows_max == (2560 if H <= 32 else 896) and p.mid_rows_max == 5120
 
 
 def test_plan_rejects_bad_input():

@@ -337,7 +337,8 @@ def test_every_e4m3_code_reaches_the_output_exactly(q_fp8):
             assert np.array_equal(got[b, h], want), (b, h)
 
 
-def test_decode_step_graph_epilogue_then_attention():
+@pytest.mark.parametrize("fork", [False, True], ids=["one-launch", "forked"])
+def test_decode_step_graph_epilogue_then_attention(fork):
     """One decode step captured in a HIP graph: the q-path GEMMs, the
     epilogue (writes each sequence's new E4M3 cache row and E4M3 queries),
     then the attention over all L rows.  Every replay equals the epilogue
@@ -347,11 +348,11 @@ def test_decode_step_graph_epilogue_then_attention():
     from tests._util import oracle_run
     B, H, L = 6, 16, 333
     st = bench.DecodeStep(B, H, L, DEV)
-    announce(f"decode step graph B={B} H={H} L={L}")
+    announce(f"decode step graph B={B} H={H} L={L} fork={fork}")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        st.step()
+        st.step(fork=fork)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     # the epilogue's inputs, materialised, and the oracle's epilogue
@@ -368,7 +369,7 @@ def test_decode_step_graph_epilogue_then_attention():
     ref, tol = oracle_out(st.w, ainp)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        st.step()
+        st.step(fork=fork)
     for _ in range(3):
         st.out.view(torch.int16).fill_(-1)
         torch.cuda.synchronize()

@@ -136,6 +136,9 @@ LAUNCHES = [M.FORCE_SMALL_T | M.FORCE_CACHED, M.FORCE_SMALL_T | M.FORCE_STREAM,
             M.FORCE_MID_T | M.FORCE_CACHED, M.FORCE_MID_T | M.FORCE_STREAM,
             M.FORCE_LARGE_T | M.FORCE_CACHED, M.FORCE_LARGE_T | M.FORCE_STREAM]
 
+VARIANTS = [("fp16", "neox", "f32"), ("bf16", "gptj", "f32"), ("bf16", "neox", "bf16"),
+            ("fp16", "gptj", "bf16")]
+
 
 @pytest.mark.parametrize("name", ["t1_h16_copy", "t64_h16_rope_fp8", "t65_h16_rope_fp8",
                                   "t256_h128_rope_qfp8"])
@@ -381,6 +384,64 @@ def test_duplicate_slots_leave_one_candidate(T, H, launch):
             assert any(np.array_equal(got[c], cand[c]) for cand in cands), (s_, c)
 
 
+def _run_subsets(w: I.Workload, inp: dict, order, launch: int, init: np.ndarray):
+    """Calls restricted to row subsets, in the given order, on one poisoned
+    q_out and one cache (random background); returns (q bits, cache bits)."""
+    qdt = torch.float8_e4m3fn if w.q_fp8 else w.torch_dtype
+    kvdt = torch.float8_e4m3fn if w.kv_fp8 else w.torch_dtype
+    q_out = torch.empty(w.tokens, w.heads, I.ROW, dtype=qdt, device=DEV)
+    q_out.view(torch.uint8).fill_(0xFF)
+    src = init.view(np.int16) if init.dtype == np.uint16 else init
+    cache = torch.from_numpy(src.copy()).view(kvdt).to(DEV)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    for sub in order:
+        announce(f"row subset {sub:#x} {w.describe()} launch {launch:#x}")
+        M.mla_decode_q_concat_kv_insert(q_out, dev["ql_nope"], dev["q_pe"], dev["kv_c"], dev["k_pe"],
+                                        cache, dev["slot_mapping"], dev["positions"],
+                                        dev["rope_cos_sin"], dev["q_scale"], dev["kv_scale"],
+                                        flags_of(w) | sub | launch)
+    torch.cuda.synchronize()
+    return bits(q_out.cpu()), bits(cache.cpu())
+
+
+@pytest.mark.parametrize("launch", [0] + LAUNCHES, ids=lambda f: f"{f:#x}")
+@pytest.mark.parametrize("T,H", [(1, 16), (64, 16), (97, 1), (300, 3)])
+def test_row_subsets_compose(T, H, launch):
+    """A call restricted to the query rows writes q_out and leaves the cache
+    alone; one restricted to the cache rows writes only the cache rows; the
+    two together, in either order, give the oracle's bytes.  Under every
+    mapping and cache policy (a cache-rows launch with one head stages one
+    table row per tail row in the throughput mapping)."""
+    w = I.custom(T, H, num_blocks=(T + 63) // 64 + 1, rope=True, q_fp8=True, kv_fp8=True,
+                 q_scale=0.04, kv_scale=0.3)
+    inp = _out_of_range(I.make_inputs(w, seed=60 + T), w, seed=61 + H, frac=0.1)
+    init = _background(w, seed=62)
+    want_q, want_cache = oracle_run(w, inp, cache_init=init)
+    q, cache = _run_subsets(w, inp, [M.Q_ROWS_ONLY], launch, init)
+    assert_same(q, want_q, "q_out (query rows only)")
+    assert np.array_equal(cache, init), "a query-rows launch touched the cache"
+    q, cache = _run_subsets(w, inp, [M.CACHE_ROWS_ONLY], launch, init)
+    assert np.all(q == (0xFF if w.q_fp8 else 0xFFFF)), "a cache-rows launch touched q_out"
+    assert_same(cache, want_cache, "cache (cache rows only)")
+    for order in ([M.Q_ROWS_ONLY, M.CACHE_ROWS_ONLY], [M.CACHE_ROWS_ONLY, M.Q_ROWS_ONLY]):
+        q, cache = _run_subsets(w, inp, order, launch, init)
+        assert_same(q, want_q, "q_out")
+        assert_same(cache, want_cache, "cache")
+
+
+@pytest.mark.parametrize("dtype,style,table", VARIANTS, ids=["-".join(v) for v in VARIANTS])
+def test_row_subsets_variants(dtype, style, table):
+    w = I.custom(130, 2, num_blocks=4, rope=True, q_fp8=False, kv_fp8=True, q_scale=0.04,
+                 kv_scale=0.3, dtype=dtype, rope_style=style, table_dtype=table)
+    inp = I.make_inputs(w, seed=63)
+    init = _background(w, seed=64)
+    want_q, want_cache = oracle_run(w, inp, cache_init=init)
+    for launch in (M.FORCE_SMALL_T, M.FORCE_LARGE_T):
+        q, cache = _run_subsets(w, inp, [M.CACHE_ROWS_ONLY, M.Q_ROWS_ONLY], launch, init)
+        assert_same(q, want_q, "q_out", dtype == "fp16")
+        assert_same(cache, want_cache, "cache")
+
+
 def test_zero_tokens_launches_nothing():
     w = I.custom(0, 16, num_blocks=1)
     inp = I.make_inputs(w)
@@ -454,9 +515,6 @@ def test_graph_replays_match_eager():
         assert_same(bits(q.cpu()), want_q, "q_out")
         assert_same(bits(dev["cache"].cpu()), want_cache, "cache")
 
-
-VARIANTS = [("fp16", "neox", "f32"), ("bf16", "gptj", "f32"), ("bf16", "neox", "bf16"),
-            ("fp16", "gptj", "bf16")]
 
 
 @pytest.mark.parametrize("dtype,style,table", VARIANTS, ids=["-".join(v) for v in VARIANTS])
@@ -569,15 +627,18 @@ def test_page_call_with_variants():
     assert_same(bits(dev["cache"].cpu()), want_cache, "cache", True)
 
 
-@pytest.mark.parametrize("T,H", [(64, 16), (8, 128)])
+@pytest.mark.parametrize("T,H", [(64, 16), (8, 128), (1, 16)])
 @pytest.mark.parametrize("force", ["plan", "small", "mid", "large"])
-def test_decode_slice_views_in_a_graph(T, H, force):
-    """The epilogue reads its inputs as strided views of upstream GEMM outputs
+@pytest.mark.parametrize("fork", [False, True], ids=["one-launch", "forked"])
+def test_decode_slice_views_in_a_graph(T, H, force, fork):
+    """The epilogue reads its inputs as strided views of upstream outputs
     (q_pe inside [T,H,192], ql_nope as the transposed [H,T,512] product,
-    kv_c/k_pe inside one [T,576] row), captured with the producers in a HIP
-    graph, under the plan's mapping and each forced one; every replay equals
-    the oracle on the materialised inputs."""
-    announce(f"decode slice in a graph T={T} H={H} mapping={force}")
+    k_pe inside the [T,2112] fused-A output), captured with the producers in
+    a HIP graph, under the plan's mapping and each forced one; forked, the
+    cache rows run on a second captured stream beside the q_b and W_UK
+    products and the query rows after them.  Every replay equals the oracle
+    on the materialised inputs."""
+    announce(f"decode slice in a graph T={T} H={H} mapping={force} fork={fork}")
     import bench
     ds = bench.DecodeSlice(T, H, DEV)
     ds.flags |= {"plan": 0, "small": M.FORCE_SMALL_T, "mid": M.FORCE_MID_T,
@@ -585,11 +646,12 @@ def test_decode_slice_views_in_a_graph(T, H, force):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        ds.step()
+        ds.step(fork=fork)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     ql_nope, q_pe, kv_c, k_pe = ds.producers()
     assert ql_nope.stride() == (512, T * 512, 1) and q_pe.stride() == (H * 192, 192, 1)
+    assert k_pe.stride() == (2112, 1)
     w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
     inp = I.make_inputs(w)
     inp.update(ql_nope=ql_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(),
@@ -597,7 +659,7 @@ def test_decode_slice_views_in_a_graph(T, H, force):
     want_q, want_cache = oracle_run(w, inp)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        ds.step()
+        ds.step(fork=fork)
     for _ in range(3):
         ds.q_out.view(torch.uint8).fill_(0xFF)
         ds.cache.view(torch.uint8).fill_(0)
