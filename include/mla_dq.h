@@ -179,7 +179,9 @@ typedef struct mla_dq_launch_plan {
                                  2 = mid-T (latency, 128 threads)              */
     int32_t streaming;        /* 1 = non-temporal loads and stores               */
     int32_t block_threads;    /* threads per workgroup (a multiple of 64)        */
-    int32_t rows_per_wave;    /* latent rows per wavefront                       */
+    int32_t rows_per_wave;    /* latent rows per wavefront (2 for mid-size calls
+                                 of the throughput mapping under the default
+                                 cache policy, else 1)                            */
     int32_t tail_steps;       /* steps of 8 tails per wavefront                  */
     int32_t reserved;
     int64_t small_rows_max;   /* row threshold of the small-T mapping in force

@@ -145,7 +145,10 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     if (flags & MLA_DQ_FORCE_STREAM) streaming = 1;
     if (flags & MLA_DQ_FORCE_CACHED) streaming = 0;
     const Mapping& m = mapping == 0 ? kSmallMapping : (mapping == 2 ? kMidMapping : kLargeMapping);
-    const int64_t latent_per_block = int64_t(m.block / 64) * m.rows_per_wave;
+    int rows_per_wave = m.rows_per_wave;
+    if (mapping == 1 && !streaming && bytes >= kMidSizeBytesMin && bytes <= kMidSizeBytesMax)
+        rows_per_wave = kMidSizeRowsPerWave;
+    const int64_t latent_per_block = int64_t(m.block / 64) * rows_per_wave;
     const int64_t tails_per_block = int64_t(m.block / 8) * m.tail_steps;
     int64_t tail_blocks = (rows + tails_per_block - 1) / tails_per_block;
 #if MLA_DQ_XCD_REMAP
@@ -156,7 +159,7 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     out->mapping = mapping;
     out->streaming = streaming;
     out->block_threads = m.block;
-    out->rows_per_wave = m.rows_per_wave;
+    out->rows_per_wave = rows_per_wave;
     out->tail_steps = m.tail_steps;
     out->reserved = 0;
     out->small_rows_max = rows_thr;

@@ -533,6 +533,11 @@ static hipError_t launch_mapping(const KernelArgs& a, const mla_dq_launch_plan& 
     if (plan.mapping == 2)
         return launch_flags<kMidMapping.block, kMidMapping.rows_per_wave,
                             kMidMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
+    if constexpr (!STREAM) {
+        if (plan.rows_per_wave == kMidSizeRowsPerWave && kMidSizeRowsPerWave != kLargeMapping.rows_per_wave)
+            return launch_flags<kLargeMapping.block, kMidSizeRowsPerWave, kLargeMapping.tail_steps, STREAM, VAR>(
+                a, grid, flags, stream);
+    }
     return launch_flags<kLargeMapping.block, kLargeMapping.rows_per_wave,
                         kLargeMapping.tail_steps, STREAM, VAR>(a, grid, flags, stream);
 }

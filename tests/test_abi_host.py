@@ -340,6 +340,20 @@ def test_plan_defaults_match_measured_choice():
         assert p.small_rows_max == (2560 if H <= 32 else 896) and p.mid_rows_max == 5120
 
 
+def test_plan_rows_per_wave_by_size_and_policy():
+    """The throughput mapping moves two latent rows per wavefront for calls
+    of 24 to 96 MiB under the default cache policy (the 256-token full-head
+    workload), one otherwise."""
+    for T, H, fl, want in ((256, 128, M.ROPE | M.Q_FP8, 2), (8192, 16, M.ROPE | M.KV_FP8, 1),
+                           (128, 128, M.ROPE | M.Q_FP8, 2), (64, 128, M.ROPE | M.Q_FP8, 1),
+                           (512, 128, M.ROPE | M.Q_FP8, 1), (1024, 16, M.ROPE | M.KV_FP8, 2),
+                           (256, 128, M.ROPE | M.Q_FP8 | M.FORCE_STREAM, 1),
+                           (256, 128, M.ROPE | M.Q_FP8 | M.FORCE_MID_T, 1)):
+        p = M.plan(_dims(T=T, H=H, NB=4096), fl)
+        in_band = p.mapping == 1 and not p.streaming and (24 << 20) <= p.bytes <= (96 << 20)
+        assert p.rows_per_wave == want == (2 if in_band else 1), (T, H, fl)
+
+
 def test_plan_rejects_bad_input():
     with pytest.raises(M.MlaDqError):
         M.plan(_dims(T=-1), 0)

@@ -179,7 +179,7 @@ FLAG_SETS = [(r, q, k) for r in (False, True) for q in (False, True) for k in (F
 
 
 @pytest.mark.parametrize("T,H", [(1, 1), (2, 3), (7, 16), (33, 5), (63, 16), (100, 1),
-                                 (129, 7), (300, 128), (1000, 16)])
+                                 (129, 7), (300, 128), (255, 128), (1000, 16)])
 @pytest.mark.parametrize("fl", FLAG_SETS, ids=lambda f: "r%dq%dk%d" % f)
 def test_ragged_shapes_all_modes(T, H, fl):
     rope, qf, kf = fl
