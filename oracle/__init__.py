@@ -74,6 +74,9 @@ def _configure(lib):
     lib.oracle_rope_f32.restype = None
     lib.oracle_rope_f64.argtypes = [f32p, f32p, f32p, ctypes.c_int, f64p]
     lib.oracle_rope_f64.restype = None
+    lib.oracle_uk_product.argtypes = [f64p, f64p, u16p, u16p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int]
+    lib.oracle_uk_product.restype = None
     lib.oracle_fp16_to_f32.argtypes = [ctypes.c_uint16]
     lib.oracle_fp16_to_f32.restype = ctypes.c_float
     lib.oracle_f32_to_fp16_rne.argtypes = [ctypes.c_float]
@@ -209,6 +212,28 @@ def rope_neox_f64(x_bits: np.ndarray, cs_row: np.ndarray) -> np.ndarray:
     _load().oracle_rope_neox_f64(_ptr(x, ctypes.c_uint16), _ptr(cs, ctypes.c_float),
                                  _ptr(y, ctypes.c_double))
     return y
+
+
+# ---- the absorbed key projection (for the epilogue fused into it) ----------
+
+def uk_product(q_nope: np.ndarray, w_uk_t: np.ndarray, fp16: bool = False,
+               with_mag: bool = False):
+    """ql[t,h,n] = sum_k q_nope[t,h,k] * w_uk_t[h,n,k], evaluated in double.
+
+    q_nope [T, H, 128] and w_uk_t [H, 512, 128] are bf16 (or fp16) bit
+    patterns (uint16).  Returns float64 [T, H, 512]; with ``with_mag`` also
+    sum_k |q_nope[t,h,k] * w_uk_t[h,n,k]|, the scale of any fp32 evaluation's
+    rounding error."""
+    q = np.ascontiguousarray(q_nope, dtype=np.uint16)
+    w = np.ascontiguousarray(w_uk_t, dtype=np.uint16)
+    T, H = q.shape[0], q.shape[1]
+    assert q.shape == (T, H, 128) and w.shape == (H, 512, 128)
+    out = np.empty((T, H, 512), dtype=np.float64)
+    mag = np.empty((T, H, 512), dtype=np.float64) if with_mag else None
+    _load().oracle_uk_product(_ptr(out, ctypes.c_double),
+                              _ptr(mag, ctypes.c_double) if with_mag else None,
+                              _ptr(q, ctypes.c_uint16), _ptr(w, ctypes.c_uint16), T, H, int(fp16))
+    return (out, mag) if with_mag else out
 
 
 # ---- the whole epilogue ---------------------------------------------------

@@ -32,7 +32,11 @@
  *    definition: bias 7, subnormal step 2^-9, max 448, NaN = S.1111.111);
  *  - positions outside [0, max_position) are clamped into the table;
  *  - slots outside [0, num_slots) leave the cache untouched (padding tokens);
- *  - with duplicate slots the later token's row is the one left in the cache.
+ *  - with duplicate slots the later token's row is the one left in the cache;
+ *  - for the epilogue fused into the absorbed key projection ahead of it,
+ *    ql_nope is that product's exact value (a double sum of exact products,
+ *    W_UK handed over transposed as [H, 512, 128]), encoded once: the fused
+ *    path never rounds ql_nope to the activation type before encoding.
  *
  * Every function here is pinned by tests against format definitions, closed
  * forms, library routines and brute force (see tests/test_oracle_pins.py).
@@ -224,6 +228,39 @@ void oracle_rope_neox_f64(const uint16_t* x, const float* cs, double* y) {
 static float elem_to_f32(uint16_t v, int fp16) {
     return fp16 ? oracle_fp16_to_f32(v) : oracle_bf16_to_f32(v);
 }
+
+/* The absorbed key projection whose output the epilogue reads (the page's
+ * kernel waits for that product before it touches ql_nope, "implementation
+ * breakdown" item 2).  With W_UK given transposed, w_uk_t[h, n, k] =
+ * W_UK[h, k, n]:
+ *   ql[t, h, n] = sum over k < 128 of q_nope[t, h, k] * w_uk_t[h, n, k],  n < 512
+ *   mag[t, h, n] = sum over k < 128 of |q_nope[t, h, k] * w_uk_t[h, n, k]|
+ * Inputs are activation bit patterns (bf16, or fp16 when asked for),
+ * contiguous: [T, H, 128] and [H, 512, 128].  Each product of two such values
+ * is exact in double and the sums are formed in double in increasing k, so
+ * ql is the exact value up to double rounding; mag (may be NULL) bounds how
+ * far any fp32 evaluation of the sum can stray from it. */
+void oracle_uk_product(double* ql, double* mag, const uint16_t* q_nope, const uint16_t* w_uk_t,
+                       int64_t T, int64_t H, int fp16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            const uint16_t* q = q_nope + ((size_t)t * H + h) * 128;
+            for (int64_t n = 0; n < NOPE; ++n) {
+                const uint16_t* w = w_uk_t + ((size_t)h * NOPE + n) * 128;
+                double acc = 0.0, acc_abs = 0.0;
+                for (int k = 0; k < 128; ++k) {
+                    const double prod = (double)elem_to_f32(q[k], fp16) * (double)elem_to_f32(w[k], fp16);
+                    acc += prod;
+                    acc_abs += fabs(prod);
+                }
+                const size_t o = ((size_t)t * H + h) * NOPE + n;
+                ql[o] = acc;
+                if (mag) mag[o] = acc_abs;
+            }
+        }
+}
+
 
 static uint16_t f32_to_elem(float x, int fp16) {
     return fp16 ? oracle_f32_to_fp16_rne(x) : oracle_f32_to_bf16_rne(x);

@@ -50,6 +50,14 @@ MUTANTS = [
     ("q_rows_transposed", "int64_t r = t * H + h;", "int64_t r = h * T + t;"),
     ("rope_f64_sign", "y[i0] = a * c - b * s;", "y[i0] = a * c + b * s;"),
     ("rope_f64_dropped_term", "y[i1] = b * c + a * s;", "y[i1] = b * c;"),
+    ("uk_weight_head_ignored", "w_uk_t + ((size_t)h * NOPE + n) * 128;", "w_uk_t + ((size_t)n) * 128;"),
+    ("uk_weight_read_untransposed", "(double)elem_to_f32(w[k], fp16);",
+     "(double)elem_to_f32(w_uk_t[((size_t)h * 128 + k) * NOPE + n], fp16);"),
+    ("uk_last_k_dropped", "for (int k = 0; k < 128; ++k) {\n                    const double prod",
+     "for (int k = 0; k < 127; ++k) {\n                    const double prod"),
+    ("uk_query_head_shifted", "q_nope + ((size_t)t * H + h) * 128;", "q_nope + ((size_t)t * H + (h + 1) % H) * 128;"),
+    ("uk_magnitude_signed", "acc_abs += fabs(prod);", "acc_abs += prod;"),
+    ("uk_fp16_read_as_bf16", "(double)elem_to_f32(q[k], fp16)", "(double)elem_to_f32(q[k], 0)"),
 ]
 
 CHECKS = [
@@ -72,6 +80,11 @@ CHECKS = [
     lambda: P.test_oracle_matches_library_composition_all_modes((True, True, False)),
     P.test_out_of_range_slots_leave_cache_untouched,
     lambda: P.test_rope_f64_is_the_complex_product_with_the_table_row(True),
+    lambda: P.test_uk_product_matches_library_matmul(False),
+    lambda: P.test_uk_product_matches_library_matmul(True),
+    P.test_uk_product_unit_rows_select_one_input,
+    P.test_uk_product_integers_brute_force,
+    P.test_uk_product_magnitude_is_the_absolute_sum,
 ]
 
 

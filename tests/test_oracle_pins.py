@@ -552,3 +552,78 @@ def test_duplicate_slots_keep_later_token():
     _, cache = oracle_run(w, inp)
     want = bits(torch.cat([inp["kv_c"][1], inp["k_pe"][1]]))
     assert np.array_equal(cache.reshape(-1, 576)[5], want)
+
+
+# ------------------------------------------- the absorbed key projection ----
+# The product that produces ql_nope (the page's kernel reads its output,
+# "implementation breakdown" item 2): ql[t,h,n] = sum_k q_nope[t,h,k] W_UK[h,k,n],
+# with W_UK handed over transposed as w_uk_t[h,n,k].
+
+def _act(x: torch.Tensor, fp16: bool) -> np.ndarray:
+    dt = torch.float16 if fp16 else torch.bfloat16
+    return x.to(dt).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("fp16", [False, True])
+def test_uk_product_matches_library_matmul(fp16):
+    """A float64 matmul of the decoded values, per head (library routine)."""
+    g = torch.Generator().manual_seed(11)
+    T, H = 9, 3
+    q = _act(torch.randn(T, H, 128, generator=g), fp16)
+    w = _act(torch.randn(H, 512, 128, generator=g) * 128 ** -0.5, fp16)
+    dt = torch.float16 if fp16 else torch.bfloat16
+    qd = torch.from_numpy(q.view(np.int16)).view(dt).double().numpy()
+    wd = torch.from_numpy(w.view(np.int16)).view(dt).double().numpy()
+    ref = np.stack([qd[:, h, :] @ wd[h].T for h in range(H)], axis=1)
+    ql, mag = oracle.uk_product(q, w, fp16=fp16, with_mag=True)
+    np.testing.assert_allclose(ql, ref, rtol=1e-13, atol=1e-13)
+    ref_mag = np.stack([np.abs(qd[:, h, :]) @ np.abs(wd[h]).T for h in range(H)], axis=1)
+    np.testing.assert_allclose(mag, ref_mag, rtol=1e-13, atol=0)
+
+
+def test_uk_product_unit_rows_select_one_input():
+    """Row n of head h's transposed weight is the unit vector e_{(5n + 3h) % 128}:
+    the product then picks q_nope[t, h, (5n + 3h) % 128] exactly.  A transposed
+    weight, a wrong head or a shifted k fails this."""
+    g = torch.Generator().manual_seed(12)
+    T, H = 4, 5
+    q = _act(torch.randn(T, H, 128, generator=g), False)
+    w = np.zeros((H, 512, 128), dtype=np.uint16)
+    pick = np.array([[(5 * n + 3 * h) % 128 for n in range(512)] for h in range(H)])
+    for h in range(H):
+        w[h, np.arange(512), pick[h]] = 0x3F80           # bf16 1.0
+    ql, mag = oracle.uk_product(q, w, with_mag=True)
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for h in range(H):
+        assert np.array_equal(ql[:, h, :], qd[:, h, pick[h]])
+        assert np.array_equal(mag[:, h, :], np.abs(qd[:, h, pick[h]]))
+
+
+def test_uk_product_integers_brute_force():
+    """Small integers (exact in bf16) against an integer triple loop."""
+    rng = np.random.default_rng(13)
+    T, H = 2, 2
+    qi = rng.integers(-8, 9, size=(T, H, 128))
+    wi = rng.integers(-8, 9, size=(H, 512, 128))
+    q = _act(torch.from_numpy(qi).float(), False)
+    w = _act(torch.from_numpy(wi).float(), False)
+    ql, mag = oracle.uk_product(q, w, with_mag=True)
+    for t in range(T):
+        for h in range(H):
+            for n in range(0, 512, 37):
+                exact = sum(int(qi[t, h, k]) * int(wi[h, n, k]) for k in range(128))
+                absum = sum(abs(int(qi[t, h, k]) * int(wi[h, n, k])) for k in range(128))
+                assert ql[t, h, n] == exact and mag[t, h, n] == absum
+
+
+def test_uk_product_magnitude_is_the_absolute_sum():
+    """Nonnegative inputs: the absolute sum equals the sum; flipping signs
+    leaves it and only shrinks the sum."""
+    g = torch.Generator().manual_seed(14)
+    qa = torch.rand(3, 2, 128, generator=g)
+    wa = torch.rand(2, 512, 128, generator=g)
+    ql, mag = oracle.uk_product(_act(qa, False), _act(wa, False), with_mag=True)
+    assert np.array_equal(ql, mag)
+    sign = torch.where(torch.rand(3, 2, 128, generator=g) < 0.5, -1.0, 1.0)
+    ql2, mag2 = oracle.uk_product(_act(qa * sign, False), _act(wa, False), with_mag=True)
+    assert np.array_equal(mag2, mag) and np.all(np.abs(ql2) <= mag2)
