@@ -201,6 +201,84 @@ typedef struct mla_dq_launch_plan {
  * (Pointers are not checked here; T == 0 gives grid_blocks = 0.) */
 int mla_dq_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* plan);
 
+/* ---- the epilogue fused into the W_UK product ------------------------------
+ *
+ * In a decode step ql_nope is the output of the per-head absorbed key
+ * projection, and the page's kernel starts by waiting for that product
+ * ("implementation breakdown" item 2).  This entry point does the product
+ * and the epilogue in one launch, so ql_nope is never stored or read back:
+ *
+ *   ql[t, h, n] = sum over k < 128 of q_nope[t, h, k] * W_UK[h, k, n]     n < 512
+ *   q_out[t, h, 0:512] = enc_q( ql[t, h, 0:512] )
+ *
+ * and everything else (the rotated tails of q, the cache rows) exactly as
+ * mla_decode_q_concat_kv_insert writes it.  The sum is formed in fp32 on the
+ * matrix cores (bf16 or fp16 products, exact in fp32); its order of
+ * additions is the library's, so ql is the exact sum within
+ * 2^-16 * sum_k |q_nope[t,h,k] * W_UK[h,k,n]| (well above the fp32 rounding
+ * bound of a 128-term sum), and enc_q rounds that fp32 value once: to bf16 /
+ * fp16 (nearest even), or to E4M3 of fl32(ql * fl32(1/q_scale)) clamped to
+ * [-448, 448].
+ *
+ *   q_nope   [T, H, 128] activations: element (t, h, k) at
+ *            t * dims->ql_nope_stride_t + h * dims->ql_nope_stride_h + k (the
+ *            two ql_nope strides of mla_dq_dims describe q_nope here), e.g.
+ *            the first 128 of each head's 192 columns of the q projection's
+ *            output.  16-B aligned, strides multiples of 8 elements.
+ *   w_uk_t   [H, 512, 128] activations, dense: w_uk_t[h, n, k] = W_UK[h, k, n]
+ *            (each head's W_UK transposed once, when the weights are loaded,
+ *            so that both operands of the product run along k).  16-B aligned.
+ *   all other arguments as for mla_decode_q_concat_kv_insert.
+ *
+ * Flags: MLA_DQ_ROPE, _Q_FP8, _KV_FP8, _FP16 (activations, weights and
+ * unquantised outputs fp16), _ROPE_GPTJ, _TABLE_BF16, and the launch
+ * overrides MLA_DQ_FORCE_SMALL_T / _FORCE_LARGE_T (latency or throughput
+ * configuration, below) and _FORCE_STREAM / _FORCE_CACHED.  The row subsets
+ * and MLA_DQ_FORCE_MID_T give MLA_DQ_ERR_FLAGS.  q_out and the cache must not
+ * overlap q_nope or w_uk_t either (MLA_DQ_ERR_ALIAS).  Errors and ownership
+ * as for mla_decode_q_concat_kv_insert.
+ */
+int mla_decode_uk_q_concat_kv_insert(void* q_out, const void* q_nope, const void* w_uk_t,
+                                     const void* q_pe, const void* kv_c, const void* k_pe,
+                                     void* cache, const int64_t* slot_mapping,
+                                     const int64_t* positions, const float* rope_cos_sin,
+                                     const float* q_scale, const float* kv_scale, uint32_t flags,
+                                     const mla_dq_dims* dims, void* stream);
+
+/* The launch of the fused product: host-only, as mla_dq_plan.  One grid of
+ * block_threads-thread workgroups holds three kinds: product workgroups
+ * first, each for one head, one group of latent columns and a range of
+ * tokens (every wavefront holds 16 * n_blocks columns of W_UK in registers
+ * and steps through the range 16 tokens at a time, one matrix-core product
+ * per 16 x 16 x 32 tile); then the positional tails of all T * (H + 1) rows;
+ * then the latent parts of the T cache rows.  The latency configuration
+ * (fewest query rows) takes 16 tokens per product workgroup and narrow
+ * column groups, so that even one token spreads over many workgroups; the
+ * throughput configuration takes wider groups and longer token ranges (up to
+ * 128 tokens, shortened while fewer than about 2048 product workgroups would
+ * result), so that each q_nope row and each weight row is read fewer times. */
+typedef struct mla_dq_uk_launch_plan {
+    int32_t mapping;          /* 0 = latency, 1 = throughput                     */
+    int32_t streaming;        /* 1 = non-temporal loads and stores               */
+    int32_t block_threads;    /* threads per workgroup                           */
+    int32_t n_blocks;         /* 16-column blocks of W_UK per wavefront           */
+    int32_t tail_steps;       /* steps of 8 tails per wavefront                  */
+    int32_t tokens_per_group; /* tokens per product workgroup (a multiple of 16) */
+    int64_t column_groups;    /* product workgroups per (head, token range)      */
+    int64_t units;            /* H * ceil(T / tokens_per_group)                  */
+    int64_t product_blocks;   /* product workgroups (a multiple of 8)            */
+    int64_t tail_blocks;      /* workgroups doing positional tails               */
+    int64_t cache_blocks;     /* workgroups doing the cache rows' latent parts   */
+    int64_t grid_blocks;      /* the sum of the three                            */
+    int64_t bytes;            /* bytes the call reads and writes, W_UK once      */
+    int64_t flops;            /* 2 * T * H * 128 * 512                           */
+    int64_t stream_bytes_min; /* byte threshold in force                         */
+    int64_t large_rows_min;   /* T * H from which the throughput configuration
+                                 is the default                                  */
+} mla_dq_uk_launch_plan;
+
+int mla_dq_uk_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_uk_launch_plan* plan);
+
 #ifdef __cplusplus
 }
 #endif

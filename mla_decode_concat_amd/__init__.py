@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     FORCE_MID_T, Q_ROWS_ONLY, CACHE_ROWS_ONLY,
     MlaDqError, Dims, LaunchPlan, fused_mla_decode_q_concat_kv_cache_insert,
     mla_decode_q_concat_kv_insert, PreparedInsert, plan, strerror, load,
+    UkLaunchPlan, uk_plan, mla_decode_uk_q_concat_kv_insert, PreparedUkInsert,
     ATTN_Q_FP8, ATTN_KV_FP8, AttnDims, AttnPlan, PreparedAttention, attn_plan,
     attn_workspace_size, mla_decode_attention, mla_decode_attention_noalloc,
 )

@@ -40,7 +40,7 @@ ERR_LAUNCH = -5
 ERR_ALIAS = -6
 
 EXPORTED_SYMBOLS = ("mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan",
-                    "mla_dq_source_digest")
+                    "mla_dq_source_digest", "mla_decode_uk_q_concat_kv_insert", "mla_dq_uk_plan")
 
 
 class Dims(ctypes.Structure):
@@ -58,6 +58,15 @@ class LaunchPlan(ctypes.Structure):
                 ("bytes", ctypes.c_int64), ("tail_blocks", ctypes.c_int64),
                 ("latent_blocks", ctypes.c_int64), ("grid_blocks", ctypes.c_int64),
                 ("total_rows", ctypes.c_int64), ("mid_rows_max", ctypes.c_int64)]
+
+
+class UkLaunchPlan(ctypes.Structure):
+    _fields_ = [("mapping", ctypes.c_int32), ("streaming", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("tail_steps", ctypes.c_int32), ("tokens_per_group", ctypes.c_int32)] + [
+        (n, ctypes.c_int64) for n in (
+            "column_groups", "units", "product_blocks", "tail_blocks", "cache_blocks", "grid_blocks",
+            "bytes", "flops", "stream_bytes_min", "large_rows_min")]
 
 
 class MlaDqError(RuntimeError):
@@ -116,6 +125,12 @@ def load() -> ctypes.CDLL:
         lib.mla_dq_strerror.restype = ctypes.c_char_p
         lib.mla_dq_plan.argtypes = [ctypes.POINTER(Dims), ctypes.c_uint32, ctypes.POINTER(LaunchPlan)]
         lib.mla_dq_plan.restype = ctypes.c_int
+        lib.mla_decode_uk_q_concat_kv_insert.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i64p, i64p, f32p, f32p, f32p, ctypes.c_uint32,
+            ctypes.POINTER(Dims), vp]
+        lib.mla_decode_uk_q_concat_kv_insert.restype = ctypes.c_int
+        lib.mla_dq_uk_plan.argtypes = [ctypes.POINTER(Dims), ctypes.c_uint32, ctypes.POINTER(UkLaunchPlan)]
+        lib.mla_dq_uk_plan.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -130,6 +145,24 @@ def plan(dims: Dims, flags: int) -> LaunchPlan:
     if rc != OK:
         raise MlaDqError(rc, strerror(rc))
     return p
+
+
+def uk_plan(dims: Dims, flags: int) -> UkLaunchPlan:
+    """The launch of the epilogue fused into the W_UK product (dims as for
+    the epilogue; the ql_nope strides describe q_nope)."""
+    p = UkLaunchPlan()
+    rc = load().mla_dq_uk_plan(ctypes.byref(dims), ctypes.c_uint32(flags), ctypes.byref(p))
+    if rc != OK:
+        raise MlaDqError(rc, strerror(rc))
+    return p
+
+
+def raw_uk_call(q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                rope_cos_sin, q_scale, kv_scale, flags: int, dims: Dims, stream) -> int:
+    """Call the fused product's C entry point with integer addresses; returns its code."""
+    return load().mla_decode_uk_q_concat_kv_insert(
+        q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+        q_scale, kv_scale, ctypes.c_uint32(flags), ctypes.byref(dims), stream)
 
 
 def raw_call(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
@@ -185,10 +218,14 @@ def mla_decode_q_concat_kv_insert(q_out: torch.Tensor, ql_nope: torch.Tensor, q_
 
 
 def _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
-                   rope_cos_sin, q_scale, kv_scale, flags) -> None:
-    """Dtype, shape, layout and device checks the C ABI cannot make."""
+                   rope_cos_sin, q_scale, kv_scale, flags, nope_name: str = "ql_nope",
+                   nope_width: int = 512, extra: tuple = ()) -> None:
+    """Dtype, shape, layout and device checks the C ABI cannot make.  For the
+    fused product the no-position input is q_nope [T, H, 128] and ``extra``
+    holds (name, tensor) pairs of further activation-typed inputs (W_UK)."""
     T = ql_nope.shape[0]
-    _check(ql_nope.dim() == 3 and ql_nope.shape[2] == 512, "ql_nope must be [T, H, 512]")
+    _check(ql_nope.dim() == 3 and ql_nope.shape[2] == nope_width,
+           f"{nope_name} must be [T, H, {nope_width}]")
     H = ql_nope.shape[1]
     _check(tuple(q_pe.shape) == (T, H, 64), "q_pe must be [T, H, 64]")
     _check(tuple(kv_c.shape) == (T, 512) and tuple(k_pe.shape) == (T, 64),
@@ -198,7 +235,7 @@ def _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positi
     _check(cache.dim() == 3 and cache.shape[2] == 576 and cache.is_contiguous(),
            "cache must be a contiguous [num_blocks, block_size, 576] tensor")
     act = torch.float16 if flags & FP16 else torch.bfloat16
-    for name, t in (("ql_nope", ql_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe)):
+    for name, t in ((nope_name, ql_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe), *extra):
         _check(t.dtype == act, f"{name} must be {act} (flag FP16 selects fp16)")
         _check(t.stride(-1) == 1, f"{name} must have unit inner stride")
     _check(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,)
@@ -227,7 +264,7 @@ def _validate_only(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positi
     dev = q_out.device
     _check(dev.type == "cuda", "tensors must be on a GPU")
     for t in (ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin, q_scale,
-              kv_scale):
+              kv_scale, *(e[1] for e in extra)):
         if t is not None:
             _check(t.device == dev, "all tensors must be on the same GPU")
 
@@ -245,8 +282,9 @@ except AttributeError:  # pragma: no cover
         return torch.cuda.current_stream(index).cuda_stream
 
 
-def _launch(args: tuple, flags: int, dims: Dims, index: int, stream) -> None:
-    fn = load().mla_decode_q_concat_kv_insert
+def _launch(args: tuple, flags: int, dims: Dims, index: int, stream,
+            entry: str = "mla_decode_q_concat_kv_insert") -> None:
+    fn = getattr(load(), entry)
     if index == torch.cuda.current_device():
         rc = fn(*args, flags, ctypes.byref(dims), _raw_stream(index, stream))
     else:
@@ -276,6 +314,56 @@ class PreparedInsert:
 
     def __call__(self, stream=None) -> None:
         _launch(self._args, self._flags, self._dims, self._index, stream)
+
+
+def _validate_uk(q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                 rope_cos_sin, q_scale, kv_scale, flags) -> None:
+    H = q_nope.shape[1] if q_nope.dim() == 3 else -1
+    _check(w_uk_t.dim() == 3 and tuple(w_uk_t.shape) == (H, 512, 128) and w_uk_t.is_contiguous(),
+           "w_uk_t must be a contiguous [H, 512, 128] tensor (W_UK transposed per head)")
+    _validate_only(q_out, q_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions, rope_cos_sin,
+                   q_scale, kv_scale, flags, "q_nope", 128, (("w_uk_t", w_uk_t),))
+
+
+def mla_decode_uk_q_concat_kv_insert(q_out: torch.Tensor, q_nope: torch.Tensor, w_uk_t: torch.Tensor,
+                                     q_pe: torch.Tensor, kv_c: torch.Tensor, k_pe: torch.Tensor,
+                                     cache: torch.Tensor, slot_mapping: torch.Tensor,
+                                     positions: torch.Tensor | None = None,
+                                     rope_cos_sin: torch.Tensor | None = None,
+                                     q_scale: torch.Tensor | None = None,
+                                     kv_scale: torch.Tensor | None = None, flags: int = 0,
+                                     stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the epilogue fused into the W_UK product: q_out [T,H,576] gets
+    enc(q_nope[t,h] @ W_UK[h]) in columns 0..511 and the rotated q_pe tail;
+    the cache rows are written as by mla_decode_q_concat_kv_insert.
+    ``q_nope`` is [T, H, 128] (strided, e.g. a view of the q projection's
+    [T, H, 192] output) and ``w_uk_t`` [H, 512, 128] holds each head's W_UK
+    transposed."""
+    _validate_uk(q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                 rope_cos_sin, q_scale, kv_scale, flags)
+    dims = _dims(q_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
+    args = (_ptr(q_out), _ptr(q_nope), _ptr(w_uk_t), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(cache),
+            _ptr(slot_mapping), _ptr(positions), _ptr(rope_cos_sin), _ptr(q_scale), _ptr(kv_scale))
+    _launch(args, flags, dims, q_out.device.index, stream, "mla_decode_uk_q_concat_kv_insert")
+
+
+class PreparedUkInsert:
+    """mla_decode_uk_q_concat_kv_insert bound to fixed tensors (checked and
+    marshalled once; each call only enqueues the launch)."""
+
+    def __init__(self, q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions=None,
+                 rope_cos_sin=None, q_scale=None, kv_scale=None, flags: int = 0):
+        tensors = (q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                   rope_cos_sin, q_scale, kv_scale)
+        _validate_uk(*tensors, flags)
+        self._tensors = tensors
+        self._args = tuple(_ptr(t) for t in tensors)
+        self._dims = _dims(q_nope, q_pe, kv_c, k_pe, cache, rope_cos_sin)
+        self._flags = flags
+        self._index = q_out.device.index
+
+    def __call__(self, stream=None) -> None:
+        _launch(self._args, self._flags, self._dims, self._index, stream, "mla_decode_uk_q_concat_kv_insert")
 
 
 def fused_mla_decode_q_concat_kv_cache_insert(ql_nope: torch.Tensor, q_pe: torch.Tensor,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_dq.so")
 SOURCES = [os.path.join(CSRC, "mla_dq_api.hip"), os.path.join(CSRC, "mla_dq_kernel.hip"),
-           os.path.join(CSRC, "mla_attn.hip")]
+           os.path.join(CSRC, "mla_dq_uk.hip"), os.path.join(CSRC, "mla_attn.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

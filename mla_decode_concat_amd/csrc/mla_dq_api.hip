@@ -66,7 +66,6 @@ int64_t stream_bytes_min() {
 
 // Bytes one call reads and writes: each 576-wide input row once (2-byte
 // elements), each output row once, plus slot, position and rope table row
-// per token.
 // per token.  A launch restricted to one kind of row counts only its rows
 // (and the slot only with the cache row).
 int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
@@ -80,6 +79,25 @@ int64_t call_bytes(const mla_dq_dims* d, uint32_t flags) {
                                      kv * ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
     return read + write;
 }
+
+int64_t uk_large_rows_min() {
+    static const int64_t v = env_int64("MLA_DQ_UK_LARGE_ROWS_MIN", kDefaultUkLargeRowsMin);
+    return v;
+}
+
+// Bytes of the fused product's call: q_nope (128 elements per query row)
+// instead of ql_nope, W_UK once, and the rest of the epilogue's traffic.
+int64_t uk_call_bytes(const mla_dq_dims* d, uint32_t flags) {
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    const bool rope = flags & MLA_DQ_ROPE;
+    const int64_t table_row = (flags & MLA_DQ_TABLE_BF16) ? 128 : 256;
+    const int64_t read = T * H * (256 + 128) + H * 512 * 128 * 2 +
+                         T * (1152 + 8 + (rope ? 8 + table_row : 0));
+    const int64_t write = T * 576 * (H * ((flags & MLA_DQ_Q_FP8) ? 1 : 2) + ((flags & MLA_DQ_KV_FP8) ? 1 : 2));
+    return read + write;
+}
+
+constexpr uint32_t kUkOnlyUnsupported = MLA_DQ_Q_ROWS_ONLY | MLA_DQ_CACHE_ROWS_ONLY | MLA_DQ_FORCE_MID_T;
 
 // Checks that do not need any pointer: flags and shapes.
 int check_flags_dims(uint32_t flags, const mla_dq_dims* d) {
@@ -173,12 +191,16 @@ int plan(const mla_dq_dims* d, uint32_t flags, mla_dq_launch_plan* out) {
     return MLA_DQ_OK;
 }
 
-int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_c,
-             const void* k_pe, void* cache, const int64_t* slot_mapping,
-             const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
-             const float* kv_scale, uint32_t flags, const mla_dq_dims* d) {
-    const int rc = check_flags_dims(flags, d);
-    if (rc != MLA_DQ_OK) return rc;
+namespace {
+
+// Pointer checks of both entry points.  `nope` is ql_nope [T, H, 512] or, for
+// the fused product, q_nope [T, H, 128] (nope_width elements per row, the
+// ql_nope strides of dims); `extra` is one more input extent (W_UK) or empty.
+int validate_io(void* q_out, const void* nope, int64_t nope_width, Extent extra, const void* q_pe,
+                const void* kv_c, const void* k_pe, void* cache, const int64_t* slot_mapping,
+                const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+                const float* kv_scale, uint32_t flags, const mla_dq_dims* d) {
+    const void* ql_nope = nope;
     const bool rope = flags & MLA_DQ_ROPE, qf8 = flags & MLA_DQ_Q_FP8, kvf8 = flags & MLA_DQ_KV_FP8;
     if (!q_out || !ql_nope || !q_pe || !kv_c || !k_pe || !cache || !slot_mapping)
         return MLA_DQ_ERR_NULL;
@@ -201,7 +223,8 @@ int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_
     const Extent none{0, 0};
     const int64_t table_row = (flags & MLA_DQ_TABLE_BF16) ? 128 : 256;
     const Extent in[] = {
-        extent3(ql_nope, T, H, d->ql_nope_stride_t, d->ql_nope_stride_h, 512, 2),
+        extent3(ql_nope, T, H, d->ql_nope_stride_t, d->ql_nope_stride_h, nope_width, 2),
+        extra,
         extent3(q_pe, T, H, d->q_pe_stride_t, d->q_pe_stride_h, 64, 2),
         extent3(kv_c, T, 1, d->kv_c_stride_t, 0, 512, 2),
         extent3(k_pe, T, 1, d->k_pe_stride_t, 0, 64, 2),
@@ -214,6 +237,111 @@ int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_
     if (overlap(q, c)) return MLA_DQ_ERR_ALIAS;
     for (const Extent& e : in)
         if (overlap(q, e) || overlap(c, e)) return MLA_DQ_ERR_ALIAS;
+    return MLA_DQ_OK;
+}
+
+// The fields both launches share; the row enumeration (row_stride,
+// first_head, rows_per_token, total_rows, tail_blocks) is the caller's.
+KernelArgs common_args(void* q_out, const void* nope, const void* q_pe, const void* kv_c,
+                       const void* k_pe, void* cache, const int64_t* slot_mapping,
+                       const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+                       const float* kv_scale, uint32_t flags, const mla_dq_dims* dims) {
+    KernelArgs a;
+    a.q_out = static_cast<uint8_t*>(q_out);
+    a.ql_nope = static_cast<const uint16_t*>(nope);
+    a.q_pe = static_cast<const uint16_t*>(q_pe);
+    a.kv_c = static_cast<const uint16_t*>(kv_c);
+    a.k_pe = static_cast<const uint16_t*>(k_pe);
+    a.cache = static_cast<uint8_t*>(cache);
+    a.slot_mapping = slot_mapping;
+    a.positions = positions;
+    a.rope_cos_sin = rope_cos_sin;
+    a.q_scale = q_scale;
+    a.kv_scale = kv_scale;
+    a.ql_nope_st = dims->ql_nope_stride_t;
+    a.ql_nope_sh = dims->ql_nope_stride_h;
+    a.q_pe_st = dims->q_pe_stride_t;
+    a.q_pe_sh = dims->q_pe_stride_h;
+    a.kv_c_st = dims->kv_c_stride_t;
+    a.k_pe_st = dims->k_pe_stride_t;
+    a.num_slots = dims->num_blocks * dims->block_size;
+    a.max_position = (flags & MLA_DQ_ROPE) ? dims->max_position : 1;
+    a.num_heads = uint32_t(dims->num_heads);
+    a.fp16 = (flags & MLA_DQ_FP16) ? 1u : 0u;
+    a.gptj = (flags & MLA_DQ_ROPE_GPTJ) ? 1u : 0u;
+    a.table_bf16 = (flags & MLA_DQ_TABLE_BF16) ? 1u : 0u;
+    return a;
+}
+
+}  // namespace
+
+int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_c,
+             const void* k_pe, void* cache, const int64_t* slot_mapping,
+             const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+             const float* kv_scale, uint32_t flags, const mla_dq_dims* d) {
+    const int rc = check_flags_dims(flags, d);
+    if (rc != MLA_DQ_OK) return rc;
+    return validate_io(q_out, ql_nope, 512, Extent{0, 0}, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                       rope_cos_sin, q_scale, kv_scale, flags, d);
+}
+
+int uk_validate(void* q_out, const void* q_nope, const void* w_uk_t, const void* q_pe,
+                const void* kv_c, const void* k_pe, void* cache, const int64_t* slot_mapping,
+                const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+                const float* kv_scale, uint32_t flags, const mla_dq_dims* d) {
+    if (flags & kUkOnlyUnsupported) return MLA_DQ_ERR_FLAGS;
+    const int rc = check_flags_dims(flags, d);
+    if (rc != MLA_DQ_OK) return rc;
+    if (!w_uk_t) return MLA_DQ_ERR_NULL;
+    if (!aligned(w_uk_t, 16)) return MLA_DQ_ERR_ALIGN;
+    return validate_io(q_out, q_nope, 128, span(w_uk_t, d->num_heads * 512 * 128 * 2), q_pe, kv_c, k_pe,
+                       cache, slot_mapping, positions, rope_cos_sin, q_scale, kv_scale, flags, d);
+}
+
+int uk_plan(const mla_dq_dims* d, uint32_t flags, mla_dq_uk_launch_plan* out) {
+    if (out == nullptr) return MLA_DQ_ERR_NULL;
+    if (flags & kUkOnlyUnsupported) return MLA_DQ_ERR_FLAGS;
+    const int rc = check_flags_dims(flags, d);
+    if (rc < 0) return rc;
+    const int64_t T = d->num_tokens, H = d->num_heads;
+    const int64_t large_min = uk_large_rows_min(), bytes_thr = stream_bytes_min();
+    const int64_t bytes = uk_call_bytes(d, flags);
+    int mapping = T * H >= large_min ? 1 : 0;
+    if (flags & MLA_DQ_FORCE_SMALL_T) mapping = 0;
+    if (flags & MLA_DQ_FORCE_LARGE_T) mapping = 1;
+    int streaming = bytes >= bytes_thr ? 1 : 0;
+    if (flags & MLA_DQ_FORCE_STREAM) streaming = 1;
+    if (flags & MLA_DQ_FORCE_CACHED) streaming = 0;
+    const int64_t block = MLA_DQ_UK_BLOCK, waves = block / 64;
+    const int64_t nb = mapping ? MLA_DQ_UK_LARGE_NB : MLA_DQ_UK_SMALL_NB;
+    const int64_t tail_steps = mapping ? kLargeMapping.tail_steps : 1;
+    const int64_t groups = 512 / (waves * 16 * nb);
+    int64_t tpg = mapping ? MLA_DQ_UK_LARGE_TOKENS : MLA_DQ_UK_SMALL_TOKENS;
+    while (tpg > 16 && H * ((T + tpg - 1) / tpg) * groups < MLA_DQ_UK_TARGET_BLOCKS) tpg /= 2;
+    const int64_t units = H * ((T + tpg - 1) / tpg);
+    const int64_t product_blocks = 8 * groups * ((units + 7) / 8);
+    const int64_t tails_per_block = (block / 8) * tail_steps;
+    const int64_t tail_blocks = (T * (H + 1) + tails_per_block - 1) / tails_per_block;
+    const int64_t cache_blocks = (T + waves - 1) / waves;
+    const int64_t grid = product_blocks + tail_blocks + cache_blocks;
+    // Work-item indices of a launch stay below 2^32.
+    if (grid * block > int64_t(UINT32_MAX)) return MLA_DQ_ERR_DIM;
+    out->mapping = mapping;
+    out->streaming = streaming;
+    out->block_threads = int32_t(block);
+    out->n_blocks = int32_t(nb);
+    out->tail_steps = int32_t(tail_steps);
+    out->tokens_per_group = int32_t(tpg);
+    out->column_groups = groups;
+    out->units = units;
+    out->product_blocks = product_blocks;
+    out->tail_blocks = tail_blocks;
+    out->cache_blocks = cache_blocks;
+    out->grid_blocks = grid;
+    out->bytes = bytes;
+    out->flops = 2 * T * H * 128 * 512;
+    out->stream_bytes_min = bytes_thr;
+    out->large_rows_min = large_min;
     return MLA_DQ_OK;
 }
 
@@ -235,41 +363,68 @@ int mla_decode_q_concat_kv_insert(void* q_out, const void* ql_nope, const void* 
     rc = mla_dq::plan(dims, flags, &p);
     if (rc != MLA_DQ_OK) return rc;
 
-    mla_dq::KernelArgs a;
-    a.q_out = static_cast<uint8_t*>(q_out);
-    a.ql_nope = static_cast<const uint16_t*>(ql_nope);
-    a.q_pe = static_cast<const uint16_t*>(q_pe);
-    a.kv_c = static_cast<const uint16_t*>(kv_c);
-    a.k_pe = static_cast<const uint16_t*>(k_pe);
-    a.cache = static_cast<uint8_t*>(cache);
-    a.slot_mapping = slot_mapping;
-    a.positions = positions;
-    a.rope_cos_sin = rope_cos_sin;
-    a.q_scale = q_scale;
-    a.kv_scale = kv_scale;
-    a.ql_nope_st = dims->ql_nope_stride_t;
-    a.ql_nope_sh = dims->ql_nope_stride_h;
-    a.q_pe_st = dims->q_pe_stride_t;
-    a.q_pe_sh = dims->q_pe_stride_h;
-    a.kv_c_st = dims->kv_c_stride_t;
-    a.k_pe_st = dims->k_pe_stride_t;
-    a.num_slots = dims->num_blocks * dims->block_size;
-    a.max_position = (flags & MLA_DQ_ROPE) ? dims->max_position : 1;
+    mla_dq::KernelArgs a = mla_dq::common_args(q_out, ql_nope, q_pe, kv_c, k_pe, cache, slot_mapping,
+                                               positions, rope_cos_sin, q_scale, kv_scale, flags, dims);
     a.row_stride = uint32_t(mla_dq::row_stride(dims->num_heads, flags));
     a.first_head = (flags & MLA_DQ_CACHE_ROWS_ONLY) ? uint32_t(dims->num_heads) : 0u;
     a.rows_per_token = make_fastdiv31(a.row_stride);
-    a.num_heads = uint32_t(dims->num_heads);
     a.total_rows = uint32_t(p.total_rows);
     a.tail_blocks = uint32_t(p.tail_blocks);
-    a.fp16 = (flags & MLA_DQ_FP16) ? 1u : 0u;
-    a.gptj = (flags & MLA_DQ_ROPE_GPTJ) ? 1u : 0u;
-    a.table_bf16 = (flags & MLA_DQ_TABLE_BF16) ? 1u : 0u;
     const hipError_t e = mla_dq::launch(a, p, flags, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
 }
 
 int mla_dq_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* plan) {
     return mla_dq::plan(dims, flags, plan);
+}
+
+int mla_decode_uk_q_concat_kv_insert(void* q_out, const void* q_nope, const void* w_uk_t,
+                                     const void* q_pe, const void* kv_c, const void* k_pe,
+                                     void* cache, const int64_t* slot_mapping,
+                                     const int64_t* positions, const float* rope_cos_sin,
+                                     const float* q_scale, const float* kv_scale, uint32_t flags,
+                                     const mla_dq_dims* dims, void* stream) {
+    int rc = mla_dq::uk_validate(q_out, q_nope, w_uk_t, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                                 rope_cos_sin, q_scale, kv_scale, flags, dims);
+    if (rc == mla_dq::kNothingToDo) return MLA_DQ_OK;
+    if (rc != MLA_DQ_OK) return rc;
+    mla_dq_uk_launch_plan p;
+    rc = mla_dq::uk_plan(dims, flags, &p);
+    if (rc != MLA_DQ_OK) return rc;
+
+    const int64_t T = dims->num_tokens, H = dims->num_heads;
+    mla_dq::UkArgs u;
+    u.tails = mla_dq::common_args(q_out, q_nope, q_pe, kv_c, k_pe, cache, slot_mapping, positions,
+                                  rope_cos_sin, q_scale, kv_scale, flags, dims);
+    u.tails.row_stride = uint32_t(H + 1);
+    u.tails.first_head = 0u;
+    u.tails.rows_per_token = make_fastdiv31(u.tails.row_stride);
+    u.tails.total_rows = uint32_t(T * (H + 1));
+    u.tails.tail_blocks = uint32_t(p.tail_blocks);
+    u.cache_rows = u.tails;
+    u.cache_rows.row_stride = 1u;
+    u.cache_rows.first_head = uint32_t(H);
+    u.cache_rows.rows_per_token = make_fastdiv31(1u);
+    u.cache_rows.total_rows = uint32_t(T);
+    u.cache_rows.tail_blocks = 0u;
+    u.q_nope = static_cast<const uint16_t*>(q_nope);
+    u.w_uk_t = static_cast<const uint16_t*>(w_uk_t);
+    u.q_nope_st = dims->ql_nope_stride_t;
+    u.q_nope_sh = dims->ql_nope_stride_h;
+    u.heads = make_fastdiv31(uint32_t(H));
+    u.num_tokens = uint32_t(T);
+    u.tokens_per_group = uint32_t(p.tokens_per_group);
+    u.units = uint32_t(p.units);
+    u.column_groups = uint32_t(p.column_groups);
+    u.product_blocks = uint32_t(p.product_blocks);
+    u.tail_blocks = uint32_t(p.tail_blocks);
+    u.cache_blocks = uint32_t(p.cache_blocks);
+    const hipError_t e = mla_dq::launch_uk(u, p, flags, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_DQ_OK : MLA_DQ_ERR_LAUNCH;
+}
+
+int mla_dq_uk_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_uk_launch_plan* plan) {
+    return mla_dq::uk_plan(dims, flags, plan);
 }
 
 #ifndef MLA_DQ_SOURCE_DIGEST

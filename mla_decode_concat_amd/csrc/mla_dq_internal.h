@@ -103,6 +103,37 @@
 #define MLA_DQ_LARGE_TABLE_LDS 1
 #endif
 
+// The epilogue fused into the W_UK product: workgroup size, 16-column
+// blocks of W_UK per wavefront and tokens per product workgroup of its two
+// configurations, and the query-row count T * H from which the throughput
+// configuration is the default.
+#ifndef MLA_DQ_UK_BLOCK
+#define MLA_DQ_UK_BLOCK 256
+#endif
+#ifndef MLA_DQ_UK_SMALL_NB
+#define MLA_DQ_UK_SMALL_NB 2
+#endif
+#ifndef MLA_DQ_UK_SMALL_TOKENS
+#define MLA_DQ_UK_SMALL_TOKENS 16
+#endif
+#ifndef MLA_DQ_UK_LARGE_NB
+#define MLA_DQ_UK_LARGE_NB 4
+#endif
+#ifndef MLA_DQ_UK_LARGE_TOKENS
+#define MLA_DQ_UK_LARGE_TOKENS 128
+#endif
+// The throughput configuration halves its tokens per product workgroup
+// (down to 16) while fewer than this many product workgroups would result.
+#ifndef MLA_DQ_UK_STREAM_PRODUCT_STORES
+#define MLA_DQ_UK_STREAM_PRODUCT_STORES 0
+#endif
+#ifndef MLA_DQ_UK_TARGET_BLOCKS
+#define MLA_DQ_UK_TARGET_BLOCKS 2048
+#endif
+#ifndef MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT
+#define MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT 4096
+#endif
+
 namespace mla_dq {
 
 // A mapping: threads per workgroup, latent rows handled by each wavefront
@@ -165,6 +196,30 @@ struct KernelArgs {
     uint32_t table_bf16;        // rope table holds bf16 (else fp32)
 };
 
+// The fused product.  Product workgroup g (g < product_blocks, a multiple of
+// 8) takes column group g / 8 % column_groups of unit 8 * (g / 8 /
+// column_groups) + g % 8 (units past the last exit): workgroups are dealt to
+// the 8 XCDs round-robin, so the column groups of one unit, which read the
+// same q_nope rows, run on one XCD one after another and share its L2.
+// Unit u is head u % H, token range u / H.
+struct UkArgs {
+    KernelArgs tails;          // every row's tail (row_stride H + 1)
+    KernelArgs cache_rows;     // the cache rows' latent parts (row_stride 1, first_head H)
+    const uint16_t* q_nope;
+    const uint16_t* w_uk_t;
+    int64_t q_nope_st, q_nope_sh;
+    FastDiv31 heads;           // divides a unit index by H
+    uint32_t num_tokens;
+    uint32_t tokens_per_group;
+    uint32_t units;
+    uint32_t column_groups;
+    uint32_t product_blocks;
+    uint32_t tail_blocks;
+    uint32_t cache_blocks;
+};
+
+constexpr int64_t kDefaultUkLargeRowsMin = MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT;
+
 // Host-side validation and planning (pure host code, no HIP calls).
 int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_c,
              const void* k_pe, void* cache, const int64_t* slot_mapping,
@@ -172,10 +227,17 @@ int validate(void* q_out, const void* ql_nope, const void* q_pe, const void* kv_
              const float* kv_scale, uint32_t flags, const mla_dq_dims* dims);
 int plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_launch_plan* out);
 int64_t row_stride(int64_t H, uint32_t flags);
+int uk_validate(void* q_out, const void* q_nope, const void* w_uk_t, const void* q_pe,
+                const void* kv_c, const void* k_pe, void* cache, const int64_t* slot_mapping,
+                const int64_t* positions, const float* rope_cos_sin, const float* q_scale,
+                const float* kv_scale, uint32_t flags, const mla_dq_dims* dims);
+int uk_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_uk_launch_plan* out);
 
 #if defined(__HIPCC__)
 hipError_t launch(const KernelArgs& a, const mla_dq_launch_plan& plan, uint32_t flags,
                   hipStream_t stream);
+hipError_t launch_uk(const UkArgs& u, const mla_dq_uk_launch_plan& plan, uint32_t flags,
+                     hipStream_t stream);
 #endif
 
 }  // namespace mla_dq

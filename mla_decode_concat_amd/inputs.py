@@ -127,6 +127,42 @@ def make_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
     q_pe = randn_act(T, H, PE)
     kv_c = randn_act(T, NOPE)
     k_pe = randn_act(T, PE)
+    out = dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe)
+    out.update(_slots_positions_cache(w, g))
+    return out
+
+
+UK_K = 128   # no-position width of a head's query before the W_UK product
+
+
+def make_uk_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
+    """CPU tensors for the epilogue fused into the W_UK product, drawn in a
+    fixed order from one generator: the q projection's output q_b
+    [T, H, 192] (N(0,1); q_nope is each head's first 128 columns, q_pe its
+    last 64, both views of q_b as in a decode step), W_UK transposed per head
+    w_uk_t [H, 512, 128] (N(0, 1/128), so that every latent column of the
+    product has unit variance like ql_nope in make_inputs), kv_c, k_pe, then
+    slots and positions as in make_inputs.  The cache starts as zeros."""
+    g = torch.Generator().manual_seed(seed)
+    T, H = w.tokens, w.heads
+
+    def randn_act(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=g, dtype=torch.float32) * scale).to(w.torch_dtype)
+
+    q_b = randn_act(T, H, UK_K + PE)
+    w_uk_t = randn_act(H, NOPE, UK_K, scale=UK_K ** -0.5)
+    kv_c = randn_act(T, NOPE)
+    k_pe = randn_act(T, PE)
+    out = dict(q_b=q_b, q_nope=q_b[..., :UK_K], q_pe=q_b[..., UK_K:], w_uk_t=w_uk_t, kv_c=kv_c,
+               k_pe=k_pe)
+    out.update(_slots_positions_cache(w, g))
+    return out
+
+
+def _slots_positions_cache(w: Workload, g: torch.Generator) -> dict:
+    """Slots, positions (in that order from g), the zero cache, the rope
+    table and the scales of a workload."""
+    T = w.tokens
     S = w.num_slots
     if w.slots == "randint":
         slots = torch.randint(0, S, (T,), generator=g, dtype=torch.int64)
@@ -152,11 +188,9 @@ def make_inputs(w: Workload, seed: int = DEFAULT_SEED) -> dict:
         table = shared_rope_table(w.max_position)
         if w.table_dtype == "bf16":
             table = table.to(torch.bfloat16)
-    out = dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
-               slot_mapping=slots, positions=positions, rope_cos_sin=table,
-               q_scale=torch.tensor([w.q_scale], dtype=torch.float32) if w.q_fp8 else None,
-               kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32) if w.kv_fp8 else None)
-    return out
+    return dict(cache=cache, slot_mapping=slots, positions=positions, rope_cos_sin=table,
+                q_scale=torch.tensor([w.q_scale], dtype=torch.float32) if w.q_fp8 else None,
+                kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32) if w.kv_fp8 else None)
 
 
 def custom(tokens: int, heads: int, num_blocks: int | None = None, block_size: int = 64,

@@ -29,7 +29,7 @@ def _declared_functions(header=HEADER):
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert set(names) == {"mla_decode_q_concat_kv_insert", "mla_dq_strerror", "mla_dq_plan",
-                          "mla_dq_source_digest"}
+                          "mla_dq_source_digest", "mla_decode_uk_q_concat_kv_insert", "mla_dq_uk_plan"}
     lib = ctypes.CDLL(B.library_path())
     for n in names:
         assert hasattr(lib, n), n
