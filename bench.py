@@ -201,7 +201,12 @@ class DecodeSlice:
     With ``fork`` the epilogue runs as two launches: the cache rows (which
     need only kv_c and k_pe) on a second stream right after the kv norm,
     beside the q_b and W_UK products, and the query rows after W_UK; the
-    main stream then waits for both."""
+    main stream then waits for both.
+
+    With ``fused`` the W_UK product and the epilogue are one launch
+    (mla_decode_uk_q_concat_kv_insert): it reads q_nope and q_pe as views of
+    the q_b output and W_UK transposed once ([H,512,128]); ql_nope is never
+    stored."""
 
     def __init__(self, T: int, H: int, dev: str, seed: int = 3):
         g = torch.Generator(device="cpu").manual_seed(seed)
@@ -213,6 +218,7 @@ class DecodeSlice:
         self.w_a = rnd(7168, 1536 + 576, scale=7168 ** -0.5)
         self.w_qb = rnd(1536, H * 192, scale=1536 ** -0.5)
         self.w_uk = rnd(H, 128, 512, scale=128 ** -0.5)
+        self.w_uk_t = self.w_uk.transpose(1, 2).contiguous()      # [H, 512, 128], done once
         self.g_q = rnd(1536, scale=0.1) + 1.0
         self.g_kv = rnd(512, scale=0.1) + 1.0
         w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
@@ -231,11 +237,21 @@ class DecodeSlice:
         kv_c = torch.nn.functional.rms_norm(qkv[:, 1536:2048], (512,), self.g_kv, 1e-6)
         return kv_c, qkv[:, 2048:]
 
-    def _q(self, qkv):
+    def _q_b(self, qkv):
         q_a = torch.nn.functional.rms_norm(qkv[:, :1536], (1536,), self.g_q, 1e-6)
-        q = (q_a @ self.w_qb).view(self.T, self.H, 192)
+        return (q_a @ self.w_qb).view(self.T, self.H, 192)
+
+    def _q(self, qkv):
+        q = self._q_b(qkv)
         ql = torch.bmm(q[..., :128].transpose(0, 1).contiguous(), self.w_uk)   # [H, T, 512]
         return ql.transpose(0, 1), q[..., 128:]
+
+    def fused_inputs(self):
+        """q_nope, q_pe (views of the q_b output), kv_c and k_pe."""
+        qkv = self.hidden @ self.w_a
+        kv_c, k_pe = self._kv(qkv)
+        q = self._q_b(qkv)
+        return q[..., :128], q[..., 128:], kv_c, k_pe
 
     def producers(self):
         qkv = self.hidden @ self.w_a
@@ -248,7 +264,15 @@ class DecodeSlice:
                                         self.slots, self.positions, self.table, self.q_scale,
                                         self.kv_scale, self.flags | extra)
 
-    def step(self, epilogue: bool = True, copies: bool = False, fork: bool = False):
+    def step(self, epilogue: bool = True, copies: bool = False, fork: bool = False,
+             fused: bool = False):
+        if fused:
+            q_nope, q_pe, kv_c, k_pe = self.fused_inputs()
+            if epilogue:
+                M.mla_decode_uk_q_concat_kv_insert(self.q_out, q_nope, self.w_uk_t, q_pe, kv_c, k_pe,
+                                                   self.cache, self.slots, self.positions, self.table,
+                                                   self.q_scale, self.kv_scale, self.flags)
+            return
         if fork:
             main = torch.cuda.current_stream()
             qkv = self.hidden @ self.w_a
@@ -298,8 +322,8 @@ class DecodeStep(DecodeSlice):
                                         max_seq_len=L)
 
     def step(self, epilogue: bool = True, copies: bool = False, attention: bool = True,
-             fork: bool = False):
-        super().step(epilogue, copies, fork)
+             fork: bool = False, fused: bool = False):
+        super().step(epilogue, copies, fork, fused)
         if (epilogue or fork) and attention:
             self.attn()
 
@@ -361,11 +385,17 @@ def decode_slice_timings(dev: str) -> dict:
                                   "small": forced(M.FORCE_SMALL_T),
                                   "mid": forced(M.FORCE_MID_T),
                                   "copies": lambda: ds.step(copies=True),
-                                  "forked": lambda: ds.step(fork=True)}, calls=20)
+                                  "forked": lambda: ds.step(fork=True),
+                                  "no_uk": lambda: ds.step(epilogue=False, fused=True),
+                                  "fused": lambda: ds.step(fused=True)}, calls=20)
         out[f"t{T}_h16"] = {"producers_us": round(r["base"], 3),
                             "with_epilogue_us": round(r["strided"], 3),
                             "with_copies_and_epilogue_us": round(r["copies"], 3),
                             "with_forked_epilogue_us": round(r["forked"], 3),
+                            "producers_before_w_uk_us": round(r["no_uk"], 3),
+                            "with_fused_w_uk_epilogue_us": round(r["fused"], 3),
+                            "w_uk_and_epilogue_separate_us": round(r["strided"] - r["no_uk"], 3),
+                            "w_uk_and_epilogue_fused_us": round(r["fused"] - r["no_uk"], 3),
                             "epilogue_increment_us": round(r["strided"] - r["base"], 3),
                             "epilogue_increment_small_t_us": round(r["small"] - r["base"], 3),
                             "epilogue_increment_mid_t_us": round(r["mid"] - r["base"], 3),
@@ -377,14 +407,74 @@ def decode_slice_timings(dev: str) -> dict:
         r = _alternating_medians({"base": lambda: st.step(epilogue=False),
                                   "epi": lambda: st.step(attention=False),
                                   "full": lambda: st.step(),
-                                  "forked": lambda: st.step(fork=True)}, calls=10)
+                                  "forked": lambda: st.step(fork=True),
+                                  "fused": lambda: st.step(fused=True)}, calls=10)
         out[f"b{B}_h16_l4096_with_attention"] = {
             "producers_us": round(r["base"], 3), "with_epilogue_us": round(r["epi"], 3),
             "with_epilogue_and_attention_us": round(r["full"], 3),
             "forked_with_attention_us": round(r["forked"], 3),
+            "fused_w_uk_epilogue_with_attention_us": round(r["fused"], 3),
             "attention_increment_us": round(r["full"] - r["epi"], 3)}
         log(f"decode step B={B} L=4096: {out[f'b{B}_h16_l4096_with_attention']}")
         del st
+    return out
+
+
+class UkSet:
+    """Device copies of one fused-product input set (make_uk_inputs) and
+    its prepared call: q_nope and q_pe as views of q_b, as in a step."""
+
+    def __init__(self, w: I.Workload, host: dict, dev: str):
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in host.items()
+             if k not in ("q_nope", "q_pe")}
+        self.d = d
+        qdt = torch.float8_e4m3fn if w.q_fp8 else w.torch_dtype
+        self.q_out = torch.empty(w.tokens, w.heads, 576, dtype=qdt, device=dev)
+        q_b = d["q_b"]
+        self.call = M.PreparedUkInsert(self.q_out, q_b[..., :128], d["w_uk_t"], q_b[..., 128:], d["kv_c"],
+                                       d["k_pe"], d["cache"], d["slot_mapping"], d["positions"],
+                                       d["rope_cos_sin"], d["q_scale"], d["kv_scale"], flags_of(w))
+
+
+def _rotating(fns: list):
+    """One call of the next of fns in turn (captured several times in a
+    graph, the calls walk through the sets)."""
+    i = [0]
+
+    def run():
+        fns[i[0] % len(fns)]()
+        i[0] += 1
+    return run
+
+
+def uk_timings(dev: str) -> dict:
+    """The epilogue fused into the W_UK product, alone, on each workload's
+    shapes and flags (inputs from make_uk_inputs): graph-replayed µs per
+    call on one buffer set (warm) and, for the two large shapes, on 4
+    rotating sets (cold), with GB/s against the call's algorithmic bytes
+    (q_nope and W_UK instead of ql_nope) and the product's TFLOP/s."""
+    out = {}
+    for name in LATENCY + MID + [HEADLINE]:
+        w = I.WORKLOADS[name]
+        host = I.make_uk_inputs(w)
+        nsets = 4 if name in MID + [HEADLINE] else 1
+        sets = [UkSet(w, host, dev) for _ in range(nsets)]
+        p = M.uk_plan(M._binding._dims(host["q_nope"], host["q_pe"], host["kv_c"], host["k_pe"],
+                                       host["cache"], host["rope_cos_sin"]), flags_of(w))
+        settle([s.call for s in sets], ms=20.0)
+        warm = time_graph_fn(sets[0].call, calls=20 if nsets == 1 else 8)
+        r = {"us_per_call_graph": round(warm, 3), "bytes": p.bytes,
+             "gbs_graph": round(p.bytes / warm / 1e3, 1),
+             "tflops_graph": round(p.flops / warm / 1e6, 2),
+             "configuration": "throughput" if p.mapping else "latency",
+             "streaming": bool(p.streaming), "grid_blocks": p.grid_blocks}
+        if nsets > 1:
+            cold = time_graph_fn(_rotating([s.call for s in sets]), calls=8)
+            r.update(us_per_call_graph_4_sets=round(cold, 3), gbs_graph_4_sets=round(p.bytes / cold / 1e3, 1))
+        out[name] = r
+        log(f"fused W_UK epilogue {name}: {r}")
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -600,16 +690,21 @@ def copy_reference(dev: str, moved_bytes: int, calls: int = 50) -> dict:
 
 
 # (name, tokens or sequences, cached tokens (None: the slice without the
-# attention), forked, extra epilogue flags, epilogue alone on the slice's views)
+# attention), step mode ("one": one epilogue launch after the W_UK product,
+# "forked": cache rows on a second stream, "fused": W_UK product and epilogue
+# in one launch), extra epilogue flags, epilogue alone on the slice's views)
 STEP_TRACE_CASES = [
-    ("slice_t64_h16", 64, None, False, 0, False),
-    ("slice_t64_h16_mid_t", 64, None, False, M.FORCE_MID_T, False),
-    ("slice_t64_h16_epilogue_alone", 64, None, False, 0, True),
-    ("slice_t64_h16_forked", 64, None, True, 0, False),
-    ("step_b64_h16_l4096", 64, 4096, False, 0, False),
-    ("step_b64_h16_l4096_forked", 64, 4096, True, 0, False),
-    ("step_b1_h16_l4096", 1, 4096, False, 0, False),
-    ("step_b1_h16_l4096_forked", 1, 4096, True, 0, False),
+    ("slice_t64_h16", 64, None, "one", 0, False),
+    ("slice_t64_h16_mid_t", 64, None, "one", M.FORCE_MID_T, False),
+    ("slice_t64_h16_epilogue_alone", 64, None, "one", 0, True),
+    ("slice_t64_h16_forked", 64, None, "forked", 0, False),
+    ("slice_t64_h16_fused", 64, None, "fused", 0, False),
+    ("step_b64_h16_l4096", 64, 4096, "one", 0, False),
+    ("step_b64_h16_l4096_forked", 64, 4096, "forked", 0, False),
+    ("step_b64_h16_l4096_fused", 64, 4096, "fused", 0, False),
+    ("step_b1_h16_l4096", 1, 4096, "one", 0, False),
+    ("step_b1_h16_l4096_forked", 1, 4096, "forked", 0, False),
+    ("step_b1_h16_l4096_fused", 1, 4096, "fused", 0, False),
 ]
 
 
@@ -619,14 +714,14 @@ def step_trace(dev: str, replays: int) -> None:
     and replays it `replays` times, draining the GPU and idling 200 µs
     between replays, so that in the trace every replay is a group of kernels
     set apart by idle time (see trace_summary)."""
-    for name, T, L, fork, extra, alone in STEP_TRACE_CASES:
+    for name, T, L, mode, extra, alone in STEP_TRACE_CASES:
         obj = DecodeSlice(T, 16, dev) if L is None else DecodeStep(T, 16, L, dev)
         obj.flags |= extra
         if alone:
             views = obj.producers()
             fn = lambda: obj._epilogue(*views)           # noqa: E731
         else:
-            fn = lambda: obj.step(fork=fork)              # noqa: E731
+            fn = lambda: obj.step(fork=mode == "forked", fused=mode == "fused")   # noqa: E731
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -648,7 +743,8 @@ def step_trace(dev: str, replays: int) -> None:
 def _short_kernel_name(name: str) -> str:
     if name.startswith("Cijk_") or "gemm" in name.lower():
         return "GEMM (hipBLASLt)"
-    for key in ("mla_dq_epilogue_kernel", "mla_attn_ring_kernel", "mla_attn_partial_kernel",
+    for key in ("mla_dq_epilogue_kernel", "mla_dq_uk_epilogue_kernel", "mla_attn_ring_kernel",
+                "mla_attn_partial_kernel",
                 "mla_attn_combine_wide_kernel", "mla_attn_combine_kernel"):
         if key in name:
             return key
@@ -690,7 +786,8 @@ def trace_summary(csv_path: str, idle_us: float = 100.0) -> str:
     # cases in the order they first ran; named after --step-trace's cases
     # when the trace holds exactly those
     kept = sorted(((sig, gs) for sig, gs in cases.items()
-                   if len(gs) >= 5 and any(k[0] == "mla_dq_epilogue_kernel" for k in sig)),
+                   if len(gs) >= 5 and any(k[0] in ("mla_dq_epilogue_kernel", "mla_dq_uk_epilogue_kernel")
+                                           for k in sig)),
                   key=lambda kv: float(np.median([g[0][0] for g in kv[1]])))
     names = [c[0] for c in STEP_TRACE_CASES] if len(kept) == len(STEP_TRACE_CASES) else [""] * len(kept)
     lines = []
@@ -731,6 +828,9 @@ def main() -> int:
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--only-attention", action="store_true",
                     help="time only the decode-attention workloads (prints their JSON)")
+    ap.add_argument("--no-uk", action="store_true")
+    ap.add_argument("--only-uk", action="store_true",
+                    help="time only the epilogue fused into the W_UK product (prints its JSON)")
     ap.add_argument("--only-decode-slice", action="store_true",
                     help="time only the decode-step slices in HIP graphs (prints their JSON)")
     ap.add_argument("--step-trace", type=int, default=0, metavar="REPLAYS",
@@ -777,6 +877,9 @@ def main() -> int:
         return 0
     if args.only_decode_slice:
         print(json.dumps({"decode_step_slice_graph": decode_slice_timings(dev)}), flush=True)
+        return 0
+    if args.only_uk:
+        print(json.dumps({"fused_w_uk_epilogue": uk_timings(dev)}), flush=True)
         return 0
     w = I.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.describe()}")
@@ -855,6 +958,7 @@ def main() -> int:
     ref_copy = copy_reference(dev, nbytes)
     log(f"reference copy: {ref_copy}")
     decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
+    fused_uk = {} if args.no_uk else uk_timings(dev)
     attention = {} if args.no_attention else attention_timings(
         dev, args.steps, 0.0 if args.no_cpu_baseline else 3.0)
 
@@ -885,6 +989,7 @@ def main() -> int:
         "latency_us": latency,
         "variants_at_headline_shape": variants,
         "decode_step_slice_graph": decode_slice,
+        "fused_w_uk_epilogue": fused_uk,
         "decode_attention": attention,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -122,16 +122,26 @@
 #ifndef MLA_DQ_UK_LARGE_TOKENS
 #define MLA_DQ_UK_LARGE_TOKENS 128
 #endif
-// The throughput configuration halves its tokens per product workgroup
-// (down to 16) while fewer than this many product workgroups would result.
+// 1 = the latency configuration's product stores also stream when the call
+// streams (they write partial lines, measured far slower that way).
 #ifndef MLA_DQ_UK_STREAM_PRODUCT_STORES
 #define MLA_DQ_UK_STREAM_PRODUCT_STORES 0
 #endif
+// The throughput configuration halves its tokens per product workgroup
+// (down to 16) while fewer than this many product workgroups would result:
+// one per CU.  Every product workgroup loads its columns of W_UK (64 KiB),
+// so shorter token ranges mostly add weight reads; measured against 2048 (and
+// 1024, 512, 128, 64): 1024 x 16 tokens 18.4 -> 8.7 us, 256 x 128 heads
+// 20.5 -> 13.3 us, 256 x 16 6.7 -> 5.1 us, 8192 x 16 unchanged.
 #ifndef MLA_DQ_UK_TARGET_BLOCKS
-#define MLA_DQ_UK_TARGET_BLOCKS 2048
+#define MLA_DQ_UK_TARGET_BLOCKS 256
 #endif
+// Measured crossover (graph replays, 16 and 128 heads): the latency
+// configuration wins up to 1024 query rows (64 x 16: 3.6 against 4.2 us;
+// 8 x 128 equal), the throughput one from 1152 (72 x 16: 4.2 against 4.6 us;
+// 10 x 128: 5.0 against 5.1 us).
 #ifndef MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT
-#define MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT 4096
+#define MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT 1088
 #endif
 
 namespace mla_dq {

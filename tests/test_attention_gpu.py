@@ -349,6 +349,7 @@ def test_decode_step_graph_epilogue_then_attention(fork):
     B, H, L = 6, 16, 333
     st = bench.DecodeStep(B, H, L, DEV)
     announce(f"decode step graph B={B} H={H} L={L} fork={fork}")
+    cache0 = st.cache.cpu().clone()       # the synthetic context, before any step writes to it
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -360,7 +361,7 @@ def test_decode_step_graph_epilogue_then_attention(fork):
     ew = I.custom(B, H, num_blocks=st.w.num_blocks, rope=True, q_fp8=True, kv_fp8=True)
     einp = dict(ql_nope=ql_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(),
                 kv_c=kv_c.cpu().contiguous(), k_pe=k_pe.cpu().contiguous(),
-                cache=st.cache.cpu(), slot_mapping=st.slots.cpu(), positions=st.positions.cpu(),
+                cache=cache0, slot_mapping=st.slots.cpu(), positions=st.positions.cpu(),
                 rope_cos_sin=st.table.cpu(), q_scale=st.q_scale.cpu(), kv_scale=st.kv_scale.cpu())
     want_q, want_cache = oracle_run(ew, einp)
     ainp = dict(q=torch.from_numpy(want_q).view(torch.float8_e4m3fn),

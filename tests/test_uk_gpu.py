@@ -298,3 +298,80 @@ def test_uk_graph_replays():
         torch.cuda.synchronize()
         assert_same(bits(q_out.cpu()), q_ref, "q (replay)")
         assert_same(bits(cache.cpu()), cache_ref, "cache (replay)")
+
+
+def _captured(fn):
+    """fn warmed up on a side stream, then captured in a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+@pytest.mark.parametrize("T,H", [(1, 16), (64, 16), (8, 128), (200, 16)])
+@pytest.mark.parametrize("force", ["plan", "small", "large"])
+def test_decode_slice_fused_in_a_graph(T, H, force):
+    """The decode-step slice with the W_UK product and the epilogue in one
+    launch: q_nope and q_pe are views of the q_b projection's [T,H,192]
+    output, k_pe a view of the fused-A output, all captured with the
+    producers in a HIP graph.  Every replay meets the bar above against the
+    oracle on the materialised inputs."""
+    announce(f"fused decode slice in a graph T={T} H={H} configuration={force}")
+    import bench
+    ds = bench.DecodeSlice(T, H, DEV)
+    ds.flags |= {"plan": 0, "small": M.FORCE_SMALL_T, "large": M.FORCE_LARGE_T}[force]
+    g = _captured(lambda: ds.step(fused=True))
+    q_nope, q_pe, kv_c, k_pe = ds.fused_inputs()
+    torch.cuda.synchronize()
+    assert q_nope.stride() == (H * 192, 192, 1) and q_pe.stride() == (H * 192, 192, 1)
+    assert k_pe.stride() == (2112, 1)
+    w = I.custom(T, H, num_blocks=max(1, (T + 63) // 64), rope=True, q_fp8=True, kv_fp8=True)
+    inp = I.make_inputs(w)
+    inp.update(q_nope=q_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(), kv_c=kv_c.cpu().contiguous(),
+               k_pe=k_pe.cpu().contiguous(), w_uk_t=ds.w_uk_t.cpu())
+    for _ in range(3):
+        ds.q_out.view(torch.uint8).fill_(0xFF)
+        ds.cache.view(torch.uint8).fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_all(w, inp, bits(ds.q_out.cpu()), bits(ds.cache.cpu()))
+
+
+def test_decode_step_fused_then_attention_in_a_graph():
+    """A decode step with the fused W_UK product + epilogue followed by the
+    decode attention, captured in one graph: every replay's queries and cache
+    meet the bar above against the oracle, and its attention output is
+    bit-identical to an eager attention call on those same queries and cache
+    (the attention itself is checked against its oracle elsewhere)."""
+    import bench
+    B, H, L = 6, 16, 333
+    st = bench.DecodeStep(B, H, L, DEV)
+    announce(f"fused decode step graph B={B} H={H} L={L}")
+    cache0 = st.cache.cpu().clone()       # the synthetic context, before any step writes to it
+    g = _captured(lambda: st.step(fused=True))
+    q_nope, q_pe, kv_c, k_pe = st.fused_inputs()
+    torch.cuda.synchronize()
+    w = I.custom(B, H, num_blocks=st.w.num_blocks, rope=True, q_fp8=True, kv_fp8=True)
+    inp = dict(q_nope=q_nope.cpu().contiguous(), q_pe=q_pe.cpu().contiguous(), kv_c=kv_c.cpu().contiguous(),
+               k_pe=k_pe.cpu().contiguous(), w_uk_t=st.w_uk_t.cpu(), cache=cache0,
+               slot_mapping=st.slots.cpu(), positions=st.positions.cpu(), rope_cos_sin=st.table.cpu(),
+               q_scale=st.q_scale.cpu(), kv_scale=st.kv_scale.cpu())
+    for _ in range(3):
+        st.out.view(torch.int16).fill_(-1)
+        st.q_out.view(torch.uint8).fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_all(w, inp, bits(st.q_out.cpu()), bits(st.cache.cpu()))
+        out_graph = st.out.clone()
+        st.out.view(torch.int16).fill_(-1)
+        st.attn()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out.view(torch.int16), out_graph.view(torch.int16))

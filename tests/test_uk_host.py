@@ -140,14 +140,14 @@ def test_plan_counts_and_coverage(T, H, flags):
     assert p.n_blocks == (4 if p.mapping else 2) and p.tail_steps == (2 if p.mapping else 1)
     assert p.column_groups * waves * 16 * p.n_blocks == 512
     # tokens per product workgroup: 16 for the latency configuration; for the
-    # throughput one the largest of 128, 64, 32 that keeps >= 2048 product
+    # throughput one the largest of 128, 64, 32 that keeps >= 256 product
     # workgroups, else 16
     if p.mapping == 0:
         assert p.tokens_per_group == 16
     else:
         want = 16
         for tpg in (128, 64, 32):
-            if H * math.ceil(T / tpg) * p.column_groups >= 2048:
+            if H * math.ceil(T / tpg) * p.column_groups >= 256:
                 want = tpg
                 break
         assert p.tokens_per_group == want
@@ -181,3 +181,15 @@ def test_plan_overrides():
     assert M.uk_plan(d, M.ROPE | M.KV_FP8).streaming == 1
     assert M.uk_plan(d, M.ROPE | M.KV_FP8 | M.FORCE_CACHED).streaming == 0
     assert M.uk_plan(d, M.FORCE_SMALL_T).mapping == 0
+
+
+def test_plan_default_thresholds():
+    """Without the environment overrides: the throughput configuration from
+    1088 query rows, streaming from the epilogue's 192 MiB."""
+    if any(v in os.environ for v in ("MLA_DQ_UK_LARGE_ROWS_MIN", "MLA_DQ_STREAM_BYTES_MIN")):
+        pytest.skip("threshold overridden in the environment")
+    for T, H, want in [(64, 16, 0), (67, 16, 0), (68, 16, 1), (72, 16, 1), (8, 128, 0), (9, 128, 1)]:
+        p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE | M.Q_FP8 | M.KV_FP8)
+        assert p.large_rows_min == 1088 and p.mapping == want
+    p = M.uk_plan(_dims(T=2048, H=16, NB=33, maxpos=32768), M.ROPE)
+    assert p.stream_bytes_min == 192 << 20 and p.streaming == 0
