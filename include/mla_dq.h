@@ -253,12 +253,13 @@ int mla_decode_uk_q_concat_kv_insert(void* q_out, const void* q_nope, const void
  * per 16 x 16 x 32 tile); then the positional tails of all T * (H + 1) rows;
  * then the latent parts of the T cache rows.  The latency configuration
  * (fewest query rows) takes 16 tokens per product workgroup and narrow
- * column groups, so that even one token spreads over many workgroups; the
+ * column groups (n_blocks 2, or 1 when there are at most 32 (head, token
+ * range) units), so that even one token spreads over many workgroups; the
  * throughput configuration takes wider groups and longer token ranges (up to
  * 128 tokens, shortened while fewer than about 256 product workgroups would
  * result), so that each q_nope row and each weight row is read fewer times.
  * The throughput configuration is the default from T * H >= large_rows_min
- * (1088, or the environment variable MLA_DQ_UK_LARGE_ROWS_MIN read once);
+ * (1025, or the environment variable MLA_DQ_UK_LARGE_ROWS_MIN read once);
  * the call streams (non-temporal stores) from stream_bytes_min bytes, the
  * epilogue's threshold (MLA_DQ_STREAM_BYTES_MIN). */
 typedef struct mla_dq_uk_launch_plan {

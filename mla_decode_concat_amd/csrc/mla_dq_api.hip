@@ -313,11 +313,16 @@ int uk_plan(const mla_dq_dims* d, uint32_t flags, mla_dq_uk_launch_plan* out) {
     if (flags & MLA_DQ_FORCE_STREAM) streaming = 1;
     if (flags & MLA_DQ_FORCE_CACHED) streaming = 0;
     const int64_t block = MLA_DQ_UK_BLOCK, waves = block / 64;
-    const int64_t nb = mapping ? MLA_DQ_UK_LARGE_NB : MLA_DQ_UK_SMALL_NB;
     const int64_t tail_steps = mapping ? kLargeMapping.tail_steps : 1;
-    const int64_t groups = 512 / (waves * 16 * nb);
+    int64_t nb = mapping ? MLA_DQ_UK_LARGE_NB : MLA_DQ_UK_SMALL_NB;
+    int64_t groups = 512 / (waves * 16 * nb);
     int64_t tpg = mapping ? MLA_DQ_UK_LARGE_TOKENS : MLA_DQ_UK_SMALL_TOKENS;
-    while (tpg > 16 && H * ((T + tpg - 1) / tpg) * groups < MLA_DQ_UK_TARGET_BLOCKS) tpg /= 2;
+    const int64_t target = mapping ? MLA_DQ_UK_TARGET_BLOCKS : MLA_DQ_UK_SMALL_TARGET_BLOCKS;
+    while (tpg > 16 && H * ((T + tpg - 1) / tpg) * groups < target) tpg /= 2;
+    if (!mapping && H * ((T + tpg - 1) / tpg) <= MLA_DQ_UK_SMALL_NB1_UNITS_MAX) {
+        nb = 1;
+        groups = 512 / (waves * 16);
+    }
     const int64_t units = H * ((T + tpg - 1) / tpg);
     const int64_t product_blocks = 8 * groups * ((units + 7) / 8);
     const int64_t tails_per_block = (block / 8) * tail_steps;

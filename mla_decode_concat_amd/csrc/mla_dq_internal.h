@@ -113,6 +113,14 @@
 #ifndef MLA_DQ_UK_SMALL_NB
 #define MLA_DQ_UK_SMALL_NB 2
 #endif
+// The latency configuration takes one 16-column block per wavefront instead
+// (twice the product workgroups, each loading half the weight columns) while
+// it has at most this many (head, token range) units: measured at 16 heads,
+// 1 / 16 / 32 tokens 3.05 -> 2.55, 3.44 -> 2.95, 3.49 -> 3.15 us; at 48
+// tokens (48 units) 3.51 -> 3.83, and at 128 heads slower from one token.
+#ifndef MLA_DQ_UK_SMALL_NB1_UNITS_MAX
+#define MLA_DQ_UK_SMALL_NB1_UNITS_MAX 32
+#endif
 #ifndef MLA_DQ_UK_SMALL_TOKENS
 #define MLA_DQ_UK_SMALL_TOKENS 16
 #endif
@@ -136,12 +144,17 @@
 #ifndef MLA_DQ_UK_TARGET_BLOCKS
 #define MLA_DQ_UK_TARGET_BLOCKS 256
 #endif
+// The same for the latency configuration.
+#ifndef MLA_DQ_UK_SMALL_TARGET_BLOCKS
+#define MLA_DQ_UK_SMALL_TARGET_BLOCKS 256
+#endif
 // Measured crossover (graph replays, 16 and 128 heads): the latency
 // configuration wins up to 1024 query rows (64 x 16: 3.6 against 4.2 us;
-// 8 x 128 equal), the throughput one from 1152 (72 x 16: 4.2 against 4.6 us;
-// 10 x 128: 5.0 against 5.1 us).
+// 8 x 128 equal), the throughput one past them (65 x 16: 4.2 against 4.5
+// us, a fifth 16-token range per head then costing the latency one more
+// than one product workgroup per CU; 72 x 16: 4.2 against 4.6 us).
 #ifndef MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT
-#define MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT 1088
+#define MLA_DQ_UK_LARGE_ROWS_MIN_DEFAULT 1025
 #endif
 
 namespace mla_dq {

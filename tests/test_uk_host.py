@@ -137,7 +137,11 @@ def test_plan_counts_and_coverage(T, H, flags):
     assert p.block_threads == 256
     waves = p.block_threads // 64
     assert p.mapping == (1 if T * H >= p.large_rows_min else 0)
-    assert p.n_blocks == (4 if p.mapping else 2) and p.tail_steps == (2 if p.mapping else 1)
+    if p.mapping:
+        assert p.n_blocks == 4
+    else:   # one 16-column block per wavefront for at most 32 (head, 16-token range) units
+        assert p.n_blocks == (1 if H * math.ceil(T / 16) <= 32 else 2)
+    assert p.tail_steps == (2 if p.mapping else 1)
     assert p.column_groups * waves * 16 * p.n_blocks == 512
     # tokens per product workgroup: 16 for the latency configuration; for the
     # throughput one the largest of 128, 64, 32 that keeps >= 256 product
@@ -185,11 +189,15 @@ def test_plan_overrides():
 
 def test_plan_default_thresholds():
     """Without the environment overrides: the throughput configuration from
-    1088 query rows, streaming from the epilogue's 192 MiB."""
+    1025 query rows, one 16-column block per wavefront in the latency one
+    for at most 32 units, streaming from the epilogue's 192 MiB."""
     if any(v in os.environ for v in ("MLA_DQ_UK_LARGE_ROWS_MIN", "MLA_DQ_STREAM_BYTES_MIN")):
         pytest.skip("threshold overridden in the environment")
-    for T, H, want in [(64, 16, 0), (67, 16, 0), (68, 16, 1), (72, 16, 1), (8, 128, 0), (9, 128, 1)]:
+    for T, H, want in [(64, 16, 0), (65, 16, 1), (72, 16, 1), (8, 128, 0), (9, 128, 1), (1024, 1, 0), (1025, 1, 1)]:
         p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE | M.Q_FP8 | M.KV_FP8)
-        assert p.large_rows_min == 1088 and p.mapping == want
+        assert p.large_rows_min == 1025 and p.mapping == want
+    for T, H, nb in [(1, 16, 1), (32, 16, 1), (33, 16, 2), (64, 16, 2), (1, 32, 1), (1, 33, 2), (1, 128, 2)]:
+        p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE)
+        assert p.mapping == 0 and p.n_blocks == nb and p.column_groups == 512 // (4 * 16 * nb)
     p = M.uk_plan(_dims(T=2048, H=16, NB=33, maxpos=32768), M.ROPE)
     assert p.stream_bytes_min == 192 << 20 and p.streaming == 0
