@@ -40,7 +40,8 @@ VARIANTS = {"fp16": dict(dtype="fp16"), "gptj": dict(rope_style="gptj"),
             "fp16_gptj_table_bf16": dict(dtype="fp16", rope_style="gptj", table_dtype="bf16")}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", f)
-                  for f in ("mla_dq_kernel.hip", "mla_dq_api.hip", "mla_dq_internal.h", "fastdiv.h")]
+                  for f in ("mla_dq_kernel.hip", "mla_dq_rows.h", "mla_dq_api.hip", "mla_dq_internal.h",
+                            "fastdiv.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_dq_epilogue_t8192_h16_traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "mla_decode_concat_amd", "csrc", "mla_attn.hip"),
                 os.path.join(ROOT, "include", "mla_attn.h")]
