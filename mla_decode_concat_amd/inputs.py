@@ -292,24 +292,34 @@ def attn_custom(batch: int, heads: int, seq_lens, block_size: int = 64, q_fp8: b
 
 
 def make_inputs_on_device(w: Workload, device: str, seed: int = DEFAULT_SEED,
-                          chunk: int = 1 << 27) -> dict:
+                          chunk: int = 1 << 27, uk: bool = False) -> dict:
     """The same recipe as make_inputs, drawn on the device by torch's device
     generator (for sizes whose host copy would be impractical; the values
     differ from make_inputs' for the same seed).  Activations are N(0,1)
     fp32 rounded to the activation type, drawn ``chunk`` elements at a time;
     slots are a prefix of a random permutation of all cache slots; positions
-    follow the workload's recipe.  The cache starts as zeros."""
+    follow the workload's recipe.  The cache starts as zeros.  With ``uk``
+    the recipe is make_uk_inputs' instead: q_b [T, H, 192] (q_nope and q_pe
+    its views) and w_uk_t [H, 512, 128] with N(0, 1/128) entries in place of
+    ql_nope and q_pe."""
     g = torch.Generator(device=device).manual_seed(seed)
     T, H = w.tokens, w.heads
 
-    def randn_act(*shape):
+    def randn_act(*shape, scale=1.0):
         out = torch.empty(*shape, dtype=w.torch_dtype, device=device)
         for part in out.view(-1).split(chunk):
-            part.copy_(torch.randn(part.numel(), generator=g, dtype=torch.float32, device=device))
+            part.copy_(torch.randn(part.numel(), generator=g, dtype=torch.float32, device=device) * scale)
         return out
 
-    ql_nope = randn_act(T, H, NOPE)
-    q_pe = randn_act(T, H, PE)
+    extra = {}
+    if uk:
+        q_b = randn_act(T, H, UK_K + PE)
+        w_uk_t = randn_act(H, NOPE, UK_K, scale=UK_K ** -0.5)
+        extra = dict(q_b=q_b, q_nope=q_b[..., :UK_K], w_uk_t=w_uk_t)
+        ql_nope, q_pe = None, q_b[..., UK_K:]
+    else:
+        ql_nope = randn_act(T, H, NOPE)
+        q_pe = randn_act(T, H, PE)
     kv_c = randn_act(T, NOPE)
     k_pe = randn_act(T, PE)
     S = w.num_slots
@@ -333,7 +343,11 @@ def make_inputs_on_device(w: Workload, device: str, seed: int = DEFAULT_SEED,
         if w.table_dtype == "bf16":
             table = table.to(torch.bfloat16)
         table = table.to(device)
-    return dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
-                slot_mapping=slots, positions=positions, rope_cos_sin=table,
-                q_scale=torch.tensor([w.q_scale], dtype=torch.float32, device=device) if w.q_fp8 else None,
-                kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32, device=device) if w.kv_fp8 else None)
+    out = dict(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe, cache=cache,
+               slot_mapping=slots, positions=positions, rope_cos_sin=table,
+               q_scale=torch.tensor([w.q_scale], dtype=torch.float32, device=device) if w.q_fp8 else None,
+               kv_scale=torch.tensor([w.kv_scale], dtype=torch.float32, device=device) if w.kv_fp8 else None)
+    if uk:
+        del out["ql_nope"]
+        out.update(extra)
+    return out

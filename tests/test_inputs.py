@@ -51,3 +51,31 @@ def test_device_recipe_on_the_cpu_device(rope):
     assert all(torch.equal(a[k], b[k]) for k in ("ql_nope", "q_pe", "kv_c", "k_pe", "slot_mapping"))
     c = I.make_inputs_on_device(w, "cpu", seed=6, chunk=1000)
     assert not torch.equal(a["ql_nope"], c["ql_nope"])
+
+
+def _check_uk_recipe(w: I.Workload, d: dict):
+    T, H = w.tokens, w.heads
+    assert d["q_b"].shape == (T, H, 192) and d["q_b"].dtype == w.torch_dtype
+    assert d["q_nope"].data_ptr() == d["q_b"].data_ptr() and d["q_nope"].shape == (T, H, 128)
+    assert d["q_pe"].data_ptr() == d["q_b"].data_ptr() + 128 * d["q_b"].element_size()
+    assert d["q_nope"].stride() == (H * 192, 192, 1) and d["q_pe"].stride() == (H * 192, 192, 1)
+    assert d["w_uk_t"].shape == (H, 512, 128) and d["w_uk_t"].dtype == w.torch_dtype
+    wt = d["w_uk_t"].float()
+    assert abs(float(wt.std()) * 128 ** 0.5 - 1.0) < 0.05      # N(0, 1/128)
+    x = d["q_b"].float()
+    assert abs(float(x.mean())) < 0.05 and abs(float(x.std()) - 1.0) < 0.05
+    assert "ql_nope" not in d
+    rest = dict(d, ql_nope=torch.zeros(T, H, 512, dtype=w.torch_dtype))
+    rest["ql_nope"].normal_()
+    _check_recipe(w, rest)
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_uk_recipes_host_and_device(rope):
+    w = I.custom(200, 16, rope=rope, q_fp8=True, kv_fp8=True)
+    h = I.make_uk_inputs(w, seed=5)
+    _check_uk_recipe(w, {k: v for k, v in h.items() if k != "ql_nope"})
+    a = I.make_inputs_on_device(w, "cpu", seed=5, chunk=1000, uk=True)
+    b = I.make_inputs_on_device(w, "cpu", seed=5, chunk=1000, uk=True)
+    _check_uk_recipe(w, a)
+    assert all(torch.equal(a[k], b[k]) for k in ("q_b", "w_uk_t", "kv_c", "k_pe", "slot_mapping"))

@@ -267,6 +267,62 @@ def test_uk_full_size(T, H, mode):
     check_latent(q[sample, :, :I.NOPE], bits(inp["q_nope"])[sample], bits(inp["w_uk_t"]), w)
 
 
+def test_uk_maximum_token_count_sampled():
+    """The largest token count the C ABI accepts at 16 heads (as for the
+    epilogue: T * (H + 1) * 72 chunks just below 2^31; one token more is
+    refused), in the throughput configuration with streaming stores: about
+    31 GB of device buffers drawn on the device.  Tails, cache rows and the
+    latent columns of both ends, of the first and last tokens of token ranges
+    and of a random sample of tokens are checked against the oracle, and the
+    untouched cache rows are still zero."""
+    H = 16
+    T = (2 ** 31 - 1) // (72 * (H + 1))
+    w = workload(T, H, True, True, True)
+    flags = flags_of(w)
+    d = M.Dims(num_tokens=T, num_heads=H, num_blocks=w.num_blocks, block_size=w.block_size,
+               max_position=w.max_position, ql_nope_stride_t=H * 192, ql_nope_stride_h=192,
+               q_pe_stride_t=H * 192, q_pe_stride_h=192, kv_c_stride_t=512, k_pe_stride_t=64)
+    p = M.uk_plan(d, flags)
+    assert p.mapping == 1 and p.streaming == 1 and p.grid_blocks * p.block_threads < 2 ** 32
+    d.num_tokens = T + 1
+    with pytest.raises(M.MlaDqError):
+        M.uk_plan(d, flags)
+    if torch.cuda.mem_get_info()[0] < 40 * (1 << 30):
+        pytest.skip("needs about 35 GB of free device memory")
+    announce(f"uk maximum size T={T} H={H}: drawing inputs on the device")
+    dev = I.make_inputs_on_device(w, DEV, seed=37, uk=True)
+    q = torch.empty(T, H, I.ROW, dtype=torch.float8_e4m3fn, device=DEV)
+    announce(f"uk maximum size T={T} H={H}: kernel ({p.grid_blocks} workgroups, {p.tokens_per_group} tokens per range)")
+    M.mla_decode_uk_q_concat_kv_insert(q, dev["q_nope"], dev["w_uk_t"], dev["q_pe"], dev["kv_c"], dev["k_pe"],
+                                       dev["cache"], dev["slot_mapping"], dev["positions"], dev["rope_cos_sin"],
+                                       dev["q_scale"], dev["kv_scale"], flags)
+    torch.cuda.synchronize()
+    tpg = p.tokens_per_group
+    gen = torch.Generator().manual_seed(41)
+    idx = torch.cat([torch.arange(64), torch.arange(T - 64, T), torch.arange(0, T, tpg * 997),
+                     torch.arange(tpg - 1, T, tpg * 1009), torch.randperm(T, generator=gen)[:1024]])
+    idx = torch.unique(idx)
+    n = idx.numel()
+    di = idx.to(DEV)
+    slots = dev["slot_mapping"][di]
+    want_q = np.zeros((n, H, I.ROW), dtype=np.uint8)
+    want_rows = np.zeros((n, 1, I.ROW), dtype=np.uint8)
+    oracle.insert(want_q, np.zeros((n, H, I.NOPE), dtype=np.uint16), bits(dev["q_pe"][di]), bits(dev["kv_c"][di]),
+                  bits(dev["k_pe"][di]), want_rows, np.arange(n, dtype=np.int64),
+                  dev["positions"][di].cpu().numpy(), dev["rope_cos_sin"].cpu().numpy(),
+                  w.q_scale, w.kv_scale, True, True, True)
+    got = bits(q[di])
+    assert_same(got[..., I.NOPE:], want_q[..., I.NOPE:], "q tails (sampled tokens)")
+    rows = dev["cache"].view(-1, I.ROW)
+    assert_same(bits(rows[slots]), want_rows.reshape(n, I.ROW), "cache rows (sampled tokens)")
+    written = torch.zeros(rows.shape[0], dtype=torch.bool, device=DEV)
+    written[dev["slot_mapping"]] = True
+    assert int(rows[~written].view(torch.uint8).count_nonzero()) == 0
+    check_latent(got[..., :I.NOPE], bits(dev["q_nope"][di]), bits(dev["w_uk_t"]), w, "q latent (sampled tokens)")
+    del dev, q, rows, written
+    torch.cuda.empty_cache()
+
+
 def test_uk_graph_replays():
     """The fused call captured in a HIP graph: every replay (with eager work
     and a synchronisation between replays) gives the eager call's bytes."""
