@@ -267,6 +267,54 @@ def test_uk_full_size(T, H, mode):
     check_latent(q[sample, :, :I.NOPE], bits(inp["q_nope"])[sample], bits(inp["w_uk_t"]), w)
 
 
+ALL_LAUNCHES = [("plan", 0), ("small_cached", M.FORCE_SMALL_T | M.FORCE_CACHED),
+                ("small_stream", M.FORCE_SMALL_T | M.FORCE_STREAM),
+                ("large_cached", M.FORCE_LARGE_T | M.FORCE_CACHED),
+                ("large_stream", M.FORCE_LARGE_T | M.FORCE_STREAM)]
+
+
+@pytest.mark.parametrize("T,H,mode", [(1, 16, (True, True, True)), (33, 16, (True, True, True)),
+                                      (65, 16, (True, False, True)), (300, 5, (True, True, False)),
+                                      (97, 128, (False, True, True))],
+                         ids=["t1_h16", "t33_h16", "t65_h16", "t300_h5", "t97_h128"])
+def test_uk_every_launch_gives_the_same_bytes(T, H, mode):
+    """Every configuration sums each latent column's 128 products in the same
+    order (four 32-wide steps of k, in turn), so the latency configuration
+    (one or two 16-column blocks per wavefront, operands from memory) and the
+    throughput one (four blocks, operands staged in LDS), cached or
+    streamed, write identical bytes; the default plan's result also meets
+    the bar against the oracle."""
+    w = workload(T, H, *mode)
+    inp = I.make_uk_inputs(w)
+    results = {}
+    for name, extra in ALL_LAUNCHES:
+        results[name] = run_uk(w, inp, extra, case=f"launch {name}")
+    q0, c0 = results["plan"]
+    check_all(w, inp, q0, c0)
+    for name, (q, c) in results.items():
+        assert np.array_equal(q, q0), f"q_out of launch {name} differs from the plan's"
+        assert np.array_equal(c, c0), f"cache of launch {name} differs from the plan's"
+
+
+def test_uk_non_default_stream():
+    """The call goes on torch's current stream: launched on a side stream and
+    synchronised with that stream alone, it has finished and meets the bar."""
+    w = workload(64, 16, True, True, True)
+    inp = I.make_uk_inputs(w)
+    announce("uk non-default stream")
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q_out = torch.empty(64, 16, I.ROW, dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        M.mla_decode_uk_q_concat_kv_insert(q_out, dev["q_b"][..., :I.UK_K], dev["w_uk_t"], dev["q_b"][..., I.UK_K:],
+                                           dev["kv_c"], dev["k_pe"], dev["cache"], dev["slot_mapping"],
+                                           dev["positions"], dev["rope_cos_sin"], dev["q_scale"], dev["kv_scale"],
+                                           flags_of(w))
+    s.synchronize()
+    check_all(w, inp, bits(q_out.cpu()), bits(dev["cache"].cpu()))
+
+
 def test_uk_maximum_token_count_sampled():
     """The largest token count the C ABI accepts at 16 heads (as for the
     epilogue: T * (H + 1) * 72 chunks just below 2^31; one token more is
