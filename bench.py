@@ -448,12 +448,53 @@ def _rotating(fns: list):
     return run
 
 
-def uk_timings(dev: str) -> dict:
+def uk_cpu_oracle(w: I.Workload, host: dict, seconds: float) -> dict:
+    """The oracle as it stands for the fused call on the first tokens of the
+    workload (as many 64-token chunks as fit in about `seconds`), scaled to
+    the whole call: the exact product (fp64), its encoding into q codes, and
+    the epilogue oracle for the tails and the cache rows, on all host
+    threads."""
+    import numpy as np
+    import oracle
+
+    def bits(t):
+        t = t.contiguous()
+        return (t.view(torch.int16).numpy().view(np.uint16) if t.dtype in (torch.bfloat16, torch.float16)
+                else t.view(torch.uint8).numpy())
+    T, H = w.tokens, w.heads
+    q_nope, q_pe = bits(host["q_nope"]), bits(host["q_pe"])
+    kv_c, k_pe, w_uk = bits(host["kv_c"]), bits(host["k_pe"]), bits(host["w_uk_t"])
+    cache = bits(host["cache"]).copy()
+    slots = host["slot_mapping"].numpy()
+    pos = host["positions"].numpy() if host["positions"] is not None else None
+    table = host["rope_cos_sin"].numpy() if host["rope_cos_sin"] is not None else None
+    done, t0 = 0, time.perf_counter()
+    while done < T and time.perf_counter() - t0 < seconds:
+        t1 = min(T, done + 64)
+        x = oracle.uk_product(q_nope[done:t1], w_uk).astype(np.float32)
+        if w.q_fp8:
+            q = np.zeros((t1 - done, H, 576), dtype=np.uint8)
+            lat = oracle.quant_e4m3_array(x, w.q_scale).reshape(x.shape)
+        else:
+            q = np.zeros((t1 - done, H, 576), dtype=np.uint16)
+            lat = oracle.f32_to_bf16_array(x).reshape(x.shape)
+        oracle.insert(q, np.zeros((t1 - done, H, 512), dtype=np.uint16), q_pe[done:t1], kv_c[done:t1],
+                      k_pe[done:t1], cache, slots[done:t1], None if pos is None else pos[done:t1], table,
+                      w.q_scale, w.kv_scale, w.rope, w.q_fp8, w.kv_fp8)
+        q[..., :512] = lat
+        done = t1
+    el = time.perf_counter() - t0
+    return {"us_per_call": round(el / done * T * 1e6, 1), "sample": f"{done} of {T} tokens",
+            "kind": "oracle", "cores": oracle.num_threads()}
+
+
+def uk_timings(dev: str, cpu_seconds: float = 0.0) -> dict:
     """The epilogue fused into the W_UK product, alone, on each workload's
     shapes and flags (inputs from make_uk_inputs): graph-replayed µs per
     call on one buffer set (warm) and, for the two large shapes, on 4
     rotating sets (cold), with GB/s against the call's algorithmic bytes
-    (q_nope and W_UK instead of ql_nope) and the product's TFLOP/s."""
+    (q_nope and W_UK instead of ql_nope) and the product's TFLOP/s; with
+    ``cpu_seconds`` the oracle timed beside it on the 8192-token shape."""
     out = {}
     for name in LATENCY + MID + [HEADLINE]:
         w = I.WORKLOADS[name]
@@ -472,6 +513,8 @@ def uk_timings(dev: str) -> dict:
         if nsets > 1:
             cold = time_graph_fn(_rotating([s.call for s in sets]), calls=8)
             r.update(us_per_call_graph_4_sets=round(cold, 3), gbs_graph_4_sets=round(p.bytes / cold / 1e3, 1))
+        if cpu_seconds > 0 and name == HEADLINE:
+            r["cpu_oracle"] = uk_cpu_oracle(w, host, cpu_seconds)
         out[name] = r
         log(f"fused W_UK epilogue {name}: {r}")
         del sets
@@ -880,7 +923,8 @@ def main() -> int:
         print(json.dumps({"decode_step_slice_graph": decode_slice_timings(dev)}), flush=True)
         return 0
     if args.only_uk:
-        print(json.dumps({"fused_w_uk_epilogue": uk_timings(dev)}), flush=True)
+        print(json.dumps({"fused_w_uk_epilogue": uk_timings(dev, 0.0 if args.no_cpu_baseline else 3.0)}),
+              flush=True)
         return 0
     w = I.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.describe()}")
@@ -959,7 +1003,7 @@ def main() -> int:
     ref_copy = copy_reference(dev, nbytes)
     log(f"reference copy: {ref_copy}")
     decode_slice = {} if args.no_decode_slice else decode_slice_timings(dev)
-    fused_uk = {} if args.no_uk else uk_timings(dev)
+    fused_uk = {} if args.no_uk else uk_timings(dev, 0.0 if args.no_cpu_baseline else 3.0)
     attention = {} if args.no_attention else attention_timings(
         dev, args.steps, 0.0 if args.no_cpu_baseline else 3.0)
 
