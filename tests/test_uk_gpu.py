@@ -201,11 +201,16 @@ def test_uk_contiguous_inputs(T, H):
     check_all(w, inp, q, cache)
 
 
-def test_uk_junk_slots_positions_and_background():
+@pytest.mark.parametrize("T,H", [(70, 16), (40, 3), (200, 1)], ids=["t70_h16", "t40_h3", "t200_h1"])
+@pytest.mark.parametrize("name,extra", [("plan", 0), ("small", M.FORCE_SMALL_T), ("large", M.FORCE_LARGE_T),
+                                        ("large_stream", M.FORCE_LARGE_T | M.FORCE_STREAM)],
+                         ids=["plan", "small", "large", "large_stream"])
+def test_uk_junk_slots_positions_and_background(T, H, name, extra):
     """Padding slots (-1), slots past the cache, positions outside the table
-    and a random cache background: skipped rows keep their bytes."""
-    T, H = 70, 16
-    w = workload(T, H, True, True, True, num_blocks=3)
+    and a random cache background, under both configurations (the
+    throughput one stages the table rows of its tail workgroups, clamped, in
+    LDS): skipped rows keep their bytes."""
+    w = workload(T, H, True, True, True, num_blocks=(T + 63) // 64 + 2)
     inp = I.make_uk_inputs(w)
     slots = inp["slot_mapping"].clone()
     slots[::7] = -1
@@ -219,7 +224,7 @@ def test_uk_junk_slots_positions_and_background():
     rng = np.random.default_rng(5)
     cache_init = rng.integers(0, 256, size=(w.num_blocks, w.block_size, I.ROW), dtype=np.uint8)
     cache_init[(cache_init & 0x7F) == 0x7F] = 0    # no NaN codes in the background
-    q, cache = run_uk(w, inp, cache_init=cache_init, case="junk")
+    q, cache = run_uk(w, inp, extra, cache_init=cache_init, case=f"junk {name}")
     check_all(w, inp, q, cache, cache_init=cache_init)
 
 
