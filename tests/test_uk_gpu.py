@@ -228,6 +228,45 @@ def test_uk_junk_slots_positions_and_background(T, H, name, extra):
     check_all(w, inp, q, cache, cache_init=cache_init)
 
 
+@pytest.mark.parametrize("T,H", [(3, 2), (120, 3)], ids=["t3_h2", "t120_h3"])
+@pytest.mark.parametrize("name,extra", [("small", M.FORCE_SMALL_T), ("large", M.FORCE_LARGE_T),
+                                        ("large_stream", M.FORCE_LARGE_T | M.FORCE_STREAM)],
+                         ids=["small", "large", "large_stream"])
+def test_uk_duplicate_slots_leave_one_candidate(T, H, name, extra):
+    """Tokens that share a slot: every 8-element chunk of that cache row comes
+    from one of them (the header's contract); q_out and the rows of unique
+    slots meet the bar, under both configurations."""
+    w = workload(T, H, True, True, True, num_blocks=(T + 63) // 64 + 1, kv_scale=0.3)
+    inp = I.make_uk_inputs(w, seed=2 + T)
+    slots = inp["slot_mapping"].numpy().copy()
+    groups = [[0, 1]] if T == 3 else [[0, 1, 2], [5, 60], [33, 119, 64, 90]]
+    for g in groups:
+        slots[g] = slots[g[0]]
+    inp["slot_mapping"] = torch.from_numpy(slots)
+    q, cache = run_uk(w, inp, extra, case=f"duplicate slots {name}")
+    want_q, want_cache = expected_rest(w, inp)
+    assert_same(q[..., I.NOPE:], want_q[..., I.NOPE:], "q tails")
+    check_latent(q[..., :I.NOPE], bits(inp["q_nope"]), bits(inp["w_uk_t"]), w)
+    rows, want_rows = cache.reshape(-1, I.ROW), want_cache.reshape(-1, I.ROW)
+    shared = {int(slots[g[0]]): g for g in groups}
+    keep = np.ones(rows.shape[0], dtype=bool)
+    keep[list(shared)] = False
+    assert_same(rows[keep], want_rows[keep], "cache rows of unique slots and untouched rows")
+    w1 = workload(1, H, True, True, True, num_blocks=1, kv_scale=0.3)
+    for s_, g in shared.items():
+        cands = []
+        for t in g:       # the row token t alone would write
+            sub = dict(inp, slot_mapping=torch.tensor([0], dtype=torch.int64),
+                       cache=torch.zeros(1, 64, I.ROW, dtype=torch.float8_e4m3fn),
+                       ql_nope=torch.zeros(1, H, I.NOPE, dtype=w.torch_dtype))
+            for k in ("q_pe", "kv_c", "k_pe", "positions"):
+                sub[k] = inp[k][t:t + 1].clone()
+            cands.append(oracle_run(w1, sub)[1].reshape(-1, I.ROW)[0].reshape(72, 8))
+        got = rows[s_].reshape(72, 8)
+        for c in range(72):
+            assert any(np.array_equal(got[c], cand[c]) for cand in cands), (s_, c)
+
+
 def test_uk_e4m3_saturation():
     """A small q_scale drives most latent values past 448: they saturate."""
     w = workload(33, 16, True, True, True, q_scale=0.002)
