@@ -255,9 +255,10 @@ int mla_decode_uk_q_concat_kv_insert(void* q_out, const void* q_nope, const void
  * (fewest query rows) takes 16 tokens per product workgroup and narrow
  * column groups (n_blocks 2, or 1 when there are at most 32 (head, token
  * range) units), so that even one token spreads over many workgroups; the
- * throughput configuration takes wider groups and longer token ranges (up to
- * 128 tokens, shortened while fewer than about 256 product workgroups would
- * result), so that each q_nope row and each weight row is read fewer times.
+ * throughput configuration takes wider groups (n_blocks 4, or 2 with at
+ * least 64 tokens and at most 16384 query rows) and longer token ranges (up to 128 tokens, shortened while
+ * fewer than about 256 product workgroups would result), so that each q_nope
+ * row and each weight row is read fewer times.
  * The throughput configuration is the default from T * H >= large_rows_min
  * (1025, or the environment variable MLA_DQ_UK_LARGE_ROWS_MIN read once);
  * the call streams (non-temporal stores) from stream_bytes_min bytes, the

@@ -315,6 +315,7 @@ int uk_plan(const mla_dq_dims* d, uint32_t flags, mla_dq_uk_launch_plan* out) {
     const int64_t block = MLA_DQ_UK_BLOCK, waves = block / 64;
     const int64_t tail_steps = mapping ? kLargeMapping.tail_steps : 1;
     int64_t nb = mapping ? MLA_DQ_UK_LARGE_NB : MLA_DQ_UK_SMALL_NB;
+    if (mapping && T * H <= MLA_DQ_UK_LARGE_NB2_ROWS_MAX && T >= MLA_DQ_UK_LARGE_NB2_TOKENS_MIN) nb = 2;
     int64_t groups = 512 / (waves * 16 * nb);
     int64_t tpg = mapping ? MLA_DQ_UK_LARGE_TOKENS : MLA_DQ_UK_SMALL_TOKENS;
     const int64_t target = mapping ? MLA_DQ_UK_TARGET_BLOCKS : MLA_DQ_UK_SMALL_TARGET_BLOCKS;

@@ -130,6 +130,22 @@
 #ifndef MLA_DQ_UK_LARGE_TOKENS
 #define MLA_DQ_UK_LARGE_TOKENS 128
 #endif
+// The throughput configuration takes two 16-column blocks per wavefront
+// instead of MLA_DQ_UK_LARGE_NB up to this many query rows T * H, from this
+// many tokens: twice the column groups, so that each product workgroup
+// loops over half the columns of its tokens.  With fewer tokens per head the
+// extra workgroups only add weight loads.  Measured (graph replays, E4M3 q):
+// 65 / 128 / 192 / 1024 tokens x 16 heads 4.19 -> 4.06, 4.75 -> 4.00,
+// 6.08 -> 4.64, 8.64 -> 8.27 us; 64 / 128 tokens x 128 heads 6.44 -> 6.37,
+// 9.05 -> 8.82 us; slower at 9-48 tokens x 128 heads (5.17 -> 5.26 at 9,
+// 5.92 -> 6.06 at 48) and from 32768 rows (2048 x 16: 12.96 -> 13.37 us,
+// 256 x 128: 12.88 -> 13.43 us).
+#ifndef MLA_DQ_UK_LARGE_NB2_ROWS_MAX
+#define MLA_DQ_UK_LARGE_NB2_ROWS_MAX 16384
+#endif
+#ifndef MLA_DQ_UK_LARGE_NB2_TOKENS_MIN
+#define MLA_DQ_UK_LARGE_NB2_TOKENS_MIN 64
+#endif
 // 1 = the latency configuration's product stores also stream when the call
 // streams (they write partial lines, measured far slower that way).
 #ifndef MLA_DQ_UK_STREAM_PRODUCT_STORES

@@ -342,8 +342,10 @@ hipError_t uk_flags(const UkArgs& u, uint32_t grid, uint32_t flags, hipStream_t 
 template <bool STREAM, bool VAR>
 hipError_t uk_config(const UkArgs& u, const mla_dq_uk_launch_plan& p, uint32_t flags, hipStream_t stream) {
     const uint32_t grid = uint32_t(p.grid_blocks);
-    if (p.mapping == 1)
+    if (p.mapping == 1) {
+        if (p.n_blocks == 2) return uk_flags<2, kLargeMapping.tail_steps, true, STREAM, VAR>(u, grid, flags, stream);
         return uk_flags<MLA_DQ_UK_LARGE_NB, kLargeMapping.tail_steps, true, STREAM, VAR>(u, grid, flags, stream);
+    }
     if (p.n_blocks == 1) return uk_flags<1, 1, false, STREAM, VAR>(u, grid, flags, stream);
     return uk_flags<MLA_DQ_UK_SMALL_NB, 1, false, STREAM, VAR>(u, grid, flags, stream);
 }

@@ -319,13 +319,13 @@ ALL_LAUNCHES = [("plan", 0), ("small_cached", M.FORCE_SMALL_T | M.FORCE_CACHED),
 
 @pytest.mark.parametrize("T,H,mode", [(1, 16, (True, True, True)), (33, 16, (True, True, True)),
                                       (65, 16, (True, False, True)), (300, 5, (True, True, False)),
-                                      (97, 128, (False, True, True))],
-                         ids=["t1_h16", "t33_h16", "t65_h16", "t300_h5", "t97_h128"])
+                                      (97, 128, (False, True, True)), (1100, 16, (True, True, True))],
+                         ids=["t1_h16", "t33_h16", "t65_h16", "t300_h5", "t97_h128", "t1100_h16"])
 def test_uk_every_launch_gives_the_same_bytes(T, H, mode):
     """Every configuration sums each latent column's 128 products in the same
     order (four 32-wide steps of k, in turn), so the latency configuration
     (one or two 16-column blocks per wavefront, operands from memory) and the
-    throughput one (four blocks, operands staged in LDS), cached or
+    throughput one (two or four blocks, operands staged in LDS), cached or
     streamed, write identical bytes; the default plan's result also meets
     the bar against the oracle."""
     w = workload(T, H, *mode)

@@ -137,8 +137,8 @@ def test_plan_counts_and_coverage(T, H, flags):
     assert p.block_threads == 256
     waves = p.block_threads // 64
     assert p.mapping == (1 if T * H >= p.large_rows_min else 0)
-    if p.mapping:
-        assert p.n_blocks == 4
+    if p.mapping:   # two 16-column blocks per wavefront from 64 tokens up to 16384 query rows
+        assert p.n_blocks == (2 if T * H <= 16384 and T >= 64 else 4)
     else:   # one 16-column block per wavefront for at most 32 (head, 16-token range) units
         assert p.n_blocks == (1 if H * math.ceil(T / 16) <= 32 else 2)
     assert p.tail_steps == (2 if p.mapping else 1)
@@ -196,6 +196,10 @@ def test_plan_default_thresholds():
     for T, H, want in [(64, 16, 0), (65, 16, 1), (72, 16, 1), (8, 128, 0), (9, 128, 1), (1024, 1, 0), (1025, 1, 1)]:
         p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE | M.Q_FP8 | M.KV_FP8)
         assert p.large_rows_min == 1025 and p.mapping == want
+    for T, H, nb in [(1024, 16, 2), (1025, 16, 4), (128, 128, 2), (129, 128, 4), (64, 128, 2), (63, 128, 4),
+                     (65, 16, 2)]:
+        p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE)
+        assert p.mapping == 1 and p.n_blocks == nb and p.column_groups == 512 // (4 * 16 * nb)
     for T, H, nb in [(1, 16, 1), (32, 16, 1), (33, 16, 2), (64, 16, 2), (1, 32, 1), (1, 33, 2), (1, 128, 2)]:
         p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE)
         assert p.mapping == 0 and p.n_blocks == nb and p.column_groups == 512 // (4 * 16 * nb)
