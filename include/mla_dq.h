@@ -281,6 +281,11 @@ typedef struct mla_dq_uk_launch_plan {
     int64_t stream_bytes_min; /* byte threshold in force                         */
     int64_t large_rows_min;   /* T * H from which the throughput configuration
                                  is the default                                  */
+    int32_t head_major;       /* 1 = each XCD takes a contiguous block of
+                                 (head, token range) units, all ranges of a
+                                 head together (from 64 heads); 0 = unit u on
+                                 XCD u % 8, ranges outermost                     */
+    int32_t reserved;
 } mla_dq_uk_launch_plan;
 
 int mla_dq_uk_plan(const mla_dq_dims* dims, uint32_t flags, mla_dq_uk_launch_plan* plan);

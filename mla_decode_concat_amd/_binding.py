@@ -66,7 +66,8 @@ class UkLaunchPlan(ctypes.Structure):
                 ("tail_steps", ctypes.c_int32), ("tokens_per_group", ctypes.c_int32)] + [
         (n, ctypes.c_int64) for n in (
             "column_groups", "units", "product_blocks", "tail_blocks", "cache_blocks", "grid_blocks",
-            "bytes", "flops", "stream_bytes_min", "large_rows_min")]
+            "bytes", "flops", "stream_bytes_min", "large_rows_min")] + [
+        ("head_major", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MlaDqError(RuntimeError):

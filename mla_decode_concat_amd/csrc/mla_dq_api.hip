@@ -325,7 +325,7 @@ int uk_plan(const mla_dq_dims* d, uint32_t flags, mla_dq_uk_launch_plan* out) {
         groups = 512 / (waves * 16);
     }
     const int64_t units = H * ((T + tpg - 1) / tpg);
-    const int64_t product_blocks = 8 * groups * ((units + 7) / 8);
+    const int64_t product_blocks = 8 * groups * ((units + 7) / 8);   // 8 XCDs x ceil(units / 8) units
     const int64_t tails_per_block = (block / 8) * tail_steps;
     const int64_t tail_blocks = (T * (H + 1) + tails_per_block - 1) / tails_per_block;
     const int64_t cache_blocks = (T + waves - 1) / waves;
@@ -338,6 +338,8 @@ int uk_plan(const mla_dq_dims* d, uint32_t flags, mla_dq_uk_launch_plan* out) {
     out->n_blocks = int32_t(nb);
     out->tail_steps = int32_t(tail_steps);
     out->tokens_per_group = int32_t(tpg);
+    out->head_major = H >= MLA_DQ_UK_HEAD_MAJOR_HEADS_MIN ? 1 : 0;
+    out->reserved = 0;
     out->column_groups = groups;
     out->units = units;
     out->product_blocks = product_blocks;
@@ -418,6 +420,9 @@ int mla_decode_uk_q_concat_kv_insert(void* q_out, const void* q_nope, const void
     u.q_nope_st = dims->ql_nope_stride_t;
     u.q_nope_sh = dims->ql_nope_stride_h;
     u.heads = make_fastdiv31(uint32_t(H));
+    u.ranges = make_fastdiv31(uint32_t((T + p.tokens_per_group - 1) / p.tokens_per_group));
+    u.units_per_xcd = uint32_t((p.units + 7) / 8);
+    u.head_major = p.head_major;
     u.num_tokens = uint32_t(T);
     u.tokens_per_group = uint32_t(p.tokens_per_group);
     u.units = uint32_t(p.units);

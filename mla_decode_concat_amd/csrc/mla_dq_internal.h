@@ -157,6 +157,14 @@
 // so shorter token ranges mostly add weight reads; measured against 2048 (and
 // 1024, 512, 128, 64): 1024 x 16 tokens 18.4 -> 8.7 us, 256 x 128 heads
 // 20.5 -> 13.3 us, 256 x 16 6.7 -> 5.1 us, 8192 x 16 unchanged.
+// Order of the product units from this many heads on: head-major, each
+// XCD taking a contiguous block of ceil(units / 8) units (all token ranges
+// of its heads back to back, so that their W_UK columns stay in its L2);
+// below it range-major, unit u dealt to XCD u % 8 (the XCDs then work on the
+// same token range at once, which keeps their q_nope reads close together).
+#ifndef MLA_DQ_UK_HEAD_MAJOR_HEADS_MIN
+#define MLA_DQ_UK_HEAD_MAJOR_HEADS_MIN 64
+#endif
 #ifndef MLA_DQ_UK_TARGET_BLOCKS
 #define MLA_DQ_UK_TARGET_BLOCKS 256
 #endif
@@ -236,11 +244,13 @@ struct KernelArgs {
 };
 
 // The fused product.  Product workgroup g (g < product_blocks, a multiple of
-// 8) takes column group g / 8 % column_groups of unit 8 * (g / 8 /
-// column_groups) + g % 8 (units past the last exit): workgroups are dealt to
-// the 8 XCDs round-robin, so the column groups of one unit, which read the
-// same q_nope rows, run on one XCD one after another and share its L2.
-// Unit u is head u % H, token range u / H.
+// 8) takes column group g / 8 % column_groups of a unit of XCD g % 8:
+// workgroups are dealt to the 8 XCDs round-robin, so the column groups of one
+// unit, which read the same q_nope rows, run on one XCD one after another and
+// share its L2.  With head_major the unit is (g % 8) * units_per_xcd +
+// g / 8 / column_groups, head unit / ranges and token range unit % ranges;
+// otherwise it is 8 * (g / 8 / column_groups) + g % 8, head unit % H and
+// token range unit / H.  Units past the last exit.
 struct UkArgs {
     KernelArgs tails;          // every row's tail (row_stride H + 1)
     KernelArgs cache_rows;     // the cache rows' latent parts (row_stride 1, first_head H)
@@ -248,9 +258,12 @@ struct UkArgs {
     const uint16_t* w_uk_t;
     int64_t q_nope_st, q_nope_sh;
     FastDiv31 heads;           // divides a unit index by H
+    FastDiv31 ranges;          // divides a unit index by the token ranges per head
     uint32_t num_tokens;
     uint32_t tokens_per_group;
     uint32_t units;
+    uint32_t units_per_xcd;    // ceil(units / 8)
+    uint32_t head_major;       // 1 = head-major unit order (see above)
     uint32_t column_groups;
     uint32_t product_blocks;
     uint32_t tail_blocks;

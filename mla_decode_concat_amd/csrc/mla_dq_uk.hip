@@ -20,12 +20,16 @@
 //    loaded during this step's products), four products over k = 0..127
 //    per 16-column block.  The result leaves lane l with token l % 16 and the
 //    four consecutive columns 16b + 4(l / 16) .. +3, which it encodes and
-//    stores (8 bytes bf16/fp16, 4 bytes E4M3).  Workgroup g takes column
-//    group g / 8 % column_groups of unit 8 (g / 8 / column_groups) + g % 8:
-//    workgroups are dealt to the eight XCDs round-robin, so the column groups
-//    that read the same q_nope rows run back to back on one XCD and find
-//    them in its L2, and each XCD sees only the heads congruent to its index
-//    modulo 8 (W_UK rows stay in its L2 across token ranges).
+//    stores (8 bytes bf16/fp16, 4 bytes E4M3).  Workgroups are dealt to the
+//    eight XCDs round-robin; workgroup g takes column group g / 8 %
+//    column_groups of its XCD's (g % 8) next unit, so the column groups that
+//    read the same q_nope rows run back to back on one XCD and find them in
+//    its L2.  From 64 heads each XCD takes a contiguous block of units in
+//    head-major order (all token ranges of a head together: its W_UK
+//    columns stay in that L2); with fewer heads unit 8 (g / 8 /
+//    column_groups) + g % 8, ranges outermost, so that the XCDs read nearby
+//    q_nope rows at the same time and each sees only the heads congruent to
+//    its index modulo 8.
 //  * tail workgroups: the positional tails of all T * (H + 1) rows, and
 //  * cache workgroups: the latent parts of the T cache rows,
 //    both done by the epilogue's own row workers (mla_dq_rows.h).
@@ -115,11 +119,20 @@ __device__ __forceinline__ void product_tile(const UkArgs& u, uint32_t g, uint8_
 
     const uint32_t xcd = g % 8u, m = g / 8u;
     const uint32_t group = m % u.column_groups;
-    const uint32_t unit = 8u * (m / u.column_groups) + xcd;
-    if (unit >= u.units) return;                          // whole workgroup: no barrier is skipped
     const uint32_t H = u.tails.num_heads;
-    const uint32_t range = fastdiv31(unit, u.heads);
-    const uint32_t h = unit - range * H;
+    uint32_t h, range;
+    if (u.head_major) {
+        const uint32_t pos = m / u.column_groups;        // place in this XCD's block of units
+        const uint32_t unit = xcd * u.units_per_xcd + pos;
+        if (pos >= u.units_per_xcd || unit >= u.units) return;   // whole workgroup: no barrier is skipped
+        h = fastdiv31(unit, u.ranges);
+        range = unit - h * u.ranges.div;
+    } else {
+        const uint32_t unit = 8u * (m / u.column_groups) + xcd;
+        if (unit >= u.units) return;                      // whole workgroup: no barrier is skipped
+        range = fastdiv31(unit, u.heads);
+        h = unit - range * H;
+    }
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t c = lane % 16u, kq = lane / 16u;

@@ -130,7 +130,7 @@ def _algorithmic_bytes(T, H, flags):
 
 
 @pytest.mark.parametrize("T,H", [(1, 16), (5, 3), (64, 16), (255, 16), (256, 16), (256, 128), (1000, 5),
-                                 (8192, 16), (4096, 1), (16384, 128)])
+                                 (8192, 16), (4096, 1), (16384, 128), (300, 64), (37, 100), (9, 128)])
 @pytest.mark.parametrize("flags", [0, M.ROPE | M.KV_FP8, M.ROPE | M.Q_FP8, M.ROPE | M.TABLE_BF16 | M.Q_FP8 | M.KV_FP8])
 def test_plan_counts_and_coverage(T, H, flags):
     p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), flags)
@@ -163,17 +163,32 @@ def test_plan_counts_and_coverage(T, H, flags):
     assert p.bytes == _algorithmic_bytes(T, H, flags)
     assert p.flops == 2 * T * H * 128 * 512
     assert p.streaming == (1 if p.bytes >= p.stream_bytes_min else 0)
-    # the documented workgroup -> (column group, unit) mapping reaches every
-    # (unit, group) pair exactly once; the other workgroups exit
+    # the documented workgroup -> (head, token range, column group) mapping
+    # reaches every triple exactly once; the other workgroups exit.  From 64
+    # heads each XCD takes a contiguous block of head-major units, else unit
+    # u = range * H + head goes to XCD u % 8.
+    ranges = math.ceil(T / p.tokens_per_group)
+    assert p.head_major == (1 if H >= 64 else 0)
+    per_xcd = math.ceil(p.units / 8)
     seen = set()
     for g in range(p.product_blocks):
         xcd, m = g % 8, g // 8
-        unit = 8 * (m // p.column_groups) + xcd
-        if unit < p.units:
-            pair = (unit, m % p.column_groups)
-            assert pair not in seen
-            seen.add(pair)
-    assert len(seen) == p.units * p.column_groups
+        group = m % p.column_groups
+        if p.head_major:
+            pos = m // p.column_groups
+            unit = xcd * per_xcd + pos
+            if pos >= per_xcd or unit >= p.units:
+                continue
+            h, r = divmod(unit, ranges)
+        else:
+            unit = 8 * (m // p.column_groups) + xcd
+            if unit >= p.units:
+                continue
+            r, h = divmod(unit, H)
+        assert 0 <= h < H and 0 <= r < ranges
+        assert (h, r, group) not in seen
+        seen.add((h, r, group))
+    assert len(seen) == p.units * p.column_groups == H * ranges * p.column_groups
 
 
 def test_plan_overrides():
