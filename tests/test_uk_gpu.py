@@ -26,7 +26,7 @@ import mla_decode_concat_amd as M
 from mla_decode_concat_amd import inputs as I
 import oracle
 from tests._util import bits, oracle_run
-from tests.test_gpu_parity import GUARD_ROWS, announce, assert_same, flags_of
+from tests.test_gpu_parity import GUARD_ROWS, _background, _out_of_range, announce, assert_same, flags_of
 
 pytestmark = pytest.mark.gpu
 
@@ -265,6 +265,46 @@ def test_uk_duplicate_slots_leave_one_candidate(T, H, name, extra):
         got = rows[s_].reshape(72, 8)
         for c in range(72):
             assert any(np.array_equal(got[c], cand[c]) for cand in cands), (s_, c)
+
+
+def _random_uk_case(i: int):
+    """Seeded random shape and mode of the fused call: tokens, heads, block
+    size, precision of each output, activation type, rotation style and table
+    type, launch override, q_nope strided or contiguous, share of padding and
+    out-of-range slots and positions, and a random cache background."""
+    rng = np.random.default_rng(2000 + i)
+    H = int(rng.choice([1, 2, 3, 5, 7, 8, 15, 16, 17, 31, 64, 65, 128]))
+    T = int(rng.integers(1, max(2, min(2000, 24000 // H))))
+    bs = int(rng.choice([1, 16, 64, 128]))
+    rope, qf, kf = bool(rng.integers(2)), bool(rng.integers(2)), bool(rng.integers(2))
+    dtype = "fp16" if rng.integers(4) == 0 else "bf16"
+    style = "gptj" if rope and rng.integers(3) == 0 else "neox"
+    table = "bf16" if rope and rng.integers(3) == 0 else "f32"
+    nb = (T + bs - 1) // bs + int(rng.integers(0, 3))
+    force = [0, M.FORCE_SMALL_T, M.FORCE_LARGE_T, M.FORCE_SMALL_T | M.FORCE_STREAM,
+             M.FORCE_LARGE_T | M.FORCE_STREAM, M.FORCE_LARGE_T | M.FORCE_CACHED][int(rng.integers(6))]
+    w = workload(T, H, rope, qf, kf, num_blocks=nb, block_size=bs,
+                 q_scale=float(rng.choice([0.05, 0.3, 1.0])), kv_scale=float(rng.choice([0.05, 2.0])),
+                 dtype=dtype, rope_style=style, table_dtype=table,
+                 max_position=int(rng.choice([1, 77, 4096])))
+    junk = float(rng.choice([0.0, 0.0, 0.1, 0.5]))
+    return w, force, int(rng.integers(1 << 30)), junk, bool(rng.integers(2)), bool(rng.integers(2))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_uk_seeded_random_shapes_and_modes(i):
+    """Random shapes, heads, block sizes, flag and variant combinations and
+    launch overrides of the fused call, some with padding or out-of-range
+    slots and positions over a random cache background, each against the
+    oracle to the bar above."""
+    w, force, seed, junk, contiguous, background = _random_uk_case(i)
+    inp = I.make_uk_inputs(w, seed=seed)
+    if junk:
+        inp = _out_of_range(inp, w, seed=seed + 1, frac=junk)
+    cache_init = _background(w, seed + 2) if background else None
+    q, cache = run_uk(w, inp, force, cache_init=cache_init, contiguous=contiguous,
+                      case=f"random case {i} (seed {seed}, junk {junk})")
+    check_all(w, inp, q, cache, cache_init=cache_init)
 
 
 def test_uk_e4m3_saturation():
