@@ -130,8 +130,10 @@ typedef struct mla_attn_plan {
     int64_t workspace_bytes;    /* = mla_decode_attention_workspace_size()         */
     int64_t target_workgroups;  /* policy: 256, or MLA_ATTN_TARGET_WGS if set      */
     int32_t xcd_remap;          /* 1 = head tiles of one key range share an XCD   */
-    int32_t block_threads;      /* 256 (bf16 cache: four wavefronts) or 512 (E4M3
-                                   cache: four compute + four loader wavefronts) */
+    int32_t block_threads;      /* 256 (bf16 cache, or E4M3 cache with 64-key
+                                   ranges: four wavefronts) or 512 (E4M3 cache,
+                                   longer ranges: four compute + four loader
+                                   wavefronts)                                  */
 } mla_attn_plan;
 
 int mla_decode_attention_plan(const mla_attn_dims* dims, uint32_t flags, mla_attn_plan* plan);

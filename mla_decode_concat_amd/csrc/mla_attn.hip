@@ -67,6 +67,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRow = 576;           // latent row: 512 value + 64 positional elements
 constexpr int kValue = 512;
@@ -624,6 +625,73 @@ __device__ __forceinline__ bf16x4 e4m3x4_to_bf16(uint32_t word) {
     return bf16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// One 16-key E4M3 tile in LDS (the ring slot layout: block i of 1 KB holds
+// at 16 l the 16 bytes of key l % 16 at row bytes 64 i + 16 (l / 16))
+// through one compute wavefront's scores, online softmax and value product.
+// The tile holds keys first + 64 t .. +15; keys from k1 on weigh zero.
+__device__ __forceinline__ void e4m3_tile(const uint8_t* base, const __bf16* qrow, int lane, int g, int vlane,
+                                          float sc, int first, int t, int k1, f32x4 (&o)[kDimTiles], float& m,
+                                          float& lsum) {
+    // All of the tile's LDS reads go out first (keys for the scores,
+    // transposed values for the value product), so their latency
+    // overlaps instead of stalling each product in turn.
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    u32x4 kraw[kSteps / 2];
+    i32x2 vraw[kDimTiles / 2];
+#pragma unroll
+    for (int i = 0; i < kSteps / 2; ++i)
+        kraw[i] = *reinterpret_cast<const u32x4*>(base + 1024 * i + 16 * lane);
+#pragma unroll
+    for (int dd = 0; dd < kDimTiles / 2; ++dd)
+        vraw[dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + vlane + 512 * dd));
+    __builtin_amdgcn_sched_barrier(0);
+    // scores: S^T = K Q^T over 18 steps of 32 dims
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kSteps / 2; ++i) {
+        const u32x4 raw = kraw[i];
+        const bf16x8 ka = e4m3x8_to_bf16(u32x2{raw[0], raw[1]});
+        const bf16x8 kb = e4m3x8_to_bf16(u32x2{raw[2], raw[3]});
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 64 * i);
+        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 64 * i + 8);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qa, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
+    }
+    const f32x4 st = s0 + s1;
+    const int key0 = first + kStepKeys * t + 4 * g;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = key0 + i < k1 ? st[i] * sc : -INFINITY;
+    float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    tm = max_rows(tm);
+    if (__builtin_amdgcn_ballot_w64(tm > m + kRebase) != 0) {
+        const float mn = tm > m + kRebase ? tm : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) o[dt] *= alpha;
+        lsum *= alpha;
+        m = mn;
+    }
+    float ps = 0.0f;
+    bf16x4 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sv[e] - m);
+        ps += pe;
+        pb[e] = (__bf16)pe;
+    }
+    lsum += sum_rows(ps);
+    // values: O^T += V^T P^T, two dim tiles per transpose load
+#pragma unroll
+    for (int dd = 0; dd < kDimTiles / 2; ++dd) {
+        const i32x2 v = vraw[dd];
+        o[2 * dd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[0])), pb,
+                                                              o[2 * dd], 0, 0, 0);
+        o[2 * dd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[1])), pb,
+                                                                  o[2 * dd + 1], 0, 0, 0);
+    }
+}
+
 template <bool QF8, bool DIRECT, bool STREAMP>
 __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
@@ -722,70 +790,76 @@ __global__ void __launch_bounds__(kRingThreads) mla_attn_ring_kernel(const Args 
             while (lds_counter(&ready[w]) <= t) __builtin_amdgcn_s_sleep(1);
             asm volatile("" ::: "memory");
             const uint8_t* base = slots + (t % kRingSlots) * kTileBytes;
-            // All of the tile's LDS reads go out first (keys for the scores,
-            // transposed values for the value product), so their latency
-            // overlaps instead of stalling each product in turn.
-            typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-            u32x4 kraw[kSteps / 2];
-            i32x2 vraw[kDimTiles / 2];
-#pragma unroll
-            for (int i = 0; i < kSteps / 2; ++i)
-                kraw[i] = *reinterpret_cast<const u32x4*>(base + 1024 * i + 16 * lane);
-#pragma unroll
-            for (int dd = 0; dd < kDimTiles / 2; ++dd)
-                vraw[dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + vlane + 512 * dd));
-            __builtin_amdgcn_sched_barrier(0);
-            // scores: S^T = K Q^T over 18 steps of 32 dims
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < kSteps / 2; ++i) {
-                const u32x4 raw = kraw[i];
-                const bf16x8 ka = e4m3x8_to_bf16(u32x2{raw[0], raw[1]});
-                const bf16x8 kb = e4m3x8_to_bf16(u32x2{raw[2], raw[3]});
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 64 * i);
-                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 64 * i + 8);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qa, s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, s1, 0, 0, 0);
-            }
-            const f32x4 st = s0 + s1;
-            const int key0 = first + kStepKeys * t + 4 * g;
-            float sv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = key0 + i < k1 ? st[i] * sc : -INFINITY;
-            float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            tm = max_rows(tm);
-            if (__builtin_amdgcn_ballot_w64(tm > m + kRebase) != 0) {
-                const float mn = tm > m + kRebase ? tm : m;
-                const float alpha = __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-                for (int dt = 0; dt < kDimTiles; ++dt) o[dt] *= alpha;
-                lsum *= alpha;
-                m = mn;
-            }
-            float ps = 0.0f;
-            bf16x4 pb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(sv[e] - m);
-                ps += pe;
-                pb[e] = (__bf16)pe;
-            }
-            lsum += sum_rows(ps);
-            // values: O^T += V^T P^T, two dim tiles per transpose load
-#pragma unroll
-            for (int dd = 0; dd < kDimTiles / 2; ++dd) {
-                const i32x2 v = vraw[dd];
-                o[2 * dd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[0])), pb,
-                                                                      o[2 * dd], 0, 0, 0);
-                o[2 * dd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16(uint32_t(v[1])), pb,
-                                                                          o[2 * dd + 1], 0, 0, 0);
-            }
+            e4m3_tile(base, qrow, lane, g, vlane, sc, first, t, k1, o, m, lsum);
             lds_publish(&done[w], t + 1);
         }
     }
 
     merge_waves<true, DIRECT, STREAMP, kRingThreads>(a, o, m, lsum, !loader, b, split, ht,
                                                      reinterpret_cast<float*>(ring), mls);
+}
+
+// Ranges of one tile per compute wavefront (64 keys, the plan's shortest):
+// no loader wavefronts.  Each of the four wavefronts copies its own tile from
+// memory straight into LDS (global_load_lds_dwordx4: lane l's 16 bytes land
+// at 16 l, which is the ring slot layout), so the tile takes no register hop
+// and no handshake.  Block-table and row reads use keys clamped to
+// max_seq_len - 1, as the ring kernel's loaders do, so they go out before the
+// sequence length arrives; the wavefront then zeroes the rows of keys past
+// the range, so that a zero weight meets finite data.  The 96 KB buffer holds
+// the four tiles first and the merge's exchange afterwards.
+template <bool QF8, bool DIRECT, bool STREAMP>
+__global__ void __launch_bounds__(kThreads) mla_attn_short_kernel(const Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t buf[kWaves * 24 * 64 * 16];
+    __shared__ __attribute__((aligned(16))) __bf16 qlds[16 * kQStride];
+    __shared__ float mls[2][kWaves][16];
+    static_assert(kWaves * kTileBytes <= kWaves * 24 * 64 * 16, "tiles inside the merge buffer");
+
+    int b, split, ht;
+    decode_wg(a, b, split, ht);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int first = split * a.keys_per_split + kTile * w;
+    const int kmax = a.max_seq_len > 0 ? a.max_seq_len - 1 : 0;
+    const int key = first + c < kmax ? first + c : kmax;
+    int page = a.block_table[(size_t)b * a.max_blocks + key / a.block_size];
+    QueryStage<QF8, kThreads> qs;
+    qs.load(a, b, ht, threadIdx.x);
+    int L = a.seq_lens[b];
+    page = page < 0 ? 0 : (page >= a.num_blocks ? a.num_blocks - 1 : page);
+    const uint8_t* row = a.cache + ((size_t)page * a.block_size + key % a.block_size) * kRow;
+    uint8_t* const slot = buf + w * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < kSteps / 2; ++i)
+        __builtin_amdgcn_global_load_lds(row + 64 * i + 16 * g, (lds_void*)(slot + 1024 * i), 16, 0, 0);
+    qs.store(a, ht, qlds, threadIdx.x);
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    const int k0 = split * a.keys_per_split;
+    const int k1 = (k0 + a.keys_per_split < L) ? k0 + a.keys_per_split : L;
+    float sc = a.score_scale * *a.kv_scale;
+    if constexpr (QF8) sc *= *a.q_scale;
+    // the tile is in LDS once this wavefront's loads are done; rows of keys
+    // past the range are overwritten only after that
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (first + c >= k1) {
+#pragma unroll
+        for (int i = 0; i < kSteps / 2; ++i)
+            *reinterpret_cast<u32x4*>(slot + 1024 * i + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    }
+    lds_barrier();
+
+    f32x4 o[kDimTiles];
+#pragma unroll
+    for (int dt = 0; dt < kDimTiles; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.0f;
+    if (k1 > first) {
+        const __bf16* qrow = qlds + c * kQStride + 16 * g;
+        const int vlane = 256 * (c >> 3) + 64 * g + 8 * (c & 7);
+        e4m3_tile(slot, qrow, lane, g, vlane, sc, first, 0, k1, o, m, lsum);
+    }
+    merge_waves<true, DIRECT, STREAMP, kThreads>(a, o, m, lsum, true, b, split, ht, reinterpret_cast<float*>(buf),
+                                                  mls);
 }
 
 // Merge the key ranges of one (sequence, head).  A wavefront's lane l owns
@@ -985,7 +1059,7 @@ int make_plan(const mla_attn_dims* d, uint32_t flags, mla_attn_plan* p) {
     p->workspace_bytes = p->combine ? d->batch * d->num_heads * splits * (kValue + 2) * 4 : 0;
     p->target_workgroups = target;
     p->xcd_remap = (head_tiles > 1 && p->workgroups % 8 == 0) ? 1 : 0;
-    p->block_threads = (flags & MLA_ATTN_KV_FP8) ? kRingThreads : kThreads;
+    p->block_threads = ((flags & MLA_ATTN_KV_FP8) && kps > kStepKeys) ? kRingThreads : kThreads;
     return MLA_DQ_OK;
 }
 
@@ -1037,14 +1111,25 @@ hipError_t launch_pair(const Args& a, const mla_attn_plan& p, hipStream_t stream
     const dim3 grid(uint32_t(p.workgroups)), block(uint32_t(p.block_threads));
     const bool streamp = int64_t(a.B) * a.H * a.splits * kValue * 4 >= kStreamPartialBytes;
     if constexpr (KVF8) {
-        if (!p.combine) {
-            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, true, false>), grid, block, 0, stream, a);
-            return hipGetLastError();
+        if (a.keys_per_split == kStepKeys) {
+            if (!p.combine) {
+                hipLaunchKernelGGL((mla_attn_short_kernel<QF8, true, false>), grid, block, 0, stream, a);
+                return hipGetLastError();
+            }
+            if (streamp)
+                hipLaunchKernelGGL((mla_attn_short_kernel<QF8, false, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((mla_attn_short_kernel<QF8, false, false>), grid, block, 0, stream, a);
+        } else {
+            if (!p.combine) {
+                hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, true, false>), grid, block, 0, stream, a);
+                return hipGetLastError();
+            }
+            if (streamp)
+                hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, false>), grid, block, 0, stream, a);
         }
-        if (streamp)
-            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, true>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((mla_attn_ring_kernel<QF8, false, false>), grid, block, 0, stream, a);
     } else {
         if (!p.combine) {
             hipLaunchKernelGGL((mla_attn_partial_kernel<QF8, true, false>), grid, block, 0, stream, a);

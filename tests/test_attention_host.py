@@ -94,8 +94,11 @@ def test_plan_covers_every_key_once(B_, H, L):
         ws = B_ * H * p.splits * (512 + 2) * 4 if p.combine else 0
         assert p.workspace_bytes == ws
         assert M.attn_workspace_size(dims(B_, H, MB=MB, L=L), flags) == ws
-        # E4M3 cache: four compute plus four loader wavefronts; bf16: four
-        assert p.block_threads == (512 if flags & M.ATTN_KV_FP8 else 256) and p.target_workgroups == 256
+        # E4M3 cache: four compute plus four loader wavefronts, or four that
+        # load their own tile when each range is one tile per wavefront;
+        # bf16: four
+        loaders = bool(flags & M.ATTN_KV_FP8) and p.keys_per_split > 64
+        assert p.block_threads == (512 if loaders else 256) and p.target_workgroups == 256
         assert p.xcd_remap == (1 if p.head_tiles > 1 and p.workgroups % 8 == 0 else 0)
 
 
