@@ -788,7 +788,7 @@ def _short_kernel_name(name: str) -> str:
     if name.startswith("Cijk_") or "gemm" in name.lower():
         return "GEMM (hipBLASLt)"
     for key in ("mla_dq_epilogue_kernel", "mla_dq_uk_epilogue_kernel", "mla_attn_ring_kernel",
-                "mla_attn_partial_kernel",
+                "mla_attn_short_kernel", "mla_attn_partial_kernel",
                 "mla_attn_combine_wide_kernel", "mla_attn_combine_kernel"):
         if key in name:
             return key

@@ -83,6 +83,14 @@ def test_trace_summary_timeline(tmp_path):
     assert "First start to last end: median 42.50 µs; sum of kernel durations 42.00 µs." in out
 
 
+def test_trace_kernel_labels():
+    assert bench._short_kernel_name("void mla_attn::mla_attn_short_kernel<true, false, false>(mla_attn::Args)") \
+        == "mla_attn_short_kernel"
+    assert bench._short_kernel_name("void mla_attn::mla_attn_combine_wide_kernel<true>(mla_attn::Args)") \
+        == "mla_attn_combine_wide_kernel"
+    assert bench._short_kernel_name("Cijk_Ailk_Bljk_BBS_BH_MT64x64") == "GEMM (hipBLASLt)"
+
+
 def test_trace_summary_drops_cases_without_an_epilogue_and_rare_cases(tmp_path):
     path = tmp_path / "run_kernel_trace.csv"
     _write_trace(path, 6, [("Cijk_only_gemm", 8, 5_000, 0)])
