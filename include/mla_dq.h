@@ -71,8 +71,10 @@ extern "C" {
  * workgroups, tails batched, rope table staged in LDS) above; the page's
  * launcher makes the same token-count-dependent choice ("implementation
  * breakdown" items 1 and 3).  Independently, loads and stores stream past
- * the caches (non-temporal) once one call moves more bytes than the
- * Infinity Cache can keep.  At most one mapping override may be set. */
+ * the caches (non-temporal) once one call moves at least stream_bytes_min
+ * bytes (80 MiB by default, measured inside a decode step; the environment
+ * variable MLA_DQ_STREAM_BYTES_MIN overrides it).  At most one mapping
+ * override may be set. */
 #define MLA_DQ_FORCE_SMALL_T (1u << 8)  /* latency mapping, 64 threads     */
 #define MLA_DQ_FORCE_LARGE_T (1u << 9)  /* throughput mapping              */
 #define MLA_DQ_FORCE_STREAM  (1u << 10) /* non-temporal loads and stores   */

@@ -61,10 +61,18 @@
 #define MLA_DQ_MID_ROWS_MAX_DEFAULT 5120
 #endif
 // Streaming (non-temporal) loads and stores once a call moves at least this
-// many bytes: above the 256 MB Infinity Cache nothing survives to the next
-// call anyway, below it the default policy lets the data stay resident.
+// many bytes.  Measured inside a captured decode step (the producing GEMMs
+// before the call; graph-replayed, nine alternating rounds), both the
+// epilogue and the fused W_UK call gain from streaming from about 85 MB on
+// (epilogue at 102 / 117 / 146 MB: 22.3-26.5 -> 18.5, 26.1-27.9 -> 22.3,
+// 32.1 -> 28.3 us; fused call at 91 / 100 MB: 32.5 -> 29.2, 37.0 -> 31.3 us)
+// and lose or break even below (epilogue at 73 MB 13.1 -> 13.8 us, fused
+// call at 73 MB 23.8 -> 24.5 us).  A call replayed alone on one resident
+// buffer set would keep the cached policy up to the 256 MB Infinity Cache
+// (2-7 % faster there), but in a step the neighbouring kernels' data leave
+// little of it resident.
 #ifndef MLA_DQ_STREAM_BYTES_MIN_DEFAULT
-#define MLA_DQ_STREAM_BYTES_MIN_DEFAULT (192ll << 20)
+#define MLA_DQ_STREAM_BYTES_MIN_DEFAULT (80ll << 20)
 #endif
 // Cache-policy bits for streaming buffer loads and stores (the non-temporal
 // bit of gfx94x/gfx950).

@@ -329,7 +329,7 @@ def test_plan_defaults_match_measured_choice():
     (measured fastest after the W_UK product of a decode step up to about
     2600 rows with at most 32 heads), the 256-token full-head one the
     throughput mapping; with 128 heads the 128-thread mapping takes over
-    above 896 rows.  All with the default cache policy below 192 MiB."""
+    above 896 rows.  All with the default cache policy below 80 MiB."""
     big = M.plan(_dims(T=8192, H=16, NB=4096), M.ROPE | M.KV_FP8)
     assert (big.mapping, big.streaming) == (1, 1)
     for T, H, mapping in ((1, 16, 0), (64, 16, 0), (65, 16, 0), (150, 16, 0), (151, 16, 2),

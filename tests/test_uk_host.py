@@ -205,7 +205,7 @@ def test_plan_overrides():
 def test_plan_default_thresholds():
     """Without the environment overrides: the throughput configuration from
     1025 query rows, one 16-column block per wavefront in the latency one
-    for at most 32 units, streaming from the epilogue's 192 MiB."""
+    for at most 32 units, streaming from the epilogue's 80 MiB."""
     if any(v in os.environ for v in ("MLA_DQ_UK_LARGE_ROWS_MIN", "MLA_DQ_STREAM_BYTES_MIN")):
         pytest.skip("threshold overridden in the environment")
     for T, H, want in [(64, 16, 0), (65, 16, 1), (72, 16, 1), (8, 128, 0), (9, 128, 1), (1024, 1, 0), (1025, 1, 1)]:
@@ -219,4 +219,4 @@ def test_plan_default_thresholds():
         p = M.uk_plan(_dims(T=T, H=H, NB=(T + 63) // 64 + 1, maxpos=32768), M.ROPE)
         assert p.mapping == 0 and p.n_blocks == nb and p.column_groups == 512 // (4 * 16 * nb)
     p = M.uk_plan(_dims(T=2048, H=16, NB=33, maxpos=32768), M.ROPE)
-    assert p.stream_bytes_min == 192 << 20 and p.streaming == 0
+    assert p.stream_bytes_min == 80 << 20 and p.streaming == 0
