@@ -218,6 +218,29 @@ def test_short_sequences_single_step():
     check(w, "short")
 
 
+@pytest.mark.parametrize("batch,heads,lengths,q_fp8", [
+    (300, 16, tuple((7 * i) % 65 for i in range(300)), True),      # one range per sequence: bf16 written directly
+    (1, 16, (1000,), False),                                       # 16 ranges, cached partial results
+    (8, 128, (256, 255, 200, 129, 64, 63, 1, 0), False),           # 4 ranges, streamed partial results
+], ids=["direct", "split", "split_streamed"])
+def test_short_range_kernel(batch, heads, lengths, q_fp8):
+    """Plans whose E4M3 ranges hold 64 keys (one tile per compute wavefront)
+    run the kernel without loader wavefronts; all three of its forms against
+    the oracle, ragged lengths included."""
+    w = I.attn_custom(batch, heads, lengths, q_fp8=q_fp8, kv_fp8=True, name="short_range")
+    inp = I.make_attn_inputs(w)
+    d = to_device(inp)
+    out = torch.empty(w.batch, w.heads, 512, dtype=torch.bfloat16, device=DEV)
+    prep = M.PreparedAttention(out, d["q"], d["cache"], d["block_table"], d["seq_lens"],
+                               w.sm_scale, d["q_scale"], d["kv_scale"])
+    assert prep.plan.keys_per_split == 64 and prep.plan.block_threads == 256
+    # partial results stream past the caches from 4 MiB per call
+    streamed = bool(prep.plan.combine) and batch * heads * prep.plan.splits * 512 * 4 >= (4 << 20)
+    want = {300: (0, False), 1: (1, False), 8: (1, True)}[batch]
+    assert (prep.plan.combine, streamed) == want
+    check(w, f"short-range kernel B={batch} H={heads}")
+
+
 def test_all_empty_sequences_give_zeros():
     w = I.attn_custom(3, 16, (0, 0, 0), name="empty")
     inp = I.make_attn_inputs(w)
