@@ -7,10 +7,12 @@
 // softmax and its own accumulator for all 512 value dimensions, and meet
 // once at the end to merge their four partial results through LDS.
 //
-// Two kernels share that scheme.  With a bf16 cache each compute wavefront
-// loads its own keys into registers (mla_attn_partial_kernel, described
-// next).  With an E4M3 cache four loader wavefronts stream the keys into an
-// LDS ring for their compute partners (mla_attn_ring_kernel, further down).
+// Three kernels share that scheme.  With a bf16 cache each compute
+// wavefront loads its own keys into registers (mla_attn_partial_kernel,
+// described next).  With an E4M3 cache four loader wavefronts stream the
+// keys into an LDS ring for their compute partners (mla_attn_ring_kernel,
+// further down), except for ranges of one tile per compute wavefront, whose
+// wavefronts copy their tile into LDS themselves (mla_attn_short_kernel).
 //
 // Per pair of 16-key tiles, in one wavefront (lane l: c = l % 16, g = l / 16):
 //  * scores on the matrix cores, transposed: S^T[key][head] = K Q^T with
