@@ -553,6 +553,14 @@ def attn_traffic_entry(name: str):
     return t.get("workloads", {}).get(name, {}).get("hbm_bytes_per_call")
 
 
+def attn_range_kernel(w: I.AttnWorkload, pl) -> str:
+    """Which range kernel the plan runs: the loader/compute ring (E4M3 cache),
+    its loader-free form for 64-key ranges, or the bf16-cache kernel."""
+    if not w.kv_fp8:
+        return "mla_attn_partial_kernel"
+    return "mla_attn_short_kernel" if pl.keys_per_split == 64 else "mla_attn_ring_kernel"
+
+
 def attn_plan_for(w: I.AttnWorkload):
     d = M.AttnDims()
     d.batch, d.num_heads, d.num_blocks, d.block_size = w.batch, w.heads, w.num_blocks, w.block_size
@@ -635,6 +643,7 @@ def attention_timings(dev: str, steps: int, cpu_seconds: float = 0.0) -> dict:
             "us_per_call_warm": round(warm["event_ms_per_call"] * 1e3, 3),
             "gbs_warm": round(nb / warm["event_ms_per_call"] / 1e6, 1),
             "splits": pl.splits, "keys_per_split": pl.keys_per_split,
+            "range_kernel": attn_range_kernel(w, pl), "block_threads": pl.block_threads,
             "workgroups": pl.workgroups, "combine": bool(pl.combine),
             "traffic_bytes": attn_traffic_entry(name),
         }

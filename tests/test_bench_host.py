@@ -83,6 +83,19 @@ def test_trace_summary_timeline(tmp_path):
     assert "First start to last end: median 42.50 µs; sum of kernel durations 42.00 µs." in out
 
 
+def test_attention_range_kernel_names():
+    """The name bench.py reports is the kernel the plan launches: 64-key
+    ranges on an E4M3 cache take the loader-free kernel (256 threads)."""
+    for name, want in (("attn_b64_l4096_h16_kvfp8", "mla_attn_ring_kernel"),
+                       ("attn_b1_l1024_h16_kvfp8", "mla_attn_short_kernel"),
+                       ("attn_b64_l4096_h16_bf16", "mla_attn_partial_kernel"),
+                       ("attn_b256_l4096_h16_kvfp8", "mla_attn_ring_kernel")):
+        w = I.ATTN_WORKLOADS[name]
+        pl = bench.attn_plan_for(w)
+        assert bench.attn_range_kernel(w, pl) == want
+        assert pl.block_threads == (512 if want == "mla_attn_ring_kernel" else 256)
+
+
 def test_trace_kernel_labels():
     assert bench._short_kernel_name("void mla_attn::mla_attn_short_kernel<true, false, false>(mla_attn::Args)") \
         == "mla_attn_short_kernel"
