@@ -117,21 +117,28 @@ def settle(fns: list, ms: float = 40.0) -> None:
 
 def time_calls(sets: list, steps: int, warmup: int) -> dict:
     """Back-to-back calls on torch's current stream (the stream the kernel is
-    launched on), bracketed by synchronisation; HIP events give the average
-    per-launch time, the host clock the wall time."""
+    launched on), bracketed by synchronisation: the host clock gives the wall
+    time per call over all `steps`.  HIP events give the average per-launch
+    time over calls 2..steps: the start event follows the first call in
+    stream order, so the GPU's wait for the host to enqueue that first call
+    after the synchronisation (several µs, which 20 steps would spread as
+    0.3-0.5 µs over each) is not counted as kernel time."""
     for i in range(warmup):
         sets[i % len(sets)].call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    first = 1 if steps >= 2 else 0
+    if first:
+        sets[0].call()
     e0.record(stream)
-    for i in range(steps):
+    for i in range(first, steps):
         sets[i % len(sets)].call()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return {"event_ms_per_call": e0.elapsed_time(e1) / steps, "wall_ms_per_call": wall * 1e3 / steps}
+    return {"event_ms_per_call": e0.elapsed_time(e1) / (steps - first), "wall_ms_per_call": wall * 1e3 / steps}
 
 
 def time_graph(sets: list, calls: int = 100, replays: int = 20) -> float:
