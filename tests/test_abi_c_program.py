@@ -35,6 +35,7 @@ int main(void) {
     CHECK(mla_dq_plan(&d, MLA_DQ_ROPE | MLA_DQ_KV_FP8, &p) == MLA_DQ_OK);
     CHECK(p.bytes == 318373888LL);
     CHECK(p.grid_blocks > 0 && p.total_rows == 8192LL * 17);
+    CHECK(p.streaming == 1 && p.stream_bytes_min == (80LL << 20));   /* default streaming threshold */
     CHECK(mla_dq_plan(&d, 1u << 30, &p) == MLA_DQ_ERR_FLAGS);
     CHECK(mla_dq_plan(NULL, 0, &p) == MLA_DQ_ERR_NULL);
 
@@ -64,8 +65,11 @@ int main(void) {
     a.max_seq_len = 4096;
     mla_attn_plan ap;
     CHECK(mla_decode_attention_plan(&a, MLA_ATTN_KV_FP8, &ap) == MLA_DQ_OK);
-    CHECK(ap.splits == 4 && ap.combine == 1 && ap.workgroups == 256);
+    CHECK(ap.splits == 4 && ap.combine == 1 && ap.workgroups == 256 && ap.block_threads == 512);
     CHECK(mla_decode_attention_workspace_size(&a, MLA_ATTN_KV_FP8) == (size_t)ap.workspace_bytes);
+    a.batch = 1; a.max_blocks_per_seq = 16; a.max_seq_len = 1024;   /* 16 ranges of 64 keys: no loaders */
+    CHECK(mla_decode_attention_plan(&a, MLA_ATTN_KV_FP8, &ap) == MLA_DQ_OK);
+    CHECK(ap.splits == 16 && ap.keys_per_split == 64 && ap.block_threads == 256);
     printf("%s\n", fails ? "failed" : "ok");
     return fails != 0;
 }
