@@ -91,6 +91,9 @@ def test_c_program_against_the_library(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     env = dict(os.environ)
+    for var in ("MLA_DQ_STREAM_BYTES_MIN", "MLA_ATTN_TARGET_WGS", "MLA_DQ_UK_LARGE_ROWS_MIN",
+                "MLA_DQ_SMALL_ROWS_MAX", "MLA_DQ_MID_ROWS_MAX"):
+        env.pop(var, None)                     # the checks above expect the library's defaults
     env["LD_LIBRARY_PATH"] = ":".join(p for p in ("/opt/rocm/lib", env.get("LD_LIBRARY_PATH", "")) if p)
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
